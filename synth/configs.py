@@ -1,0 +1,92 @@
+"""The five workload configurations, as literal values.
+
+Shapes, budgets and RoPE/DCA/YaRN settings of the synthetic layers the path
+is measured and checked on.  Values the workload description leaves open are
+fixed here (and listed with their reasons in the design doc):
+
+* tiny: DCA local window W = 64 (so the key period S = C - W = 192 is a
+  multiple of the 64-key tile), one prefill chunk of 1024;
+* 7B-shaped 128K and 14B-shaped 256K: no YaRN (s = 1) and DCA off (both are
+  within the 262,144-token training length, where DCA is the identity);
+* 1M and refinement-stress: DCA chunk C = 262,144, local window W = 32,768,
+  YaRN factor s = N / 262,144 (4 and 2); no YaRN frequency blend on the
+  attention path (temperature only).
+"""
+
+from dataclasses import dataclass, field, replace
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    cid: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seq_len: int
+    prefill_chunk: int
+    in_dtype: str                 # "fp32" or "bf16" at the library boundary
+    rope_base: float
+    yarn_factor: float = 1.0      # s; 1 = no YaRN
+    yarn_orig_max_pos: int = 262144
+    dca_chunk: int = 0            # C; 0 = DCA off
+    dca_local: int = 0            # W
+    n_vert: int = 1000
+    n_slash: int = 6096
+    last_q: int = 64
+    planting: str = "none"        # see synth.gen
+    sink_every: int = 0           # sink spacing for planting "sinks_every"
+    recall_threshold: float = 0.9
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def group(self):
+        return self.n_heads // self.n_kv_heads
+
+    @property
+    def seed(self):
+        return 0x1C5A0000 + self.cid
+
+    @property
+    def n_chunks(self):
+        return -(-self.seq_len // self.prefill_chunk)
+
+    def chunk_bounds(self, c):
+        c0 = c * self.prefill_chunk
+        return c0, min(self.seq_len, c0 + self.prefill_chunk) - c0
+
+
+TINY = LayerConfig(
+    name="tiny", cid=1, n_heads=1, n_kv_heads=1, head_dim=64, seq_len=1024,
+    prefill_chunk=1024, in_dtype="fp32", rope_base=1e4, dca_chunk=256,
+    dca_local=64, n_vert=32, n_slash=64, planting="none")
+
+SEVEN_B_128K = LayerConfig(
+    name="7b_128k", cid=2, n_heads=28, n_kv_heads=4, head_dim=128,
+    seq_len=131072, prefill_chunk=32768, in_dtype="bf16", rope_base=1e7,
+    planting="sinks_band")
+
+FOURTEEN_B_256K = LayerConfig(
+    name="14b_256k", cid=3, n_heads=40, n_kv_heads=8, head_dim=128,
+    seq_len=262144, prefill_chunk=32768, in_dtype="bf16", rope_base=1e7,
+    planting="sinks_band")
+
+SEVEN_B_1M = LayerConfig(
+    name="7b_1m_dca", cid=4, n_heads=28, n_kv_heads=4, head_dim=128,
+    seq_len=1048576, prefill_chunk=32768, in_dtype="bf16", rope_base=1e7,
+    yarn_factor=4.0, dca_chunk=262144, dca_local=32768,
+    planting="sinks_every", sink_every=65536)
+
+FOURTEEN_B_512K_REFINE = LayerConfig(
+    name="14b_512k_refine", cid=5, n_heads=40, n_kv_heads=8, head_dim=128,
+    seq_len=524288, prefill_chunk=32768, in_dtype="bf16", rope_base=1e7,
+    yarn_factor=2.0, dca_chunk=262144, dca_local=32768,
+    planting="far_sinks_stripes")
+
+CONFIGS = {c.name: c for c in (TINY, SEVEN_B_128K, FOURTEEN_B_256K,
+                               SEVEN_B_1M, FOURTEEN_B_512K_REFINE)}
+
+
+def scaled(cfg, **kw):
+    """A copy of a config with some fields changed (test shapes)."""
+    return replace(cfg, **kw)

@@ -1,0 +1,196 @@
+"""Seeded synthetic Q/K/V for the five layer shapes.
+
+Input creation only: this module holds none of the method's arithmetic (no
+rotary embedding, no softmax, no selection).  Both the HIP path and the fp64
+oracle consume exactly the tensors made here.
+
+Recipe (all magnitudes are stated as the logit excess E over the background,
+whose standard deviation is 1 at the 1/sqrt(D) scale):
+
+* noise: Q, K, V iid N(0, 1) in fp32; bf16 configs are then rounded to bf16
+  (torch's round-to-nearest-even), the tiny config stays fp32 (the library
+  rounds it on entry);
+* "sinks_band" / "sinks_every" (7B/14B-shaped layers): per KV head a unit
+  sink direction u in the four lowest-frequency rotary planes (planes
+  D/2-4 .. D/2-1, both halves), added with amplitude sqrt(E_sink sqrt(D)) to
+  the sink keys and, scaled by a per-query-head factor, to every query; and a
+  unit band direction e spread evenly over rotary planes 10..47 with random
+  phases, added to every query and key.  After rotation, q.k of the shared
+  band direction is a sum of cosines of (i - j) * theta_p, so it peaks on the
+  main diagonal and fades with distance: a local band of slash lines.  Sinks
+  sit at columns 0..15, or at multiples of `sink_every`;
+* "far_sinks_stripes" (refinement stress): 64 sinks per KV head at seeded
+  uniform positions, plus periodic diagonal stripes: a harmonic code
+  c(a) = (cos(2 pi k a / P), sin(2 pi k a / P))_{k=1..8} / sqrt(8) in rotary
+  planes 52..59 added to key j with a = j mod P and to query i with
+  a = i mod P, so q.k peaks where i - j is a multiple of P.  The period P
+  cycles over (64, 96, 128, 192, 256, 512, 1024, 2048) by KV head; the
+  per-query-head stripe factor varies, so some heads are well covered by the
+  base budget and some are not;
+* "none" (tiny): noise only.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+E_SINK = 3.0
+E_BAND = 3.0
+E_FAR_SINK = 6.0
+E_STRIPE = 4.0
+BAND_PLANES = (10, 48)
+SINK_PLANES = 4
+STRIPE_PLANES = (52, 60)
+STRIPE_PERIODS = (64, 96, 128, 192, 256, 512, 1024, 2048)
+N_FAR_SINKS = 64
+
+
+def _rng(cfg, *tags):
+    return np.random.default_rng([cfg.seed] + [int(t) for t in tags])
+
+
+def _torch_seed(cfg, *tags):
+    return int(np.random.SeedSequence([cfg.seed] + [int(t) for t in tags])
+               .generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
+
+
+def _plane_dims(d, planes):
+    half = d // 2
+    lo, hi = planes
+    return np.arange(lo, hi), np.arange(lo, hi) + half
+
+
+def _band_direction(cfg, g):
+    d = cfg.head_dim
+    rng = _rng(cfg, 101, g)
+    a, b = _plane_dims(d, BAND_PLANES)
+    phase = rng.uniform(0, 2 * math.pi, a.size)
+    e = np.zeros(d)
+    e[a] = np.cos(phase)
+    e[b] = np.sin(phase)
+    return e / np.linalg.norm(e)
+
+
+def _sink_direction(cfg, g):
+    d = cfg.head_dim
+    rng = _rng(cfg, 102, g)
+    a, b = _plane_dims(d, (d // 2 - SINK_PLANES, d // 2))
+    u = np.zeros(d)
+    u[a] = rng.normal(size=a.size)
+    u[b] = rng.normal(size=b.size)
+    return u / np.linalg.norm(u)
+
+
+def _stripe_codes(cfg, g, positions):
+    """Harmonic stripe code for each position, [n, D] (float64)."""
+    d = cfg.head_dim
+    period = STRIPE_PERIODS[g % len(STRIPE_PERIODS)]
+    a, b = _plane_dims(d, STRIPE_PLANES)
+    k = np.arange(1, a.size + 1)
+    ph = 2 * math.pi * np.outer(np.asarray(positions) % period, k) / period
+    code = np.zeros((len(positions), d))
+    code[:, a] = np.cos(ph)
+    code[:, b] = np.sin(ph)
+    return code / math.sqrt(a.size)
+
+
+def sink_positions(cfg, g):
+    """Key columns planted as sinks for KV head g."""
+    n = cfg.seq_len
+    if cfg.planting == "sinks_band":
+        return np.arange(min(16, n))
+    if cfg.planting == "sinks_every":
+        return np.arange(0, n, cfg.sink_every)[:16]
+    if cfg.planting == "far_sinks_stripes":
+        rng = _rng(cfg, 103, g)
+        return np.sort(rng.choice(n, size=min(N_FAR_SINKS, n), replace=False))
+    return np.zeros(0, dtype=np.int64)
+
+
+def head_factors(cfg):
+    """Per-query-head multipliers of the planted excess, [H] each."""
+    rng = _rng(cfg, 104)
+    return {"band": rng.uniform(0.6, 1.2, cfg.n_heads),
+            "sink": rng.uniform(0.8, 1.2, cfg.n_heads),
+            "stripe": rng.uniform(0.0, 1.2, cfg.n_heads)}
+
+
+def _amp(excess, d):
+    return math.sqrt(excess * math.sqrt(d))
+
+
+def _noise(shape, seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def generate(cfg, device="cpu", n_tokens=None):
+    """Q [H, N, D], K [H_kv, N, D], V [H_kv, N, D] on `device`.
+
+    fp32 for the tiny config (made with numpy, identical on every device),
+    bf16 otherwise (made with torch's seeded generator on `device`).
+    n_tokens < seq_len keeps the recipe of the full layer but stops early.
+    """
+    n = cfg.seq_len if n_tokens is None else int(n_tokens)
+    H, G, D = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    if cfg.in_dtype == "fp32":
+        rng = _rng(cfg, 1)
+        q = rng.standard_normal((H, n, D), dtype=np.float32)
+        k = rng.standard_normal((G, n, D), dtype=np.float32)
+        v = rng.standard_normal((G, n, D), dtype=np.float32)
+        if cfg.planting != "none":
+            raise ValueError("planting is defined for bf16 layers only")
+        return (torch.from_numpy(q).to(device), torch.from_numpy(k).to(device),
+                torch.from_numpy(v).to(device))
+
+    fac = head_factors(cfg)
+    out_q = torch.empty((H, n, D), dtype=torch.bfloat16, device=device)
+    out_k = torch.empty((G, n, D), dtype=torch.bfloat16, device=device)
+    out_v = torch.empty((G, n, D), dtype=torch.bfloat16, device=device)
+    group = H // G
+    for g in range(G):
+        k = _noise((n, D), _torch_seed(cfg, 2, g), device)
+        per_head_q = []
+        if cfg.planting in ("sinks_band", "sinks_every"):
+            e = torch.tensor(_band_direction(cfg, g), dtype=torch.float32,
+                             device=device)
+            u = torch.tensor(_sink_direction(cfg, g), dtype=torch.float32,
+                             device=device)
+            k += _amp(E_BAND, D) * e
+            sp = sink_positions(cfg, g)
+            sinks = torch.as_tensor(sp[sp < n], device=device)
+            k[sinks] += _amp(E_SINK, D) * u
+            for hh in range(group):
+                h = g * group + hh
+                per_head_q.append(_amp(E_BAND, D) * float(fac["band"][h]) * e
+                                  + _amp(E_SINK, D) * float(fac["sink"][h]) * u)
+        elif cfg.planting == "far_sinks_stripes":
+            u = torch.tensor(_sink_direction(cfg, g), dtype=torch.float32,
+                             device=device)
+            sp = sink_positions(cfg, g)
+            sinks = torch.as_tensor(sp[sp < n], device=device)
+            k[sinks] += _amp(E_FAR_SINK, D) * u
+            period = STRIPE_PERIODS[g % len(STRIPE_PERIODS)]
+            codes = torch.tensor(_stripe_codes(cfg, g, np.arange(period)),
+                                 dtype=torch.float32, device=device)
+            idx = torch.arange(n, device=device) % period
+            k += _amp(E_STRIPE, D) * codes[idx]
+            for hh in range(group):
+                h = g * group + hh
+                per_head_q.append(_amp(E_FAR_SINK, D) * float(fac["sink"][h]) * u)
+        out_k[g] = k.to(torch.bfloat16)
+        del k
+        out_v[g] = _noise((n, D), _torch_seed(cfg, 3, g), device).to(
+            torch.bfloat16)
+        for hh in range(group):
+            h = g * group + hh
+            q = _noise((n, D), _torch_seed(cfg, 1, h), device)
+            if per_head_q:
+                q += per_head_q[hh]
+            if cfg.planting == "far_sinks_stripes":
+                q += (_amp(E_STRIPE, D) * float(fac["stripe"][h])) * codes[idx]
+            out_q[h] = q.to(torch.bfloat16)
+            del q
+    return out_q, out_k, out_v
