@@ -1,0 +1,20 @@
+"""MI355X (gfx950) sparse long-context prefill: DCA + YaRN RoPE +
+vertical-slash sparse attention over a GQA KV cache.
+
+The compute lives in liblcsr.so (HIP, C ABI in include/lcsr.h); this package
+is its thin binding plus the chunk loop.  Importing it loads the library and
+fails loudly if it has not been built.
+"""
+
+from . import _capi
+from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, yarn_softmax_scale,
+                  rope_yarn_apply, dca_positions, vs_pattern_estimate,
+                  vs_sparse_attn_prefill, attn_recall_check, workspace_bytes)
+from .driver import ChunkedSparsePrefill
+
+_capi.load()
+
+__all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "yarn_softmax_scale",
+           "rope_yarn_apply", "dca_positions", "vs_pattern_estimate",
+           "vs_sparse_attn_prefill", "attn_recall_check", "workspace_bytes",
+           "ChunkedSparsePrefill"]

@@ -1,0 +1,187 @@
+// RoPE / YaRN rotation, DCA position maps and the query pre-rotations.
+//
+// Rotation: rotate_half convention (deepseekmodel.com long-context
+// architecture page, §2.4 code): the pair (x_p, x_{p+D/2}) turns by
+// pos * theta_p.  The angle is formed in fp64 from the integer position and
+// reduced to [-pi, pi] before sin/cos, so positions up to 2^31 keep full
+// fp32 accuracy; the rotation itself is fp32 and the store bf16 (RNE).
+#include <cmath>
+
+#include "lcsr_internal.h"
+
+namespace lcsr {
+
+DcaParams make_dca(const lcsr_dca_t* dca) {
+  DcaParams d{0, 0, 0};
+  if (dca && dca->chunk > 0) {
+    d.chunk = dca->chunk;
+    d.local = dca->local;
+    d.period = dca->chunk - dca->local;
+  }
+  return d;
+}
+
+int build_freq_table(const lcsr_rope_t* rope, int64_t head_dim, FreqTable* out) {
+  if (!rope) return fail(LCSR_EINVAL, "rope is NULL");
+  if (head_dim <= 0 || head_dim % 2 || head_dim / 2 > kMaxRopeHalf)
+    return fail(LCSR_EINVAL, "head_dim %lld must be even and <= %d",
+                (long long)head_dim, 2 * kMaxRopeHalf);
+  if (!(rope->base > 1.0))
+    return fail(LCSR_EINVAL, "rope base must be > 1");
+  const bool blend = (rope->flags & LCSR_ROPE_YARN_FREQ) && rope->yarn_factor > 1.0;
+  if (blend && (rope->orig_max_pos <= 0 || !(rope->beta_fast > rope->beta_slow)))
+    return fail(LCSR_EINVAL, "YaRN blend needs orig_max_pos > 0 and beta_fast > beta_slow");
+  const int64_t half = head_dim / 2;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int64_t p = 0; p < half; ++p) {
+    double theta = std::pow(rope->base, -2.0 * (double)p / (double)head_dim);
+    if (blend) {
+      // YaRN NTK-by-parts: r = turns of the pair over the training length.
+      double r = (double)rope->orig_max_pos * theta / two_pi;
+      double g = (r - rope->beta_slow) / (rope->beta_fast - rope->beta_slow);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      theta = theta * ((1.0 - g) / rope->yarn_factor + g);
+    }
+    out->inv_freq[p] = theta;
+  }
+  for (int64_t p = half; p < kMaxRopeHalf; ++p) out->inv_freq[p] = 0.0;
+  return LCSR_OK;
+}
+
+namespace {
+
+// fp32 inputs are rounded to bf16 on entry, like every input of the library
+__device__ __forceinline__ float load_elem(const void* base, int32_t dtype, int64_t off) {
+  if (dtype == LCSR_FP32) return bf16_to_f32(f32_to_bf16(static_cast<const float*>(base)[off]));
+  return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
+}
+
+// One thread per (token, pair); the angle is shared by every head.
+__global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft) {
+  const int64_t half = a.head_dim / 2;
+  const int64_t tok_per_block = 256 / half;
+  const int64_t t = (int64_t)blockIdx.x * tok_per_block + threadIdx.x / half;
+  const int64_t p = threadIdx.x % half;
+  if (threadIdx.x >= tok_per_block * half || t >= a.n_tok) return;
+  float c = 1.0f, s = 0.0f;
+  if (a.mode != kNoRotate) {
+    int64_t pos;
+    if (a.mode == kPosArray) pos = a.pos[t];
+    else if (a.mode == kPosAffine) pos = t + a.pos_offset;
+    else pos = dca_query_pos(t + a.pos_offset, a.variant, a.dca);
+    rope_cos_sin(pos, ft.inv_freq[p], &c, &s);
+  }
+  for (int64_t h = 0; h < a.n_heads; ++h) {
+    const int64_t so = h * a.src_sh + t * a.src_st;
+    const float x1 = load_elem(a.src, a.src_dtype, so + p);
+    const float x2 = load_elem(a.src, a.src_dtype, so + p + half);
+    const float y1 = (x1 * c - x2 * s) * a.scale;
+    const float y2 = (x2 * c + x1 * s) * a.scale;
+    uint16_t* d = a.dst + h * a.dst_sh + t * a.dst_st;
+    d[p] = f32_to_bf16(y1);
+    d[p + half] = f32_to_bf16(y2);
+  }
+}
+
+__global__ void dca_positions_kernel(int64_t tok_start, int64_t n_tok, DcaParams d,
+                                     int32_t* pk, int32_t* pi, int32_t* ps, int32_t* pn) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tok) return;
+  const int64_t i = tok_start + t;
+  if (pk) pk[t] = (int32_t)dca_key_pos(i, d);
+  if (pi) pi[t] = (int32_t)dca_query_pos(i, 0, d);
+  if (ps) ps[t] = (int32_t)dca_query_pos(i, 1, d);
+  if (pn) pn[t] = (int32_t)dca_query_pos(i, 2, d);
+}
+
+__global__ void fill_zero_kernel(u32x4* p, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = (u32x4){0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
+  // callers pass 256-byte aligned workspace slices whose size is a multiple of 16
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return LCSR_OK;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     static_cast<u32x4*>(ptr), n16);
+  return check_launch("fill_zero");
+}
+
+int launch_rotate(const RotateArgs& a, const FreqTable& ft, hipStream_t s) {
+  if (a.n_tok == 0 || a.n_heads == 0) return LCSR_OK;
+  const int64_t half = a.head_dim / 2;
+  const int64_t tok_per_block = 256 / half;
+  const int64_t blocks = (a.n_tok + tok_per_block - 1) / tok_per_block;
+  hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
+  return check_launch("rotate");
+}
+
+int launch_dca_positions(int64_t tok_start, int64_t n_tok, const DcaParams& d,
+                         int32_t* pk, int32_t* pi, int32_t* ps, int32_t* pn,
+                         hipStream_t s) {
+  if (n_tok == 0) return LCSR_OK;
+  const int64_t blocks = (n_tok + 255) / 256;
+  hipLaunchKernelGGL(dca_positions_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     tok_start, n_tok, d, pk, pi, ps, pn);
+  return check_launch("dca_positions");
+}
+
+int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
+                             const DcaParams& d, uint16_t* dst, int n_var,
+                             hipStream_t s) {
+  const int64_t D = p.head_dim, L = p.chunk_len, H = p.n_heads;
+  for (int v = 0; v < n_var; ++v) {
+    RotateArgs a{};
+    a.src = p.q;
+    a.src_dtype = p.q_dtype;
+    a.src_sh = p.q_stride_h;
+    a.src_st = p.q_stride_t;
+    a.dst = dst + (int64_t)v * H * L * D;
+    a.dst_sh = L * D;
+    a.dst_st = D;
+    a.n_heads = H;
+    a.n_tok = L;
+    a.head_dim = D;
+    a.pos_offset = p.chunk_start;
+    a.mode = kPosDca;
+    a.variant = v;
+    a.dca = d;
+    a.scale = 1.0f;
+    int rc = launch_rotate(a, ft, s);
+    if (rc) return rc;
+  }
+  return LCSR_OK;
+}
+
+int launch_rotate_q_estimate(const lcsr_problem_t& p, const FreqTable& ft,
+                             const DcaParams& d, int64_t row0, int n_rows,
+                             int n_kc, uint16_t* dst, hipStream_t s) {
+  const int64_t D = p.head_dim, H = p.n_heads;
+  const int64_t t0 = row0 - p.chunk_start;
+  for (int c = 0; c < n_kc; ++c) {
+    RotateArgs a{};
+    a.src = (p.q_dtype == LCSR_FP32)
+                ? (const void*)((const float*)p.q + t0 * p.q_stride_t)
+                : (const void*)((const uint16_t*)p.q + t0 * p.q_stride_t);
+    a.src_dtype = p.q_dtype;
+    a.src_sh = p.q_stride_h;
+    a.src_st = p.q_stride_t;
+    a.dst = dst + (int64_t)c * H * kEstRows * D;
+    a.dst_sh = (int64_t)kEstRows * D;
+    a.dst_st = D;
+    a.n_heads = H;
+    a.n_tok = n_rows;
+    a.head_dim = D;
+    a.pos_offset = row0 - (int64_t)c * d.period;
+    a.mode = kPosAffine;
+    a.scale = 1.0f;
+    int rc = launch_rotate(a, ft, s);
+    if (rc) return rc;
+  }
+  return LCSR_OK;
+}
+
+}  // namespace lcsr

@@ -1,0 +1,126 @@
+"""Chunked sparse prefill of one attention layer, with sparsity refinement.
+
+The loop of the page "論文解説: Qwen2.5-1M" (0h-n0.github.io), section
+"アルゴリズム: DCAと疎アテンションの統合": the prompt is processed in prefill
+chunks; for each chunk the critical tokens are chosen from the chunk's last
+queries with continuous positions, then the chunk's attention is computed
+over them with DCA positions.  Chunked Prefill gives the 32,768-token chunk
+and the attention-recall check used by the refinement.
+
+Every numeric step runs in liblcsr.so; this module only sequences the calls
+on one stream and owns the KV cache buffers.
+"""
+
+import torch
+
+from . import ops
+
+
+class ChunkedSparsePrefill:
+    """One layer's KV cache plus the calls of the chunk loop.
+
+    K and V caches are bf16 [H_kv, max_ctx, D]; keys are stored rotated at
+    their DCA key position.  Budgets are per query head and may be raised by
+    `refine_chunk`.
+    """
+
+    def __init__(self, n_heads, n_kv_heads, head_dim, max_ctx, rope, dca, sm_scale,
+                 n_vert, n_slash, last_q=64, device="cuda", max_vert=None, max_slash=None):
+        self.H, self.Hkv, self.D = n_heads, n_kv_heads, head_dim
+        self.max_ctx = int(max_ctx)
+        self.rope, self.dca, self.sm_scale = rope, dca, float(sm_scale)
+        self.last_q = last_q
+        self.device = torch.device(device)
+        self.n_vert = [int(n_vert)] * n_heads if isinstance(n_vert, int) else list(n_vert)
+        self.n_slash = [int(n_slash)] * n_heads if isinstance(n_slash, int) else list(n_slash)
+        self.k_cache = torch.empty((n_kv_heads, self.max_ctx, head_dim), dtype=torch.bfloat16,
+                                   device=self.device)
+        self.v_cache = torch.empty_like(self.k_cache)
+        mv = max_vert or max(self.n_vert)
+        ms = max_slash or max(self.n_slash)
+        self.pattern = ops.Pattern(n_heads, mv, ms, self.device)
+
+    def append_kv(self, k_chunk, v_chunk, chunk_start):
+        """Rotate the chunk's keys into the K cache at P_k and copy V."""
+        n = k_chunk.shape[1]
+        pos = ops.dca_positions(chunk_start, n, self.dca, self.device)["pk"]
+        ops.rope_yarn_apply(k_chunk, pos, self.rope,
+                            out=self.k_cache[:, chunk_start:chunk_start + n])
+        ops.rope_yarn_apply(v_chunk, None, self.rope, rotate=False,
+                            out=self.v_cache[:, chunk_start:chunk_start + n])
+
+    def estimate(self, q_chunk, chunk_start, head_mask=None):
+        c1 = chunk_start + q_chunk.shape[1]
+        return ops.vs_pattern_estimate(
+            q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
+            self.n_vert, self.n_slash, self.pattern, last_q=self.last_q, head_mask=head_mask)
+
+    def attend(self, q_chunk, chunk_start, out=None, lse=None, stats=None, head_mask=None,
+               dense=False):
+        c1 = chunk_start + q_chunk.shape[1]
+        return ops.vs_sparse_attn_prefill(
+            q_chunk, self.k_cache[:, :c1], self.v_cache[:, :c1], chunk_start, self.rope,
+            self.dca, self.sm_scale, None if dense else self.pattern, out=out, lse=lse,
+            stats=stats, head_mask=head_mask, dense=dense)
+
+    def recall(self, q_chunk, chunk_start, rows, head_mask=None):
+        c1 = chunk_start + q_chunk.shape[1]
+        return ops.attn_recall_check(q_chunk, self.k_cache[:, :c1], chunk_start, self.rope,
+                                     self.dca, self.sm_scale, self.pattern, rows,
+                                     head_mask=head_mask)
+
+    def prefill_chunk(self, q_chunk, k_chunk, v_chunk, chunk_start, out=None, lse=None,
+                      stats=None):
+        """One chunk: KV append, pattern estimate, sparse attention."""
+        self.append_kv(k_chunk, v_chunk, chunk_start)
+        self.estimate(q_chunk, chunk_start)
+        return self.attend(q_chunk, chunk_start, out=out, lse=lse, stats=stats)
+
+    def refine_chunk(self, q_chunk, chunk_start, rows, out, lse=None, threshold=0.9,
+                     max_rounds=3):
+        """Sparsity refinement for one chunk: heads whose mean recall over
+        `rows` is under the threshold get doubled budgets (capped at the
+        number of keys), are re-estimated and re-attended; at most
+        `max_rounds` rounds.  Raised budgets carry over to later chunks.
+        Returns the per-round head recalls (host tensors)."""
+        c1 = chunk_start + q_chunk.shape[1]
+        history = []
+        for _ in range(max_rounds + 1):
+            _, _, rec = self.recall(q_chunk, chunk_start, rows)
+            mean = rec.mean(dim=1).cpu()
+            history.append(mean)
+            low = [bool(mean[h] < threshold) and
+                   (self.n_vert[h] < c1 or self.n_slash[h] < c1) for h in range(self.H)]
+            if len(history) > max_rounds or not any(low):
+                break
+            for h in range(self.H):
+                if low[h]:
+                    self.n_vert[h] = min(2 * self.n_vert[h], c1)
+                    self.n_slash[h] = min(2 * self.n_slash[h], c1)
+            need_v, need_s = max(self.n_vert), max(self.n_slash)
+            if need_v > self.pattern.max_vert or need_s > self.pattern.max_slash:
+                old = self.pattern
+                self.pattern = ops.Pattern(self.H, max(need_v, old.max_vert),
+                                           max(need_s, old.max_slash), self.device)
+                # keep the heads that are not re-estimated
+                for h in range(self.H):
+                    if not low[h]:
+                        self.pattern.vert_idx[h, :old.max_vert] = old.vert_idx[h]
+                        self.pattern.slash_idx[h, :old.max_slash] = old.slash_idx[h]
+                        self.pattern.vert_cnt[h] = old.vert_cnt[h]
+                        self.pattern.slash_cnt[h] = old.slash_cnt[h]
+            self.estimate(q_chunk, chunk_start, head_mask=low)
+            self.attend(q_chunk, chunk_start, out=out, lse=lse, head_mask=low)
+        return history
+
+    def run(self, q, k, v, chunk_size, out=None, lse=None, stats=None):
+        """Whole-prompt chunked prefill; q [H, N, D], k/v [H_kv, N, D]."""
+        N = q.shape[1]
+        if out is None:
+            out = torch.empty((self.H, N, self.D), dtype=torch.float32, device=self.device)
+        for c0 in range(0, N, chunk_size):
+            c1 = min(N, c0 + chunk_size)
+            self.prefill_chunk(q[:, c0:c1], k[:, c0:c1], v[:, c0:c1], c0,
+                               out=out[:, c0:c1], lse=None if lse is None else lse[:, c0:c1],
+                               stats=stats)
+        return out

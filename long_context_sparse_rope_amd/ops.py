@@ -1,0 +1,266 @@
+"""Thin Python binding of the five C-ABI calls (argument marshalling only).
+
+Each function has the name of its C entry point without the ``lcsr_``
+prefix.  Tensors are torch device tensors (PyTorch supplies device memory
+and the stream); every computation runs in liblcsr.so.
+"""
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _capi as C
+
+
+class LcsrError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"lcsr error {code}: {msg}")
+        self.code = code
+
+
+@dataclass(frozen=True)
+class RopeConfig:
+    """RoPE base and YaRN settings (lcsr_rope_t)."""
+    base: float = 1e4
+    yarn_factor: float = 1.0
+    orig_max_pos: int = 262144
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    freq_blend: bool = False
+
+    def c(self):
+        return C.lcsr_rope_t(self.base, self.yarn_factor, self.orig_max_pos, self.beta_fast,
+                             self.beta_slow, C.LCSR_ROPE_YARN_FREQ if self.freq_blend else 0)
+
+
+@dataclass(frozen=True)
+class DcaConfig:
+    """Dual Chunk Attention: chunk = C (0: off), local = W (lcsr_dca_t)."""
+    chunk: int = 0
+    local: int = 0
+
+    def c(self):
+        return C.lcsr_dca_t(self.chunk, self.local)
+
+
+def yarn_softmax_scale(head_dim, yarn_factor):
+    """1 / (t sqrt(D)) with sqrt(1/t) = 0.1 ln(s) + 1 (s <= 1: no scaling)."""
+    m = 1.0 if yarn_factor <= 1.0 else 0.1 * math.log(yarn_factor) + 1.0
+    return m * m / math.sqrt(head_dim)
+
+
+class Pattern:
+    """Device buffers of a vertical-slash pattern (lcsr_pattern_t)."""
+
+    def __init__(self, n_heads, max_vert, max_slash, device):
+        self.max_vert = int(max_vert)
+        self.max_slash = int(max_slash)
+        self.vert_idx = torch.full((n_heads, max(1, self.max_vert)), -1, dtype=torch.int32,
+                                   device=device)
+        self.slash_idx = torch.full((n_heads, max(1, self.max_slash)), -1, dtype=torch.int32,
+                                    device=device)
+        self.vert_cnt = torch.zeros(n_heads, dtype=torch.int32, device=device)
+        self.slash_cnt = torch.zeros(n_heads, dtype=torch.int32, device=device)
+
+    @classmethod
+    def from_lists(cls, verts, slashes, device, max_vert=None, max_slash=None):
+        """Pattern from per-head index lists (host), sorted ascending."""
+        H = len(verts)
+        mv = max_vert or max(1, max(len(v) for v in verts))
+        ms = max_slash or max(1, max(len(s) for s in slashes))
+        p = cls(H, mv, ms, device)
+        for h in range(H):
+            v = torch.as_tensor(sorted(int(x) for x in verts[h]), dtype=torch.int32)
+            s = torch.as_tensor(sorted(int(x) for x in slashes[h]), dtype=torch.int32)
+            p.vert_idx[h, :len(v)] = v.to(device)
+            p.slash_idx[h, :len(s)] = s.to(device)
+            p.vert_cnt[h] = len(v)
+            p.slash_cnt[h] = len(s)
+        return p
+
+    def c(self):
+        return C.lcsr_pattern_t(self.vert_idx.data_ptr(), self.vert_cnt.data_ptr(),
+                                self.max_vert, self.slash_idx.data_ptr(),
+                                self.slash_cnt.data_ptr(), self.max_slash)
+
+    def lists(self):
+        """Per-head (verticals, slashes) as host int64 tensors."""
+        vi, vc = self.vert_idx.cpu(), self.vert_cnt.cpu()
+        si, sc = self.slash_idx.cpu(), self.slash_cnt.cpu()
+        return ([vi[h, :vc[h]].long() for h in range(vi.shape[0])],
+                [si[h, :sc[h]].long() for h in range(si.shape[0])])
+
+
+def _check(rc):
+    if rc != 0:
+        raise LcsrError(rc, C.load().lcsr_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return C.LCSR_BF16
+    if t.dtype == torch.float32:
+        return C.LCSR_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _host_i32(values):
+    """Host int32 array for a (host) pointer argument, kept alive by the caller."""
+    return (ctypes.c_int32 * len(values))(*[int(x) for x in values])
+
+
+def _ptr(arr):
+    return None if arr is None else ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _head_mask(mask, H):
+    if mask is None:
+        return None
+    if len(mask) != H:
+        raise ValueError("head_mask needs one entry per query head")
+    return _host_i32([bool(x) for x in mask])
+
+
+def _problem(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale):
+    if q.dim() != 3 or k_cache.dim() != 3:
+        raise ValueError("q is [H, L, D], caches are [H_kv, N, D]")
+    if q.stride(2) != 1 or k_cache.stride(2) != 1 or (v_cache is not None and v_cache.stride(2) != 1):
+        raise ValueError("the head dimension must be contiguous")
+    if k_cache.dtype != torch.bfloat16 or (v_cache is not None and v_cache.dtype != torch.bfloat16):
+        raise TypeError("caches must be bfloat16")
+    if v_cache is not None and v_cache.stride() != k_cache.stride():
+        raise ValueError("K and V caches must share strides")
+    H, L, D = q.shape
+    return C.lcsr_problem_t(
+        q.data_ptr(), _dtype_code(q), q.stride(0), q.stride(1),
+        k_cache.data_ptr(), 0 if v_cache is None else v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), H, k_cache.shape[0], D,
+        int(chunk_start), L, rope.c(), dca.c(), float(sm_scale))
+
+
+_ws_cache = {}
+
+
+def _workspace(kind, prob, max_vert, max_slash, device, workspace):
+    nbytes = C.load().lcsr_workspace_bytes(kind, ctypes.byref(prob), max_vert, max_slash)
+    if nbytes == 0:
+        _check(C.LCSR_EINVAL)
+    if workspace is not None:
+        return workspace
+    key = (kind, str(device))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def workspace_bytes(kind, q, k_cache, chunk_start, rope, dca, sm_scale=1.0, max_vert=0,
+                    max_slash=0):
+    prob = _problem(q, k_cache, None, chunk_start, rope, dca, sm_scale)
+    return C.load().lcsr_workspace_bytes(kind, ctypes.byref(prob), max_vert, max_slash)
+
+
+def rope_yarn_apply(x, pos, rope, out=None, scale=1.0, rotate=True, stream=None):
+    """out[h, t] = scale * R(pos[t]) x[h, t] in bf16 (lcsr_rope_yarn_apply)."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [H, n, D] with a contiguous last dimension")
+    H, n, D = x.shape
+    if out is None:
+        out = torch.empty((H, n, D), dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or out.shape != x.shape or out.stride(2) != 1:
+        raise ValueError("out must be bf16 with the shape of x")
+    flags = 0 if rotate else C.LCSR_ROPE_NO_ROTATE
+    r = rope.c()
+    _check(C.load().lcsr_rope_yarn_apply(
+        x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1), out.data_ptr(), out.stride(0),
+        out.stride(1), H, n, D, None if pos is None else pos.data_ptr(), ctypes.byref(r),
+        float(scale), flags, _stream(stream)))
+    return out
+
+
+def dca_positions(tok_start, n_tok, dca, device, stream=None):
+    """DCA position maps {pk, intra, succ, inter} as int32 tensors."""
+    outs = {k: torch.empty(n_tok, dtype=torch.int32, device=device)
+            for k in ("pk", "intra", "succ", "inter")}
+    d = dca.c()
+    _check(C.load().lcsr_dca_positions(int(tok_start), int(n_tok), ctypes.byref(d),
+                                       outs["pk"].data_ptr(), outs["intra"].data_ptr(),
+                                       outs["succ"].data_ptr(), outs["inter"].data_ptr(),
+                                       _stream(stream)))
+    return outs
+
+
+def vs_pattern_estimate(q, k_cache, chunk_start, rope, dca, sm_scale, n_vert, n_slash,
+                        pattern, last_q=64, head_mask=None, vert_score=None,
+                        slash_score=None, select_only=False, workspace=None, stream=None):
+    """Fill `pattern` with each head's verticals and slashes (lcsr_vs_pattern_estimate)."""
+    prob = _problem(q, k_cache, None, chunk_start, rope, dca, sm_scale)
+    H = q.shape[0]
+    if len(n_vert) != H or len(n_slash) != H:
+        raise ValueError("one budget per query head")
+    nv = _host_i32(n_vert)
+    ns = _host_i32(n_slash)
+    hm = _head_mask(head_mask, H)
+    ws = _workspace(C.LCSR_WS_ESTIMATE, prob, pattern.max_vert, pattern.max_slash, q.device,
+                    workspace)
+    pat = pattern.c()
+    flags = C.LCSR_EST_SELECT_ONLY if select_only else 0
+    _check(C.load().lcsr_vs_pattern_estimate(
+        ctypes.byref(prob), int(last_q), _ptr(nv), _ptr(ns), _ptr(hm), ctypes.byref(pat),
+        None if vert_score is None else vert_score.data_ptr(),
+        None if slash_score is None else slash_score.data_ptr(), flags, ws.data_ptr(),
+        ws.numel(), _stream(stream)))
+    return pattern
+
+
+def vs_sparse_attn_prefill(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale, pattern,
+                           out=None, out_dtype=torch.float32, lse=None, stats=None,
+                           head_mask=None, dense=False, workspace=None, stream=None):
+    """Sparse causal attention of the chunk's rows (lcsr_vs_sparse_attn_prefill).
+
+    Returns (out [H, L, D], lse [H, L] or None)."""
+    prob = _problem(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale)
+    H, L, D = q.shape
+    if out is None:
+        out = torch.empty((H, L, D), dtype=out_dtype, device=q.device)
+    ms = 1 if pattern is None else pattern.max_slash
+    mv = 1 if pattern is None else pattern.max_vert
+    ws = _workspace(C.LCSR_WS_ATTN, prob, mv, ms, q.device, workspace)
+    pat_s = None if pattern is None else pattern.c()
+    pat = None if pat_s is None else ctypes.byref(pat_s)
+    hm = _head_mask(head_mask, H)
+    _check(C.load().lcsr_vs_sparse_attn_prefill(
+        ctypes.byref(prob), pat, _ptr(hm), out.data_ptr(), _dtype_code(out),
+        out.stride(0), out.stride(1), None if lse is None else lse.data_ptr(),
+        None if stats is None else stats.data_ptr(), C.LCSR_ATTN_DENSE if dense else 0,
+        ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def attn_recall_check(q, k_cache, chunk_start, rope, dca, sm_scale, pattern, rows,
+                      head_mask=None, workspace=None, stream=None):
+    """(lse_full, lse_sparse, recall), each [H, n_rows] (lcsr_attn_recall_check)."""
+    prob = _problem(q, k_cache, None, chunk_start, rope, dca, sm_scale)
+    H = q.shape[0]
+    n = rows.numel()
+    outs = [torch.empty((H, n), dtype=torch.float32, device=q.device) for _ in range(3)]
+    ws = _workspace(C.LCSR_WS_RECALL, prob, pattern.max_vert, pattern.max_slash, q.device,
+                    workspace)
+    pat = pattern.c()
+    hm = _head_mask(head_mask, H)
+    if rows.dtype != torch.int32:
+        raise TypeError("rows must be int32")
+    _check(C.load().lcsr_attn_recall_check(
+        ctypes.byref(prob), ctypes.byref(pat), _ptr(hm), rows.data_ptr(), n,
+        outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream(stream)))
+    return tuple(outs)

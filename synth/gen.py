@@ -7,18 +7,26 @@ oracle consume exactly the tensors made here.
 Recipe (all magnitudes are stated as the logit excess E over the background,
 whose standard deviation is 1 at the 1/sqrt(D) scale):
 
-* noise: Q, K, V iid N(0, 1) in fp32; bf16 configs are then rounded to bf16
-  (torch's round-to-nearest-even), the tiny config stays fp32 (the library
-  rounds it on entry);
+* noise: V iid N(0, 1); Q and K iid N(0, 1) for the tiny config, and
+  N(0, NOISE_QK^2) under the planted components for the other layers, so
+  that their elements keep roughly unit scale while the far-field logits stay
+  flat (background logit std ~0.7), as trained heads have; bf16 configs are
+  rounded to bf16 (torch's round-to-nearest-even), the tiny config stays fp32
+  (the library rounds it on entry);
 * "sinks_band" / "sinks_every" (7B/14B-shaped layers): per KV head a unit
   sink direction u in the four lowest-frequency rotary planes (planes
   D/2-4 .. D/2-1, both halves), added with amplitude sqrt(E_sink sqrt(D)) to
   the sink keys and, scaled by a per-query-head factor, to every query; and a
-  unit band direction e spread evenly over rotary planes 10..47 with random
-  phases, added to every query and key.  After rotation, q.k of the shared
-  band direction is a sum of cosines of (i - j) * theta_p, so it peaks on the
-  main diagonal and fades with distance: a local band of slash lines.  Sinks
-  sit at columns 0..15, or at multiples of `sink_every`;
+  band component b_t with equal weight in rotary planes 10..47, added to
+  query and key t of the KV head (amplitude sqrt(E_band sqrt(D)), per-head
+  factor on the query side).  In plane p, b_t has the phase phi_{t,p}, a
+  Gaussian random walk along t (step variance 2 / BAND_DRIFT) from a random
+  start: slowly drifting shared content.  After rotation, q_i.k_j of the band
+  is a sum over planes of cos((i - j) theta_p + phi_{i,p} - phi_{j,p}): it
+  peaks on the main diagonal and fades both as the planes decohere with
+  distance and as the content drifts (mean factor exp(-|i - j| / BAND_DRIFT)),
+  a local band of slash lines with no coherent far-range ripple.  Sinks sit
+  at columns 0..15, or at multiples of `sink_every`;
 * "far_sinks_stripes" (refinement stress): 64 sinks per KV head at seeded
   uniform positions, plus periodic diagonal stripes: a harmonic code
   c(a) = (cos(2 pi k a / P), sin(2 pi k a / P))_{k=1..8} / sqrt(8) in rotary
@@ -35,8 +43,10 @@ import math
 import numpy as np
 import torch
 
+NOISE_QK = 0.5
 E_SINK = 3.0
-E_BAND = 3.0
+E_BAND = 4.0
+BAND_DRIFT = 32768.0
 E_FAR_SINK = 6.0
 E_STRIPE = 4.0
 BAND_PLANES = (10, 48)
@@ -61,15 +71,20 @@ def _plane_dims(d, planes):
     return np.arange(lo, hi), np.arange(lo, hi) + half
 
 
-def _band_direction(cfg, g):
+def _band_component(cfg, g, n, device):
+    """Unit-norm band vector of every token, [n, D] fp32 on `device`."""
     d = cfg.head_dim
-    rng = _rng(cfg, 101, g)
     a, b = _plane_dims(d, BAND_PLANES)
-    phase = rng.uniform(0, 2 * math.pi, a.size)
-    e = np.zeros(d)
-    e[a] = np.cos(phase)
-    e[b] = np.sin(phase)
-    return e / np.linalg.norm(e)
+    rng = _rng(cfg, 101, g)
+    start = torch.tensor(rng.uniform(0, 2 * math.pi, a.size), dtype=torch.float64,
+                         device=device)
+    steps = _noise((n, a.size), _torch_seed(cfg, 105, g), device).double()
+    steps *= math.sqrt(2.0 / BAND_DRIFT)
+    phase = start + torch.cumsum(steps, dim=0)
+    comp = torch.zeros((n, d), dtype=torch.float32, device=device)
+    comp[:, a] = (torch.cos(phase) / math.sqrt(a.size)).float()
+    comp[:, b] = (torch.sin(phase) / math.sqrt(a.size)).float()
+    return comp
 
 
 def _sink_direction(cfg, g):
@@ -151,21 +166,20 @@ def generate(cfg, device="cpu", n_tokens=None):
     out_v = torch.empty((G, n, D), dtype=torch.bfloat16, device=device)
     group = H // G
     for g in range(G):
-        k = _noise((n, D), _torch_seed(cfg, 2, g), device)
+        k = _noise((n, D), _torch_seed(cfg, 2, g), device) * NOISE_QK
         per_head_q = []
+        band = None
         if cfg.planting in ("sinks_band", "sinks_every"):
-            e = torch.tensor(_band_direction(cfg, g), dtype=torch.float32,
-                             device=device)
+            band = _band_component(cfg, g, n, device)
             u = torch.tensor(_sink_direction(cfg, g), dtype=torch.float32,
                              device=device)
-            k += _amp(E_BAND, D) * e
+            k += _amp(E_BAND, D) * band
             sp = sink_positions(cfg, g)
             sinks = torch.as_tensor(sp[sp < n], device=device)
             k[sinks] += _amp(E_SINK, D) * u
             for hh in range(group):
                 h = g * group + hh
-                per_head_q.append(_amp(E_BAND, D) * float(fac["band"][h]) * e
-                                  + _amp(E_SINK, D) * float(fac["sink"][h]) * u)
+                per_head_q.append(_amp(E_SINK, D) * float(fac["sink"][h]) * u)
         elif cfg.planting == "far_sinks_stripes":
             u = torch.tensor(_sink_direction(cfg, g), dtype=torch.float32,
                              device=device)
@@ -186,11 +200,14 @@ def generate(cfg, device="cpu", n_tokens=None):
             torch.bfloat16)
         for hh in range(group):
             h = g * group + hh
-            q = _noise((n, D), _torch_seed(cfg, 1, h), device)
+            q = _noise((n, D), _torch_seed(cfg, 1, h), device) * NOISE_QK
             if per_head_q:
                 q += per_head_q[hh]
+            if band is not None:
+                q += (_amp(E_BAND, D) * float(fac["band"][h])) * band
             if cfg.planting == "far_sinks_stripes":
                 q += (_amp(E_STRIPE, D) * float(fac["stripe"][h])) * codes[idx]
             out_q[h] = q.to(torch.bfloat16)
             del q
+        del band
     return out_q, out_k, out_v
