@@ -1,0 +1,198 @@
+"""Benchmark: one attention layer's chunked sparse prefill on one MI355X.
+
+A step is the whole chunk loop over the prompt (per 32K chunk: keys rotated
+into the KV cache at their DCA positions, V copied, vertical-slash pattern
+estimated from the chunk's last 64 queries, sparse attention of the chunk),
+inputs resident in HBM.  Default workload: the 7B-shaped layer (28 query /
+4 KV heads, head_dim 128, bf16) at 1,048,576 tokens with DCA (C = 262,144,
+W = 32,768), YaRN s = 4, budgets 1000 verticals + 6096 slashes.
+
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: this
+build runs on one GPU.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import long_context_sparse_rope_amd as L  # noqa: E402
+import synth  # noqa: E402
+from synth.configs import CONFIGS  # noqa: E402
+
+METRIC = ("ms + effective TFLOP/s per 1M-token sparse prefill (one layer); "
+          "% bf16 MFMA peak")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+
+
+def make_layer(cfg, dev):
+    rope = L.RopeConfig(base=cfg.rope_base, yarn_factor=cfg.yarn_factor,
+                        orig_max_pos=cfg.yarn_orig_max_pos)
+    dca = L.DcaConfig(cfg.dca_chunk, cfg.dca_local)
+    sm = L.yarn_softmax_scale(cfg.head_dim, cfg.yarn_factor)
+    return L.ChunkedSparsePrefill(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, rope,
+                                  dca, sm, cfg.n_vert, cfg.n_slash, cfg.last_q, dev)
+
+
+class StageTimer:
+    """HIP events on the current stream around each stage of each chunk."""
+
+    def __init__(self):
+        self.marks = []
+
+    def mark(self, name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.marks.append((name, ev))
+
+    def totals(self):
+        out = {}
+        for (name, a), (_, b) in zip(self.marks[:-1], self.marks[1:]):
+            if name.startswith("end"):
+                continue
+            out.setdefault(name, []).append(a.elapsed_time(b))
+        return out
+
+
+def run_step(layer, cfg, q, k, v, out, stats, timer=None):
+    for c in range(cfg.n_chunks):
+        c0, lc = cfg.chunk_bounds(c)
+        c1 = c0 + lc
+        if timer:
+            timer.mark("kv_append")
+        layer.append_kv(k[:, c0:c1], v[:, c0:c1], c0)
+        if timer:
+            timer.mark("estimate")
+        layer.estimate(q[:, c0:c1], c0)
+        if timer:
+            timer.mark("attention")
+        layer.attend(q[:, c0:c1], c0, out=out[:, c0:c1], stats=stats)
+        if timer:
+            timer.mark("end")
+
+
+def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the same workload: sparse
+    attention rows of the last chunk (first query head, the GPU's own
+    pattern), as many as fit in about `budget_s` seconds."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
+    c1 = c0 + lc
+    h, g = 0, 0
+    verts, slashes = layer.pattern.lists()
+    vh, sh = verts[h].numpy(), slashes[h].numpy()
+    t_setup = time.perf_counter()
+    K = k[g, :c1].float().cpu().numpy().astype(np.float64)
+    V = v[g, :c1].float().cpu().numpy().astype(np.float64)
+    th = oracle.rope_inv_freq(cfg.head_dim, cfg.rope_base)
+    ctx = oracle.KeyContext(K, V, th, cfg.dca_chunk, cfg.dca_local)
+    ctx.k_dca()
+    setup_s = time.perf_counter() - t_setup
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(np.arange(c0, c1), size=4096, replace=False))
+    qh = q[h, rows].float().cpu().numpy().astype(np.float64)
+    sm = layer.sm_scale
+    done, pairs = 0, 0
+    t0 = time.perf_counter()
+    while done < rows.size and time.perf_counter() - t0 < budget_s:
+        blk = slice(done, min(rows.size, done + 64))
+        _, _, sizes = oracle.sparse_rows(qh[blk], rows[blk], ctx, vh, sh, sm)
+        pairs += int(sizes.sum())
+        done = blk.stop
+    el = time.perf_counter() - t0
+    flops = 4.0 * cfg.head_dim * pairs
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 sparse attention of {done} sampled rows of the last 32K chunk "
+                       f"(query head 0, GPU pattern), {el:.1f} s after {setup_s:.1f} s of "
+                       f"key rotation; {pairs} critical pairs"),
+            "seconds": el, "rows": done}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="7b_1m_dca")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = synth.generate(cfg, dev)
+    layer = make_layer(cfg, dev)
+    out = torch.empty((cfg.n_heads, cfg.seq_len, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    stats = torch.zeros(2, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_step(layer, cfg, q, k, v, out, stats)
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
+    stats.zero_()
+    timer = StageTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(layer, cfg, q, k, v, out, stats, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] {args.steps} timed steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    ms_step = wall * 1e3 / args.steps
+    st = stats.cpu().tolist()
+    sel_pairs = st[1] / args.steps
+    exe_pairs = st[0] / args.steps
+    alg_flops = 4.0 * cfg.head_dim * sel_pairs            # per step
+    exe_flops = 4.0 * cfg.head_dim * exe_pairs
+    stages = {k_: sum(v_) / args.steps for k_, v_ in timer.totals().items()}
+    attn_calls = cfg.n_chunks
+    attn_ms_call = stages["attention"] / attn_calls
+    achieved = alg_flops / attn_calls / (attn_ms_call * 1e-3) / 1e12
+    exec_rate = exe_flops / attn_calls / (attn_ms_call * 1e-3) / 1e12
+    eff = alg_flops / (ms_step * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "vs_sparse_attn_prefill (pattern aux + attention)",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "executed_tflops": round(exec_rate, 2),
+                "executed_frac": round(exec_rate / PEAK_BF16_TFLOPS, 4),
+                "avg_call_ms": round(attn_ms_call, 4)}
+    rec = {
+        "metric": METRIC, "value": round(eff, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "seq_len": cfg.seq_len,
+                   "prefill_chunk": cfg.prefill_chunk, "dca_chunk": cfg.dca_chunk,
+                   "dca_local": cfg.dca_local, "yarn_factor": cfg.yarn_factor,
+                   "n_vert": cfg.n_vert, "n_slash": cfg.n_slash, "out_dtype": "bf16"},
+        "stage_ms": {k_: round(v_, 3) for k_, v_ in stages.items()},
+        "algorithmic_tflop_per_step": round(alg_flops / 1e12, 3),
+        "executed_tflop_per_step": round(exe_flops / 1e12, 3),
+        "waste_ratio": round(exe_pairs / max(sel_pairs, 1), 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, layer, q, k, v, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -59,18 +59,33 @@ EstimateLayout estimate_layout(const lcsr_problem_t& p) {
   return L;
 }
 
-AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_slash, bool with_q) {
+AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_slash,
+                       bool attention) {
   AttnLayout L{};
   const int64_t H = p.n_heads, D = p.head_dim;
   L.n_ctx = p.chunk_start + p.chunk_len;
-  L.n_words = (L.n_ctx + 31) / 32 + 8;   // zero padding: reads reach 192 bits past n_ctx
+  L.n_words = (L.n_ctx + 31) / 32 + 2 * kBitPad;   // per-head stride, zero words at both ends
   L.n_var = p.dca.chunk > 0 ? 3 : 1;
-  L.q_rot = with_q ? align256((size_t)L.n_var * H * p.chunk_len * D * 2) : 0;
-  L.off_bits = align256((size_t)H * L.n_words * 4);
-  L.col_bits = L.off_bits;
-  L.runs = align256((size_t)H * (max_slash > 0 ? max_slash : 1) * 2 * 4);
-  L.run_cnt = align256((size_t)H * 4);
-  L.total = L.q_rot + L.off_bits + L.col_bits + L.runs + L.run_cnt;
+  L.n_qt = (p.chunk_len + kTileQ - 1) / kTileQ;
+  L.with_vl = attention;
+  if (max_vert < 1) max_vert = 1;
+  if (max_slash < 1) max_slash = 1;
+  size_t off = 0;
+  L.o_q_rot = off;
+  off += attention ? align256((size_t)L.n_var * H * p.chunk_len * D * 2) : 0;
+  L.o_off_bits = off;
+  off += align256((size_t)H * L.n_words * 4);
+  L.o_col_bits = off;
+  off += align256((size_t)H * L.n_words * 4);
+  L.o_runs = off;
+  off += align256((size_t)H * max_slash * 2 * 4);
+  L.o_run_cnt = off;
+  off += align256((size_t)H * 4);
+  L.o_vl = off;
+  off += attention ? align256((size_t)H * L.n_qt * max_vert * 4) : 0;
+  L.o_vl_cnt = off;
+  off += attention ? align256((size_t)H * L.n_qt * 4) : 0;
+  L.total = off;
   return L;
 }
 
@@ -156,11 +171,10 @@ const char* lcsr_last_error(void) { return g_err; }
 size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert,
                             int32_t max_slash) {
   if (!p || validate_problem(p, false) != LCSR_OK) return 0;
-  (void)max_vert;
   switch (which) {
     case LCSR_WS_ESTIMATE: return estimate_layout(*p).total;
-    case LCSR_WS_ATTN: return attn_layout(*p, max_slash, true).total;
-    case LCSR_WS_RECALL: return attn_layout(*p, max_slash, false).total;
+    case LCSR_WS_ATTN: return attn_layout(*p, max_vert, max_slash, true).total;
+    case LCSR_WS_RECALL: return attn_layout(*p, max_vert, max_slash, false).total;
     default: set_error("unknown workspace kind %d", which); return 0;
   }
 }
@@ -275,7 +289,7 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
   head_mask_bits(p, head_mask, &hm);
   lcsr_pattern_t empty{};
   const lcsr_pattern_t& P = (dense && !pat) ? empty : *pat;
-  const AttnLayout L = attn_layout(*p, dense ? 1 : P.max_slash, true);
+  const AttnLayout L = attn_layout(*p, dense ? 1 : P.max_vert, dense ? 1 : P.max_slash, true);
   if (!ws || ws_bytes < L.total || !aligned16(ws))
     return fail(LCSR_EWORKSPACE, "attention needs %zu workspace bytes (16-byte aligned), got %zu",
                 L.total, ws_bytes);
@@ -297,7 +311,7 @@ int lcsr_attn_recall_check(const lcsr_problem_t* p, const lcsr_pattern_t* pat,
     return fail(LCSR_EINVAL, "rows and the three outputs must be non-NULL");
   uint64_t hm;
   head_mask_bits(p, head_mask, &hm);
-  const AttnLayout L = attn_layout(*p, pat->max_slash, false);
+  const AttnLayout L = attn_layout(*p, pat->max_vert, pat->max_slash, false);
   if (!ws || ws_bytes < L.total || !aligned16(ws))
     return fail(LCSR_EWORKSPACE, "recall needs %zu workspace bytes (16-byte aligned), got %zu",
                 L.total, ws_bytes);

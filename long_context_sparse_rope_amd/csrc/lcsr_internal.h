@@ -30,6 +30,7 @@ constexpr int kMaxGroup = 16;            // n_heads / n_kv_heads
 constexpr int kTileQ = 128;              // query rows per attention workgroup
 constexpr int kTileK = 64;               // keys per tile (attention, estimate)
 constexpr int kEstRows = 64;             // largest last_q
+constexpr int kBitPad = 8;               // zero words before and after each head's bitmap
 
 // fp64 inverse frequencies, built on the host from lcsr_rope_t.
 struct FreqTable {
@@ -141,11 +142,13 @@ struct EstimateLayout {
   size_t q_est, part, lse, vscore, sscore, diag, total;
 };
 struct AttnLayout {
-  int64_t n_ctx, n_words, n_var;
-  size_t q_rot, off_bits, col_bits, runs, run_cnt, total;
+  int64_t n_ctx, n_words, n_var, n_qt;
+  bool with_vl;  // per-tile leftover vertical lists (attention only)
+  size_t o_q_rot, o_off_bits, o_col_bits, o_runs, o_run_cnt, o_vl, o_vl_cnt, total;
 };
 EstimateLayout estimate_layout(const lcsr_problem_t& p);
-AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_slash, bool with_q);
+AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_slash,
+                       bool attention);
 
 // ---------------------------------------------------------------- kernels
 struct HeadSet {

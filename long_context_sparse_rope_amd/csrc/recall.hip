@@ -91,8 +91,8 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
   __syncthreads();
   const int g = h / a.G;
   const uint16_t* kb = a.k + (int64_t)g * a.kv_sh;
-  const uint32_t* ob = a.off_bits + (int64_t)h * a.n_words;
-  const uint32_t* cb = a.col_bits + (int64_t)h * a.n_words;
+  const uint32_t* ob = a.off_bits + (int64_t)h * a.n_words + kBitPad;
+  const uint32_t* cb = a.col_bits + (int64_t)h * a.n_words + kBitPad;
   const int64_t qc = a.dca.period ? i / a.dca.period : 0;
   float mf = -INFINITY, lf = 0.f, ms = -INFINITY, ls = 0.f;
   for (int64_t j = threadIdx.x; j <= i; j += kRecallThreads) {
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
 int run_recall(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head_mask,
                const int32_t* rows, int32_t n_rows, float* lse_full, float* lse_sparse,
                float* recall, char* ws, hipStream_t s) {
-  const AttnLayout L = attn_layout(p, pat.max_slash, false);
+  const AttnLayout L = attn_layout(p, pat.max_vert, pat.max_slash, false);
   int rc = build_pattern_aux(p, pat, head_mask, false, L, ws, s);
   if (rc) return rc;
   RecallArgs a{};
@@ -166,8 +166,8 @@ int run_recall(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head
   a.n_ctx = L.n_ctx;
   a.dca = make_dca(&p.dca);
   a.scale_log2 = p.sm_scale * kLog2e;
-  a.off_bits = reinterpret_cast<const uint32_t*>(ws + L.q_rot);
-  a.col_bits = reinterpret_cast<const uint32_t*>(ws + L.q_rot + L.off_bits);
+  a.off_bits = reinterpret_cast<const uint32_t*>(ws + L.o_off_bits);
+  a.col_bits = reinterpret_cast<const uint32_t*>(ws + L.o_col_bits);
   a.n_words = L.n_words;
   a.head_mask = head_mask;
   a.rows = rows;

@@ -10,8 +10,8 @@ import torch
 import oracle
 import synth
 from synth.configs import TINY, SEVEN_B_128K, scaled
-from tests.gpu_util import (DEV, compare, lse_compare, host64, oracle_inputs, rope_of, dca_of,
-                            oracle_freqs)
+from tests.gpu_util import (DEV, MAX_ABS, MEAN_ABS, compare, lse_compare, host64,
+                            oracle_inputs, rope_of, dca_of, oracle_freqs)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,7 +167,14 @@ def _attn_case(cfg, c0, lc, verts, slashes, dense=False, out_dtype=torch.float32
         else:
             ro, rl, sizes = oracle.sparse_rows(qo[h, c0:c1], rows, ctx, np.array(verts[h]),
                                                np.array(slashes[h]), layer.sm_scale)
-        compare(host64(out[h]), ro)
+        if out_dtype == torch.bfloat16:
+            # the bf16 store adds up to half an ulp of |O| on top of the fp32 bar
+            g = host64(out[h])
+            d = np.abs(g - ro)
+            assert np.all(d <= MAX_ABS + 2.0 ** -9 * np.abs(ro)), d.max()
+            assert d.mean() <= MEAN_ABS + np.mean(2.0 ** -9 * np.abs(ro))
+        else:
+            compare(host64(out[h]), ro)
         lse_compare(host64(lse[h]), rl)
         sizes_total += int(np.sum(sizes))
     st = stats.cpu().tolist()
