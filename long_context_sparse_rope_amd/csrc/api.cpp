@@ -63,11 +63,16 @@ AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_sl
                        bool attention) {
   AttnLayout L{};
   const int64_t H = p.n_heads, D = p.head_dim;
+  const int64_t G = p.n_kv_heads > 0 ? p.n_heads / p.n_kv_heads : 1;
   L.n_ctx = p.chunk_start + p.chunk_len;
   L.n_words = (L.n_ctx + 31) / 32 + 2 * kBitPad;   // per-head stride, zero words at both ends
   L.n_var = p.dca.chunk > 0 ? 3 : 1;
-  L.n_qt = (p.chunk_len + kTileQ - 1) / kTileQ;
-  L.with_vl = attention;
+  L.n_rb = (p.chunk_len + kRowBlock - 1) / kRowBlock;
+  L.n_sub = (G + kMaxAttnWaves - 1) / kMaxAttnWaves;
+  L.nw = (G + L.n_sub - 1) / L.n_sub;
+  L.n_wgg = p.n_kv_heads * L.n_sub;
+  L.ubw = (L.n_ctx + 32 * kGranule - 1) / (32 * kGranule);
+  L.with_plan = attention;
   if (max_vert < 1) max_vert = 1;
   if (max_slash < 1) max_slash = 1;
   size_t off = 0;
@@ -81,10 +86,12 @@ AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_sl
   off += align256((size_t)H * max_slash * 2 * 4);
   L.o_run_cnt = off;
   off += align256((size_t)H * 4);
+  L.o_union = off;
+  off += attention ? align256((size_t)L.n_wgg * L.n_rb * L.ubw * 4) : 0;
   L.o_vl = off;
-  off += attention ? align256((size_t)H * L.n_qt * max_vert * 4) : 0;
+  off += attention ? align256((size_t)H * L.n_rb * max_vert * 4) : 0;
   L.o_vl_cnt = off;
-  off += attention ? align256((size_t)H * L.n_qt * 4) : 0;
+  off += attention ? align256((size_t)H * L.n_rb * 4) : 0;
   L.total = off;
   return L;
 }

@@ -8,27 +8,29 @@
 // softmax: deepseekmodel.com long-context architecture page, §3.2.
 //
 // Work decomposition (our design; the pages give no kernel):
-//  * a workgroup = one query head x 128 query rows (4 waves x 32 rows), two
-//    workgroups per CU;
-//  * slash offsets are merged into runs (consecutive offsets at most 128
-//    apart); run [oa, ob] covers the key span [r0 - ob, r0 + 127 - oa] of the
-//    tile, cut at DCA chunk edges into 64-key tiles;
-//  * verticals outside every span of the tile are listed per (head, tile)
-//    by a pre-kernel and gathered 64 at a time;
+//  * a workgroup = the query heads of one KV head (up to 8, one wave each)
+//    x one block of 32 query rows; every wave multiplies the same K/V tiles,
+//    so a tile is read from HBM once for all heads of the group;
+//  * a planning kernel marks, per (KV group, row block), the 16-key granules
+//    that any head's slash runs reach (run [oa, ob] reaches keys
+//    [r0 - ob, rlast - oa]); the attention walks the marked granules in
+//    64-key tiles (cut at DCA chunk edges), and lists per head the verticals
+//    in unmarked granules, which are gathered 64 at a time;
 //  * K and V tiles go straight from HBM to LDS (global_load_lds_dwordx4,
-//    16-byte chunks XOR-swizzled by row), double buffered: the next tile is
-//    in flight while the current one is multiplied;
-//  * per (wave, key tile) the pair mask is: key <= row and (offset bit or
-//    column bit); tiles a wave does not touch are skipped, tiles it fully
-//    covers run without a mask;
+//    16-byte chunks XOR-swizzled by row) through a ring of four stages: three
+//    tiles are in flight while one is multiplied;
+//  * per (wave, key tile) the pair mask is: key <= row and (offset bit of the
+//    wave's head or column bit in a marked granule); tiles a head does not
+//    touch are skipped by its wave, tiles it fully covers run unmasked;
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (V^T read
 //    with the LDS transpose load ds_read_b64_tr_b16): each lane owns one
 //    query row, so the softmax max / sum and the O rescale are in-lane; the
 //    row max is only raised when it grows by more than 2^8 (the exponent
 //    bound keeps p <= 256), and the row sum adds the bf16 weights the PV
 //    product uses (v_dot2_f32_bf16);
-//  * the DCA relation of a (wave, tile) pair picks one of three pre-rotated
-//    query variants (intra / successive / inter).
+//  * the DCA relation of the row block and a tile picks one of three
+//    pre-rotated query variants (intra / successive / inter).
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -40,9 +42,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kStages = 4;             // LDS ring of K/V tiles
+constexpr int kRunGap = kRowBlock;     // offsets at most this far apart share a run
+constexpr int kGranPerChunk = 64 * 32; // granules covered by one 64-word bitmap chunk
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -56,18 +59,16 @@ struct AttnArgs {
   int32_t H, G, n_var;
   int64_t c0, L, n_ctx;
   int64_t period;          // S (0: DCA off)
-  int64_t n_qt;            // query tiles
-  int64_t n_blocks;        // H * n_qt
   float scale_log2;
   const uint32_t* __restrict__ off_bits;  // [H][n_words]
   const uint32_t* __restrict__ col_bits;  // [H][n_words]
   int64_t n_words;
-  const int32_t* __restrict__ runs;       // [H][max_runs][2]
-  const int32_t* __restrict__ run_cnt;    // [H]
-  int32_t max_runs;
-  const int32_t* __restrict__ vl;         // [H][n_qt][max_vert] leftover verticals
-  const int32_t* __restrict__ vl_cnt;     // [H][n_qt]
+  const uint32_t* __restrict__ ubits;     // [n_wgg][n_rb][ubw] granule bitmaps
+  int64_t ubw;
+  const int32_t* __restrict__ vl;         // [H][n_rb][max_vert] leftover verticals
+  const int32_t* __restrict__ vl_cnt;     // [H][n_rb]
   int32_t max_vert;
+  int32_t n_rb, n_sub, nw, n_wgg;
   int32_t dense;
   uint64_t head_mask;
   void* out;
@@ -77,36 +78,16 @@ struct AttnArgs {
   unsigned long long* stats;
 };
 
-// bits [pos, pos + 64) of a bitmap; bits at negative positions are 0 (the
-// bitmap carries zero words past its end).
-__device__ __forceinline__ uint64_t get64(const uint32_t* bm, int64_t pos) {
-  if (pos <= -64) return 0;
-  const int64_t wi = pos >> 5;
-  const int sh = (int)(pos & 31);
-  const uint32_t w0 = wi >= 0 ? bm[wi] : 0u;
-  const uint32_t w1 = wi + 1 >= 0 ? bm[wi + 1] : 0u;
-  const uint32_t w2 = wi + 2 >= 0 ? bm[wi + 2] : 0u;
-  const uint64_t lo = ((uint64_t)w1 << 32) | w0;
-  return sh ? (lo >> sh) | ((uint64_t)w2 << (64 - sh)) : lo;
-}
-
 __device__ __forceinline__ uint64_t low_bits(int64_t n) {  // n clamped to [0, 64]
   return n >= 64 ? ~0ull : (n <= 0 ? 0ull : ((1ull << n) - 1));
 }
 
-// any / all bits set in [a, b] (a > b: empty -> any false, all true)
-__device__ __forceinline__ bool any_bits(const uint32_t* bm, int64_t a, int64_t b) {
-  for (int64_t p = a; p <= b; p += 64) {
-    if (get64(bm, p) & low_bits(b - p + 1)) return true;
-  }
-  return false;
-}
-__device__ __forceinline__ bool all_bits(const uint32_t* bm, int64_t a, int64_t b) {
-  for (int64_t p = a; p <= b; p += 64) {
-    const uint64_t m = low_bits(b - p + 1);
-    if ((get64(bm, p) & m) != m) return false;
-  }
-  return true;
+// Uniform read through the constant address space: it becomes a scalar load
+// (the direct-to-LDS loads count as memory writes for the compiler, which
+// would otherwise turn later uniform reads into vector loads that wait behind
+// the tile loads in flight).
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
 // 128 bitmap bits [base, base + 128) loaded with uniform (scalar) loads.
@@ -118,8 +99,6 @@ struct Win {
 __device__ __forceinline__ Win load_win(const uint32_t* bm, int32_t pos) {
   // floor(pos / 32); the bitmaps carry kBitPad zero words before bit 0
   const int32_t wi = pos >= 0 ? pos >> 5 : -((31 - pos) >> 5);
-  // constant address space: uniform loads become scalar loads, which do not
-  // wait behind the tile loads in flight
   typedef const __attribute__((address_space(4))) uint32_t cu32;
   cu32* p = (cu32*)(bm + wi);
   return Win{p[0], p[1], p[2], p[3], wi * 32};
@@ -157,101 +136,156 @@ __device__ __forceinline__ uint64_t bitrev64(uint64_t x) {
   return ((uint64_t)lo << 32) | hi;
 }
 
-// One 64-key tile: keys [ks, ks + n) (gather == 0) or vl[ks .. ks + n).
-// W / C: the offset window of this wave and the column window of the tile,
-// loaded one iteration ahead so that they are ready with the tile itself.
+// One 64-key tile.  Span tiles (wave < 0): keys [ks, ks + n), granule bits of
+// its four granules in `gran`.  Gathered tiles: wave `wave` only (its head's
+// leftover list), keys list[ks .. ks + n).
 struct Tile {
-  int32_t ks;      // first key (span) / slot of the first key (gather)
+  int32_t ks;      // first key (span) / first slot (gather)
   int32_t n;
-  int32_t gather;
+  int32_t wave;    // -1: span tile; else the wave whose head owns the list
   int32_t kchunk;  // DCA chunk of the tile's keys
-  int32_t kmin, kmax;
-  Win W, C;
+  int32_t kmax;    // last key
+  int32_t gran;    // span tile: marked bits of granules ks/16 .. ks/16 + 3
 };
 
-// Scalar walk over the tile list of one workgroup: the spans of the slash
-// runs, then the leftover verticals.  Every thread computes the same thing.
-struct TileWalk {
+// The walk over one workgroup's tiles, identical in every wave: marked
+// granules in ascending key order, then each head's leftover verticals.
+struct Walk {
   int32_t phase;   // 0 spans, 1 verticals, 2 done
-  int32_t ru;      // next run
-  int32_t ks, hi;  // current span position / end (inclusive)
-  int32_t s0;      // next vertical slot
+  int32_t pos;     // first key not covered yet
+  int32_t chunk;   // bitmap chunk held in the lanes' `cw` (-1: none)
+  uint64_t nz;     // non-zero words of that chunk
+  int32_t kc;      // DCA chunk of pos
+  int32_t edge;    // first key of the next DCA chunk
+  int32_t gw;      // verticals: wave (head) being listed
+  int32_t s0;      // next slot of that list
+  int32_t vcnt;    // its length
 };
 
-__device__ __forceinline__ bool next_tile(const AttnArgs& a, int32_t r0, int32_t rlast,
-                                          int32_t period, const int32_t* runs, int n_runs,
-                                          const int32_t* vl, int32_t vcnt, TileWalk& w,
-                                          Tile& t) {
-  while (w.phase == 0) {
-    if (w.ks <= w.hi) {
-      int32_t ke = w.ks + kTileK < w.hi + 1 ? w.ks + kTileK : w.hi + 1;
-      const int32_t kc = period ? w.ks / period : 0;
-      if (period && ke > (kc + 1) * period) ke = (kc + 1) * period;
-      t.ks = w.ks;
-      t.n = ke - w.ks;
-      t.gather = 0;
-      t.kchunk = kc;
-      t.kmin = w.ks;
+struct WalkConst {
+  int32_t rlast, period, glast, nwords, n_here, rb, h_first;
+  const uint32_t* ub;   // LDS bitmap
+};
+
+__device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c, Walk& w,
+                                          uint32_t& cw, Tile& t) {
+  const int lane = threadIdx.x & 63;
+  if (w.phase == 0) {
+    // first granule at or after pos (pos is a multiple of 16 except after
+    // the tile that ends the row block's keys at rlast + 1)
+    int32_t g = (w.pos + kGranule - 1) / kGranule;
+    bool found = false;
+    while (g <= c.glast) {
+      const int32_t ch = g / kGranPerChunk;
+      if (ch != w.chunk) {
+        const int32_t wi = ch * 64 + lane;
+        cw = wi < c.nwords ? c.ub[wi] : 0u;
+        w.nz = __ballot(cw != 0u);
+        w.chunk = ch;
+      }
+      const int32_t wl = (g >> 5) & 63;
+      const uint32_t word =
+          (uint32_t)__builtin_amdgcn_readlane(cw, wl) & (0xFFFFFFFFu << (g & 31));
+      if (word) {
+        g = (g & ~31) + __builtin_ctz(word);
+        found = true;
+        break;
+      }
+      const uint64_t rest = wl == 63 ? 0ull : (w.nz & (~0ull << (wl + 1)));
+      g = rest ? ch * kGranPerChunk + 32 * __builtin_ctzll(rest) : (ch + 1) * kGranPerChunk;
+    }
+    if (found && g <= c.glast) {
+      const int32_t ks = g * kGranule;
+      int32_t ke = ks + kTileK < c.rlast + 1 ? ks + kTileK : c.rlast + 1;
+      if (c.period) {
+        while (ks >= w.edge) {
+          ++w.kc;
+          w.edge += c.period;
+        }
+        if (ke > w.edge) ke = w.edge;
+      }
+      // marked bits of the tile's four granules (they may straddle a word)
+      const int32_t wl = (g >> 5) & 63, sh = g & 31;
+      // (readlane returns int: shift the word as unsigned)
+      uint32_t gb = (uint32_t)__builtin_amdgcn_readlane(cw, wl) >> sh;
+      if (sh > 28) {
+        const int32_t nwi = (g >> 5) + 1;
+        const uint32_t nx =
+            wl < 63 ? (uint32_t)__builtin_amdgcn_readlane(cw, wl + 1)
+                    : (nwi < c.nwords ? (uint32_t)__builtin_amdgcn_readfirstlane(c.ub[nwi]) : 0u);
+        gb |= nx << (32 - sh);
+      }
+      t.ks = ks;
+      t.n = ke - ks;
+      t.wave = -1;
+      t.kchunk = w.kc;
       t.kmax = ke - 1;
-      w.ks = ke;
+      t.gran = (int32_t)(gb & 15u);
+      w.pos = ke;
       return true;
     }
-    if (w.ru >= n_runs) {
-      w.phase = 1;
-      break;
-    }
-    const int32_t oa = a.dense ? 0 : runs[2 * w.ru];
-    const int32_t ob = a.dense ? (int32_t)a.n_ctx - 1 : runs[2 * w.ru + 1];
-    ++w.ru;
-    if (oa > r0 + kTileQ - 1) {
-      w.phase = 1;
-      break;
-    }
-    w.ks = r0 - ob > 0 ? r0 - ob : 0;
-    w.hi = (r0 + kTileQ - 1 - oa < rlast) ? r0 + kTileQ - 1 - oa : rlast;
+    w.phase = 1;
+    w.gw = -1;
+    w.s0 = 0;
+    w.vcnt = 0;
   }
   if (w.phase == 1) {
-    if (a.dense || w.s0 >= vcnt) {
-      w.phase = 2;
-      return false;
+    while (w.s0 >= w.vcnt) {
+      ++w.gw;
+      if (w.gw >= c.n_here) {
+        w.phase = 2;
+        return false;
+      }
+      const int h = c.h_first + w.gw;
+      w.s0 = 0;
+      w.vcnt = (a.dense || !((a.head_mask >> h) & 1))
+                   ? 0
+                   : min(ld_uniform(a.vl_cnt + (int64_t)h * a.n_rb + c.rb), a.max_vert);
     }
+    const int h = c.h_first + w.gw;
+    const int32_t* vl = a.vl + ((int64_t)h * a.n_rb + c.rb) * a.max_vert;
     const int32_t s0 = w.s0;
-    int32_t s1 = s0 + kTileK < vcnt ? s0 + kTileK : vcnt;
-    const int32_t k0 = vl[s0];
-    const int32_t kc = period ? k0 / period : 0;
-    if (period && vl[s1 - 1] / period != kc) {
+    int32_t s1 = s0 + kTileK < w.vcnt ? s0 + kTileK : w.vcnt;
+    const int32_t k0 = ld_uniform(vl + s0);
+    const int32_t kc = c.period ? k0 / c.period : 0;
+    if (c.period && ld_uniform(vl + s1 - 1) / c.period != kc) {
       // first slot of the next DCA chunk (keys ascending)
       int lo = s0 + 1, hi = s1 - 1;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (vl[mid] / period != kc) hi = mid;
+        if (ld_uniform(vl + mid) / c.period != kc) hi = mid;
         else lo = mid + 1;
       }
       s1 = lo;
     }
     t.ks = s0;
     t.n = s1 - s0;
-    t.gather = 1;
+    t.wave = w.gw;
     t.kchunk = kc;
-    t.kmin = k0;
-    t.kmax = vl[s1 - 1];
+    t.kmax = ld_uniform(vl + s1 - 1);
+    t.gran = 0;
     w.s0 = s1;
     return true;
   }
   return false;
 }
 
-// LDS layout of one buffer: K rows then V rows, 64 rows of D bf16 each.  The
-// 16-byte chunk c of K row r sits at slot c ^ (r & 15) and of V row r at slot
-// c ^ 4 (r & 3) (both mod the chunks per row): the K fragment reads (one
-// chunk of 32 consecutive rows) and the V transpose reads (two chunks of four
-// consecutive rows per 16 lanes) then hit distinct banks.
+// LDS layout of one stage: K rows, V rows (64 rows of D bf16 each), then the
+// 64 keys of a gathered tile.  The 16-byte chunk c of K row r sits at slot
+// c ^ (r & 15) and of V row r at slot c ^ 4 (r & 3) (both mod the chunks per
+// row): the K fragment reads (one chunk of 32 consecutive rows) and the V
+// transpose reads (two chunks of four consecutive rows per 16 lanes) then hit
+// distinct banks.
 template <int D>
 struct Buf {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;
   static constexpr int kKBytes = kTileK * kRowBytes;
-  static constexpr int kBytes = 2 * kKBytes;
+  static constexpr int kKeyOff = 2 * kKBytes;
+  static constexpr int kBytes = 2 * kKBytes + kTileK * 4;
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;  // rows one 64-lane load fills
+  static constexpr int kInstrPerMat = kTileK / kRowsPerInstr;
+  static constexpr int kInstr = 2 * kInstrPerMat;         // loads per tile (K and V)
 };
 
 template <int D>
@@ -263,29 +297,16 @@ __device__ __forceinline__ int swz_v(int chunk, int row) {
   return (chunk ^ ((row & 3) << 2)) & (Buf<D>::kChunks - 1);
 }
 
-// Per-lane constants of the tile pipeline, computed once per workgroup.
+// Per-lane LDS read offsets, computed once per workgroup.
 template <int D>
 struct LaneConst {
-  static constexpr int kCh = Buf<D>::kChunks;
-  static constexpr int kRowsPerInstr = 64 / kCh;   // rows one wave fills per load
-  static constexpr int kInstr = kTileK / (kWaves * kRowsPerInstr);
-  int32_t row[kInstr];      // tile row this lane loads in load i
-  int32_t k_chunk[kInstr];  // global chunk it loads for K / V
-  int32_t v_chunk[kInstr];
-  int32_t k_rd[D / 16];     // LDS byte offset of the K fragment of step s (kb = 0)
-  int32_t v_rd[D / 32];     // LDS byte offset of the V^T fragment of block db (s = 0)
+  int32_t k_rd[D / 16];  // K fragment of step s (kb = 0)
+  int32_t v_rd[D / 32];  // V^T fragment of block db (s = 0)
 };
 
 template <int D>
-__device__ __forceinline__ void lane_consts(LaneConst<D>& c, int w, int lane) {
-  constexpr int kCh = Buf<D>::kChunks, RB = Buf<D>::kRowBytes;
-#pragma unroll
-  for (int i = 0; i < LaneConst<D>::kInstr; ++i) {
-    const int row = (i * kWaves + w) * LaneConst<D>::kRowsPerInstr + lane / kCh;
-    c.row[i] = row;
-    c.k_chunk[i] = swz_k<D>(lane % kCh, row);  // the XOR swizzles are involutions
-    c.v_chunk[i] = swz_v<D>(lane % kCh, row);
-  }
+__device__ __forceinline__ void lane_consts(LaneConst<D>& c, int lane) {
+  constexpr int RB = Buf<D>::kRowBytes;
   const int half = lane >> 5;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
@@ -303,42 +324,82 @@ __device__ __forceinline__ void lane_consts(LaneConst<D>& c, int w, int lane) {
   }
 }
 
-// Toggle the LDS read offsets between the two buffers.
-template <int D>
-__device__ __forceinline__ void flip_buffers(LaneConst<D>& c) {
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) c.k_rd[s] ^= Buf<D>::kBytes;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) c.v_rd[db] ^= Buf<D>::kBytes;
+// Direct-to-LDS loads written as inline assembly: the compiler then does not
+// see LDS writes in flight, so it adds no waits before reading the other
+// stages (the kernel waits for its own loads explicitly).  They have no
+// register results.  M0 holds the LDS byte address of lane 0's 16 bytes.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16_v(const void* addr, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4_v(const void* addr, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
 }
 
-// Issue the direct-to-LDS loads of one tile into the buffer at byte `buf`.
-// Padding rows (past t.n) repeat the tile's last key, so every value is finite.
-template <int D>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, int g, const int32_t* vl,
-                                           const Tile& t, int buf, const LaneConst<D>& c,
-                                           int32_t* keys_lds, int w, int lane) {
-  constexpr int kCh = Buf<D>::kChunks, RB = Buf<D>::kRowBytes;
-  const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
-  const char* kbase = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
-  const char* vbase = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
-  if (!t.gather) {
-    kbase += (int64_t)t.ks * kvst_b;
-    vbase += (int64_t)t.ks * kvst_b;
-  }
+// Loads of one tile issued by one wave: P per wave (the last waves repeat one
+// of their loads, so every wave issues the same count and can wait for its
+// own loads with a fixed vmcnt).
+template <int D, int NW>
+struct Issue {
+  static constexpr int P = (Buf<D>::kInstr + NW - 1) / NW;
+};
+
+// This wave's share of the direct-to-LDS loads of one tile into the stage at
+// LDS address `dst`.  Load i of the tile fills rows (i mod M) * R .. + R - 1
+// of K (i < M) or V (M = loads per matrix, R rows per load); padding rows
+// past t.n repeat the last key.  For gathered tiles the keys of each load's
+// rows come from scalar loads, and wave 0 also copies the tile's keys into
+// the stage (for the masks).
+template <int D, int NW>
+__device__ __forceinline__ void issue_share(const char* kg, const char* vg, uint32_t kvst_b,
+                                            const Tile& t, const int32_t* vl, uint32_t dst,
+                                            int w, int lane) {
+  using B = Buf<D>;
+  constexpr int P = Issue<D, NW>::P;
+  constexpr int M = B::kInstrPerMat, R = B::kRowsPerInstr;
+  const int sub = lane / B::kChunks;  // row within a load
+  const int cl = lane % B::kChunks;   // LDS slot of this lane's 16 bytes
+  if (t.wave < 0) {
+    const char* kb = kg + (int64_t)t.ks * kvst_b;
+    const char* vb = vg + (int64_t)t.ks * kvst_b;
 #pragma unroll
-  for (int i = 0; i < LaneConst<D>::kInstr; ++i) {
-    const int rr = c.row[i] < t.n ? c.row[i] : t.n - 1;
-    int64_t roff;
-    if (t.gather) roff = (int64_t)vl[t.ks + rr] * kvst_b;
-    else roff = (uint32_t)rr * kvst_b;
-    const int lds = buf + (i * kWaves + w) * LaneConst<D>::kRowsPerInstr * RB;
-    __builtin_amdgcn_global_load_lds(kbase + roff + c.k_chunk[i] * 16, (lds_void*)(lds), 16,
-                                     0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + roff + c.v_chunk[i] * 16,
-                                     (lds_void*)(lds + Buf<D>::kKBytes), 16, 0, 0);
-    if (t.gather && (lane % kCh) == 0)
-      keys_lds[c.row[i]] = c.row[i] < t.n ? vl[t.ks + c.row[i]] : INT32_MAX;
+    for (int p = 0; p < P; ++p) {
+      int gi = p * NW + w;
+      if (gi >= B::kInstr) gi = w;
+      const bool isv = gi >= M;
+      const int gm = isv ? gi - M : gi;
+      const int row = gm * R + sub;
+      const uint32_t rr = (uint32_t)(row < t.n ? row : t.n - 1);
+      const int chunk = isv ? swz_v<D>(cl, row) : swz_k<D>(cl, row);
+      dma16_s(isv ? vb : kb, rr * kvst_b + (uint32_t)chunk * 16u,
+              dst + (isv ? B::kKBytes : 0) + gm * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      int gi = p * NW + w;
+      if (gi >= B::kInstr) gi = w;
+      const bool isv = gi >= M;
+      const int gm = isv ? gi - M : gi;
+      // keys of the R rows of this load (uniform), then this lane's one
+      int32_t key = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = gm * R + r;
+        const int32_t kr = ld_uniform(vl + t.ks + (row < t.n ? row : t.n - 1));
+        key = sub == r ? kr : key;
+      }
+      const int row = gm * R + sub;
+      const int chunk = isv ? swz_v<D>(cl, row) : swz_k<D>(cl, row);
+      dma16_v((isv ? vg : kg) + (int64_t)key * kvst_b + chunk * 16,
+              dst + (isv ? B::kKBytes : 0) + gm * 1024);
+    }
+    if (w == 0) dma4_v(vl + t.ks + (lane < t.n ? lane : t.n - 1), dst + B::kKeyOff);
   }
 }
 
@@ -347,85 +408,90 @@ struct WaveState {
   bf16x8 q[D / 16];
   f32x16 o[D / 32];
   float m, l;
-  int var;
-  uint32_t sel;   // critical-set pairs of this lane's row
 };
 
+// Query variant `var` of this wave's 32 rows (rows past the chunk read the
+// chunk's last row; their outputs are not written).
 template <int D>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int h, int32_t i0, int var,
                                        WaveState<D>& st) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)i0 - a.c0 + (lane & 31);
+  int64_t t = (int64_t)i0 - a.c0 + (lane & 31);
+  if (t > a.L - 1) t = a.L - 1;
   const uint16_t* base = a.q_rot + (((int64_t)var * a.H + h) * a.L + t) * D + 8 * (lane >> 5);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (t < a.L) st.q[s] = *reinterpret_cast<const bf16x8*>(base + s * 16);
-    else st.q[s] = (bf16x8){};
-  }
-  st.var = var;
+  for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const bf16x8*>(base + s * 16);
 }
 
-// One (wave, key tile) step on the current buffer (offsets in `c`).  With
-// `masked`, mword is the 64-bit key mask of this lane's row.
-template <int D>
+// max / sum of this lane's value and the value of lane l ^ 32
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One (wave, key tile) step on the stage `smem`.  With `masked`, mword is the
+// 64-bit key mask of this lane's row.  A wave with nothing in the tile
+// (act false) skips the QK product and the softmax but still runs the PV
+// product with zero weights: the O accumulators then go through the same
+// instructions on every path, and the compiler keeps them in place (a branch
+// around the PV product makes it copy them between register sets).
+// `after_qk` runs once the QK products are issued (scalar loads issued there
+// land during the softmax).
+template <int D, typename F>
 __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
-                                          const LaneConst<D>& c, WaveState<D>& st,
-                                          bool masked, uint64_t mword, int half) {
+                                          const LaneConst<D>& c, WaveState<D>& st, bool act,
+                                          bool masked, uint64_t mword, int half, F&& after_qk) {
   constexpr int RB = Buf<D>::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  // every K fragment of the tile is requested before the first product, so
-  // the LDS latency is paid once per tile, not once per MFMA
-  bf16x8 kf[2][KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      kf[kb][s] = *reinterpret_cast<const bf16x8*>(smem + c.k_rd[s] + kb * 32 * RB);
-  __builtin_amdgcn_sched_barrier(0);  // keep every K read ahead of the products
   f32x16 acc[2];
+  float mx = -INFINITY;
+  if (act) {
+    // the K fragments of each 32-key half are requested together, so the LDS
+    // latency is paid once per half, not once per MFMA
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) acc[kb] = (f32x16){};
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8*>(smem + c.k_rd[s] + kb * 32 * RB);
+      acc[kb] = (f32x16){};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], st.q[s], acc[kb], 0, 0, 0);
-  // V^T fragments of the first two 16-key steps, in flight during the softmax;
-  // each lane receives V[16 s + 4 half + r][d0 + j] (r = 0..3 for the first
-  // load, +8 for the second), the k-order of its P fragment
-  auto load_v = [&](int s, int db) {
-    const char* p = smem + c.v_rd[db] + 16 * s * RB;
-    const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-    const v4i16 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * RB));
-    const v4i16 vv[2] = {va, vb};
-    bf16x8 vf;
-    __builtin_memcpy(&vf, vv, 16);
-    return vf;
-  };
-  bf16x8 vf[2][DB];
+      for (int s = 0; s < KS; ++s)
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], st.q[s], acc[kb], 0, 0, 0);
+    }
+    after_qk();
+    // key k of the tile sits in register r of block kb: k = 32 kb + 8 (r / 4)
+    // + 4 half + r % 4
+    if (__builtin_expect(masked, 0)) {
+      const uint64_t mh = mword >> (4 * half);
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t word = (uint32_t)(mh >> (32 * kb));
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vf[s][db] = load_v(s, db);
-  __builtin_amdgcn_sched_barrier(0);  // V reads in flight before the softmax
-  // key k of the tile sits in register r of block kb: k = 32 kb + 8 (r / 4)
-  // + 4 half + r % 4
-  if (__builtin_expect(masked, 0)) {
-    const uint64_t mh = mword >> (4 * half);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int bit = 32 * kb + 8 * (r >> 2) + (r & 3);
-        if (!((mh >> bit) & 1ull)) acc[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          // all ones where the key is kept, zero where it is masked
+          const uint32_t keep =
+              (uint32_t)__builtin_amdgcn_sbfe((int)word, 8 * (r >> 2) + (r & 3), 1);
+          acc[kb][r] = __uint_as_float((__float_as_uint(acc[kb][r]) & keep) |
+                                       (0xFF800000u & ~keep));
+        }
       }
-  }
-  // row max of the raw scores (the scale is positive)
-  float mx = fmaxf(acc[0][0], acc[1][0]);
+    }
+    // row max of the raw scores (the scale is positive)
+    mx = fmaxf(acc[0][0], acc[1][0]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, acc[0][r]), acc[1][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, acc[0][r]), acc[1][r]);
+    mx = max_halves(mx) * a.scale_log2;
+  } else {
+    after_qk();
+  }
   if (__builtin_expect(__ballot(mx > st.m + kRescaleSlack) != 0ull, 0)) {
     const float m_new = fmaxf(st.m, mx);
     const float alpha = (st.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
@@ -436,204 +502,346 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
       for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     st.m = m_new;
   }
-  const float msub = (st.m == -INFINITY) ? 0.f : st.m;
   bf16x8 pf[4];
+  if (act) {
+    const float msub = (st.m == -INFINITY) ? 0.f : st.m;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      pf[s][e] = (__bf16)__builtin_amdgcn_exp2f(
-          fmaf(acc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msub));
-  // row sum of the bf16 weights the PV product uses
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float psum = 0.f;
+      for (int e = 0; e < 8; ++e)
+        pf[s][e] = (__bf16)__builtin_amdgcn_exp2f(
+            fmaf(acc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msub));
+    // row sum of the bf16 weights the PV product uses
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum = 0.f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 pr = {pf[s][e], pf[s][e + 1]};
-      psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
-    }
-  st.l += psum;
-  // O^T += V^T P^T: steps 0, 1 from the fragments in flight, 2, 3 after
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pf[s][e], pf[s][e + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+      }
+    st.l += psum;
+  } else {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][db], pf[s], st.o[db], 0, 0, 0);
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) vf[s][db] = load_v(s + 2, db);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][db], pf[s + 2], st.o[db], 0, 0,
-                                                         0);
-}
-
-template <int D>
-constexpr size_t attn_smem_bytes() {
-  return 2 * Buf<D>::kBytes + 2 * kTileK * sizeof(int32_t) + 2 * sizeof(unsigned long long);
-}
-
-// Per (wave, tile) decision: false = skip; masked + mword otherwise.
-__device__ __forceinline__ bool tile_mask(const Tile& t, int32_t i0, int32_t my_row, int lane,
-                                          const int32_t* keys_lds, bool& masked,
-                                          uint64_t& mword) {
-  masked = false;
-  mword = 0;
-  if (!t.gather) {
-    const int32_t wlo = i0 - t.ks - 63;
-    const uint64_t wcol = bits_at(t.C, t.ks - t.C.base) & low_bits(t.n);
-    const int32_t olo = i0 - t.kmax, ohi = i0 + 31 - t.ks;
-    if (!wcol && !win_any(t.W, olo > 0 ? olo : 0, ohi)) return false;
-    if (!(t.n == kTileK && t.kmax <= i0 && win_all(t.W, olo, ohi))) {
-      masked = true;
-      // this lane's 64 offsets start at wlo + lane % 32
-      const uint64_t woff = bits_at(t.W, wlo - t.W.base + (lane & 31));
-      mword = (bitrev64(woff) | wcol) & low_bits(my_row - t.ks + 1) & low_bits(t.n);
-    }
-  } else if (!(t.n == kTileK && t.kmax <= i0)) {
-    masked = true;
-    int lo = 0, hi = t.n;  // keys <= my_row (keys ascending)
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (keys_lds[mid] <= my_row) lo = mid + 1;
-      else hi = mid;
-    }
-    mword = low_bits(lo);
+    for (int s = 0; s < 4; ++s) pf[s] = (bf16x8){};
   }
-  return true;
+  // O^T += V^T P^T; each lane receives V[16 s + 4 half + r][d0 + j] (r = 0..3
+  // for the first transpose load, +8 for the second), the k-order of its P
+  // fragment
+  auto load_v = [&](int s, int db) {
+    const char* p = smem + c.v_rd[db] + 16 * s * RB;
+    const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * RB));
+    const v4i16 vv[2] = {va, vb};
+    bf16x8 vf;
+    __builtin_memcpy(&vf, vv, 16);
+    return vf;
+  };
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 vf[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vf[db] = load_v(s, db);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[s], st.o[db], 0, 0, 0);
+  }
 }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  int32_t* keys_lds = reinterpret_cast<int32_t*>(smem + 2 * Buf<D>::kBytes);  // [2][64]
-  unsigned long long* stat_lds = reinterpret_cast<unsigned long long*>(keys_lds + 2 * kTileK);
-  // XCD-aware order: consecutive logical blocks (same KV group and query
-  // tile, then the next tile) land on one XCD, sharing its L2.
-  const int32_t nb = (int32_t)a.n_blocks;
+// 16 copies of each of the four low bits of g
+__device__ __forceinline__ uint64_t granule_keys(int32_t g) {
+  uint64_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((g >> i) & 1) m |= 0xFFFFull << (16 * i);
+  return m;
+}
+
+// Key mask of this lane's row for one tile and this wave's head (bit k: key
+// k of the tile is critical for the row).  Span tiles: the pair (row, key)
+// is critical when its offset row - key is a slash of the head or the key is
+// a vertical of the head in a marked granule (verticals elsewhere are
+// gathered); keys <= row.  W / C: the head's offset bits from word
+// floor((i0 - ks - 63) / 32) (they hold [row - ks - 63, row - ks] for every
+// row) and column bits from word ks / 32.  Straight-line vector code: only
+// the 64-bit window shift depends on the lane.
+__device__ __forceinline__ uint64_t span_mask(const Tile& t, const Win& W, const Win& C,
+                                              int32_t i0, int32_t row, int r) {
+  const uint64_t gk = granule_keys(t.gran) & low_bits(t.n);
+  const int cs = t.ks - C.base;  // 0 .. 31
+  const uint64_t c01 = ((uint64_t)C.w1 << 32) | C.w0;
+  const uint64_t wcol = (cs ? (c01 >> cs) | ((uint64_t)C.w2 << (64 - cs)) : c01) & gk;
+  const uint64_t lo = ((uint64_t)W.w1 << 32) | W.w0;
+  const uint64_t hi = ((uint64_t)W.w3 << 32) | W.w2;
+  const uint32_t rel = (uint32_t)(i0 - t.ks - 63 - W.base + r);  // 0 .. 62
+  const uint64_t woff = rel ? (lo >> rel) | (hi << (64 - rel)) : lo;
+  return (bitrev64(woff) | wcol) & low_bits(row - t.ks + 1) & low_bits(t.n);
+}
+
+// Gathered tile: the keys of the list (in the stage, ascending) that are <=
+// the row.
+__device__ __forceinline__ uint64_t gather_mask(const Tile& t, const int32_t* keys,
+                                                int32_t row) {
+  int lo = 0, hi = t.n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (keys[mid] <= row) lo = mid + 1;
+    else hi = mid;
+  }
+  return low_bits(lo);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched: at most N of this wave's
+// vector-memory operations are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier of the tile ring.  It carries no release fence: a fenced
+// barrier waits for every load in flight (vmcnt(0)), which would drain the
+// ring.  A stage is visible to all waves because the producer waits for its
+// loads of that stage (wait_vm) before arriving; the lgkmcnt(0) wait retires
+// this wave's LDS reads and writes (stage reads, descriptor writes) before
+// the barrier.  The empty asm statements keep the compiler from moving memory
+// accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+constexpr int kRing = 8;  // tile descriptors in LDS (producer -> consumers)
+
+// Descriptor: {ks, n | (wave + 1) << 8 | gran << 16, kchunk, kmax}; n = 0
+// ends the walk.
+__device__ __forceinline__ int4 pack_desc(const Tile& t) {
+  return make_int4(t.ks, t.n | ((t.wave + 1) << 8) | (t.gran << 16), t.kchunk, t.kmax);
+}
+__device__ __forceinline__ Tile read_desc(const int4* slot) {
+  const int4 d = *slot;
+  Tile t;
+  t.ks = __builtin_amdgcn_readfirstlane(d.x);
+  const int32_t info = __builtin_amdgcn_readfirstlane(d.y);
+  t.kchunk = __builtin_amdgcn_readfirstlane(d.z);
+  t.kmax = __builtin_amdgcn_readfirstlane(d.w);
+  t.n = info & 0xFF;
+  t.wave = ((info >> 8) & 0xFF) - 1;
+  t.gran = (info >> 16) & 0xF;
+  return t;
+}
+
+// Waves 0 .. NW - 1 compute (one query head each) and issue the tile loads
+// between them; wave NW walks the tiles and publishes a descriptor per tile
+// four tiles ahead.  Tile i sits in stage i mod 4; its loads are issued three
+// tiles ahead.  One barrier per tile.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
+  using B = Buf<D>;
+  constexpr int P = Issue<D, NW>::P;  // loads per tile per computing wave
+  __shared__ __attribute__((aligned(16))) char stage[kStages][B::kBytes];
+  __shared__ int4 ring[kRing];
+  __shared__ unsigned long long sstat[2];
+  extern __shared__ uint32_t ub_lds[];  // granule bitmap of this row block
+
+  // XCD-aware order: consecutive logical blocks (same KV group, next row
+  // block) land on one XCD, sharing its L2.
+  const int32_t nb = a.n_wgg * a.n_rb;
   const int32_t per_xcd = (nb + 7) / 8;
   const int32_t logical = (int32_t)(blockIdx.x % 8) * per_xcd + (int32_t)(blockIdx.x / 8);
   if (logical >= nb) return;
-  const int32_t gq = logical / a.G;
-  const int hh = logical % a.G;
-  const int g = gq / (int32_t)a.n_qt;
-  const int32_t qt = gq % (int32_t)a.n_qt;
-  const int h = g * a.G + hh;
-  if (!((a.head_mask >> h) & 1)) return;
+  const int32_t wgg = logical / a.n_rb;
+  const int32_t rb = logical % a.n_rb;
+  const int g = wgg / a.n_sub;
+  const int sub = wgg % a.n_sub;
+  const int h_first = g * a.G + sub * a.nw;
+  const int n_here = min(a.nw, a.G - sub * a.nw);
+  const uint64_t wg_heads = ((n_here >= 64 ? ~0ull : ((1ull << n_here) - 1)) << h_first);
+  if (!(a.head_mask & wg_heads)) return;
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, half = lane >> 5;
   const int32_t c0 = (int32_t)a.c0, c1 = (int32_t)a.n_ctx, period = (int32_t)a.period;
-  const int32_t r0 = c0 + qt * kTileQ;
-  const int32_t rlast = (r0 + kTileQ - 1 < c1 - 1) ? r0 + kTileQ - 1 : c1 - 1;
-  const int32_t i0 = r0 + 32 * w;
-  const bool wave_live = i0 <= rlast;
-  const int32_t my_row = i0 + (lane & 31);
-  const int32_t qchunk = period ? i0 / period : 0;
-  const uint32_t* offb = a.off_bits + (int64_t)h * a.n_words + kBitPad;
-  const uint32_t* colb = a.col_bits + (int64_t)h * a.n_words + kBitPad;
-  const int32_t* runs = a.runs + (int64_t)h * a.max_runs * 2;
-  const int n_runs = a.dense ? 1 : min(a.run_cnt[h], a.max_runs);
-  const int32_t* vl = a.vl + ((int64_t)h * a.n_qt + qt) * a.max_vert;
-  const int32_t vcnt = a.dense ? 0 : min(a.vl_cnt[(int64_t)h * a.n_qt + qt], a.max_vert);
+  const int32_t r0 = c0 + rb * kRowBlock;
+  const int32_t rlast = (r0 + kRowBlock - 1 < c1 - 1) ? r0 + kRowBlock - 1 : c1 - 1;
+  const int32_t i0 = r0;
 
-  LaneConst<D> lc;
-  lane_consts<D>(lc, w, lane);
-  WaveState<D> st;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) st.o[db] = (f32x16){};
-  st.m = -INFINITY;
-  st.l = 0.f;
-  st.var = -1;
-  st.sel = 0;
-  uint32_t exec_tiles = 0;
-  if (threadIdx.x < 2) stat_lds[threadIdx.x] = 0;
-
-  // offset / column windows of a span tile for this wave (offsets the wave
-  // can meet: [i0 - kmax, i0 + 31 - ks]; lane windows [my_row - ks - 63,
-  // my_row - ks] all sit in the 128 bits from i0 - ks - 63)
-  auto load_windows = [&](Tile& t) {
-    if (!t.gather && wave_live) {
-      t.W = load_win(offb, i0 - t.ks - 63);
-      t.C = load_win(colb, t.ks);
-    }
-  };
-  TileWalk walk{0, 0, 0, -1, 0};
-  Tile cur, nxt;
-  bool have = next_tile(a, r0, rlast, period, runs, n_runs, vl, vcnt, walk, cur);
-  if (have) {
-    load_windows(cur);
-    issue_tile<D>(a, g, vl, cur, 0, lc, keys_lds, w, lane);
+  // the row block's granule bitmap into LDS
+  const int32_t glast = rlast / kGranule;
+  const int32_t nwords = glast / 32 + 1;
+  {
+    const uint32_t* src = a.ubits + ((int64_t)wgg * a.n_rb + rb) * a.ubw;
+    for (int i = threadIdx.x; i < nwords; i += 64 * (NW + 1)) ub_lds[i] = src[i];
   }
-  int b = 0;
-  while (have) {
-    const bool have_next = next_tile(a, r0, rlast, period, runs, n_runs, vl, vcnt, walk, nxt);
-    if (have_next) load_windows(nxt);
-    __syncthreads();  // tile `cur` landed in buffer b; buffer b ^ 1 is free
-    if (have_next)
-      issue_tile<D>(a, g, vl, nxt, (b ^ 1) * Buf<D>::kBytes, lc, keys_lds + (b ^ 1) * kTileK,
-                    w, lane);
-    bool masked;
-    uint64_t mword;
-    if (wave_live && cur.kmin <= i0 + 31 &&
-        tile_mask(cur, i0, my_row, lane, keys_lds + b * kTileK, masked, mword)) {
-      const int32_t rel = qchunk - cur.kchunk;
-      const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : rel);
-      if (var != st.var) load_q<D>(a, h, i0, var, st);
-      wave_tile<D>(a, smem, lc, st, masked, mword, half);
-      ++exec_tiles;
-      if (half == 0 && my_row <= rlast) st.sel += masked ? (uint32_t)__popcll(mword) : cur.n;
-    }
-    flip_buffers<D>(lc);
-    cur = nxt;
-    have = have_next;
-    b ^= 1;
-  }
+  if (threadIdx.x < 2) sstat[threadIdx.x] = 0;
+  __syncthreads();
 
-  // ---------------- epilogue
-  if (wave_live) {
-    const float l_tot = st.l + __shfl_xor(st.l, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_row <= rlast) {
-      const int64_t t = my_row - c0;
+  uint32_t exec_tiles = 0, sel = 0;
+  if (w == NW) {
+    // ---------------- walker: publishes tile j during step j - 4
+    const WalkConst wc{rlast, period, glast, nwords, n_here, rb, h_first, ub_lds};
+    Walk walk;
+    walk.phase = 0;
+    walk.pos = 0;
+    walk.chunk = -1;
+    walk.nz = 0;
+    walk.kc = 0;
+    walk.edge = period;
+    walk.gw = -1;
+    walk.s0 = 0;
+    walk.vcnt = 0;
+    uint32_t cw = 0;
+    Tile t;
+    int n_tiles = -1;  // known once the walk ends
+    auto publish = [&](int j) {
+      const bool e = n_tiles < 0 && next_tile(a, wc, walk, cw, t);
+      if (!e && n_tiles < 0) n_tiles = j;
+      if (lane == 0) ring[j & (kRing - 1)] = e ? pack_desc(t) : make_int4(0, 0, 0, 0);
+    };
+    for (int j = 0; j < 4; ++j) publish(j);
+    ring_barrier();  // descriptors 0 .. 3 published
+    for (int i = 0; n_tiles < 0 || i < n_tiles; ++i) {
+      ring_barrier();  // step i
+      publish(i + 4);
+    }
+  } else {
+    // ---------------- consumers: wave w multiplies for head h
+    const int h = h_first + w;
+    const bool live = w < n_here && ((a.head_mask >> h) & 1);
+    const int32_t my_row = i0 + (lane & 31);
+    const int32_t qchunk = period ? i0 / period : 0;
+    const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
+    const char* vg = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
+    const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+    const uint32_t stage0 = lds_addr(&stage[0][0]);
+    auto list_of = [&](const Tile& tt) {
+      return a.vl + ((int64_t)(h_first + (tt.wave < 0 ? 0 : tt.wave)) * a.n_rb + rb) * a.max_vert;
+    };
+    auto issue = [&](const Tile& tt, int j) {
+      if (tt.n > 0)
+        issue_share<D, NW>(kg, vg, kvst_b, tt, list_of(tt),
+                           stage0 + (uint32_t)((j & (kStages - 1)) * B::kBytes), w, lane);
+    };
+    LaneConst<D> lc;
+    lane_consts<D>(lc, lane);
+    WaveState<D> st;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db) st.o[db] = (f32x16){};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    const uint32_t* offb = a.off_bits + (int64_t)(live ? h : 0) * a.n_words + kBitPad;
+    const uint32_t* colb = a.col_bits + (int64_t)(live ? h : 0) * a.n_words + kBitPad;
+    // offset / column windows of a span tile for this head (scalar loads)
+    auto load_windows = [&](const Tile& tt, Win& W, Win& C) {
+      if (tt.n > 0 && tt.wave < 0 && live) {
+        W = load_win(offb, i0 - tt.ks - 63);
+        C = load_win(colb, tt.ks);
+      }
+    };
+    ring_barrier();  // descriptors 0 .. 3 published
+    Tile t0 = read_desc(&ring[0]);
+    {
+      const Tile t1 = read_desc(&ring[1]), t2 = read_desc(&ring[2]);
+      issue(t0, 0);
+      issue(t1, 1);
+      issue(t2, 2);
+    }
+    // DCA relation of a tile (the same for every wave: all share the rows)
+    auto var_of = [&](const Tile& tt) {
+      const int32_t rel = qchunk - tt.kchunk;
+      return a.n_var == 1 ? 0 : (rel >= 2 ? 2 : rel);
+    };
+    Win W0{}, C0{}, W1{}, C1{};
+    load_windows(t0, W0, C0);
+    int i = 0;
+    // one step per tile (tile i in stage i mod 4)
+    auto step = [&]() {
+      // this wave's loads of tile i have landed (i + 1 and i + 2 may be in flight)
+      const Tile t1 = read_desc(&ring[(i + 1) & (kRing - 1)]);
+      const Tile t2 = read_desc(&ring[(i + 2) & (kRing - 1)]);
+      if (t2.n > 0) wait_vm<2 * P>();
+      else if (t1.n > 0) wait_vm<P>();
+      else wait_vm<0>();
+      ring_barrier();  // tile i is in its stage for every wave; stage i - 1 is free
+      issue(read_desc(&ring[(i + 3) & (kRing - 1)]), i + 3);
+      const char* bc = stage[i & (kStages - 1)];
+      // this wave's key mask for the tile; act: any pair, full: all 64 x 32
+      uint64_t mword = 0;
+      if (live && t0.wave < 0)
+        mword = span_mask(t0, W0, C0, i0, my_row, lane & 31);
+      else if (live && t0.wave == w)
+        mword = gather_mask(t0, reinterpret_cast<const int32_t*>(bc + B::kKeyOff), my_row);
+      const bool row_ok = my_row <= rlast;
+      const bool act = __ballot(mword != 0 && row_ok) != 0;
+      const bool masked = __ballot(mword == ~0ull || !row_ok) != ~0ull;
+      // the next tile's windows are requested during this tile's softmax
+      wave_tile<D>(a, bc, lc, st, act, masked, mword, half, [&] { load_windows(t1, W1, C1); });
+      if (act) {
+        ++exec_tiles;
+        if (half == 0 && row_ok) sel += (uint32_t)__popcll(mword);
+      }
+      t0 = t1;
+      W0 = W1;
+      C0 = C1;
+      ++i;
+    };
+    // tiles come in runs of one DCA relation (keys ascend, so it changes at
+    // most twice per walk); the query variant is loaded once per run, outside
+    // the inner loop
+    while (t0.n > 0) {
+      const int var = var_of(t0);
+      if (live) {
+        load_q<D>(a, h, i0, var, st);
+        wait_vm<0>();
+      }
+      do {
+        step();
+      } while (t0.n > 0 && var_of(t0) == var);
+    }
+
+    // ---------------- epilogue
+    if (live) {
+      const float l_tot = sum_halves(st.l);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (my_row <= rlast) {
+        const int64_t tr = my_row - c0;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = 32 * db + 8 * i4 + 4 * half;
-          const float v0 = st.o[db][4 * i4 + 0] * inv, v1 = st.o[db][4 * i4 + 1] * inv;
-          const float v2 = st.o[db][4 * i4 + 2] * inv, v3 = st.o[db][4 * i4 + 3] * inv;
-          if (a.out_dtype == LCSR_FP32) {
-            float* o = static_cast<float*>(a.out) + h * a.o_sh + t * a.o_st + d;
-            *reinterpret_cast<float4*>(o) = make_float4(v0, v1, v2, v3);
-          } else {
-            uint16_t* o = static_cast<uint16_t*>(a.out) + h * a.o_sh + t * a.o_st + d;
-            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = 32 * db + 8 * i4 + 4 * half;
+            const float v0 = st.o[db][4 * i4 + 0] * inv, v1 = st.o[db][4 * i4 + 1] * inv;
+            const float v2 = st.o[db][4 * i4 + 2] * inv, v3 = st.o[db][4 * i4 + 3] * inv;
+            if (a.out_dtype == LCSR_FP32) {
+              float* o = static_cast<float*>(a.out) + h * a.o_sh + tr * a.o_st + d;
+              *reinterpret_cast<float4*>(o) = make_float4(v0, v1, v2, v3);
+            } else {
+              uint16_t* o = static_cast<uint16_t*>(a.out) + h * a.o_sh + tr * a.o_st + d;
+              *reinterpret_cast<uint2*>(o) =
+                  make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            }
           }
-        }
-      if (a.lse && half == 0)
-        a.lse[(int64_t)h * a.L + t] = l_tot > 0.f ? (st.m + log2f(l_tot)) * kLn2 : -INFINITY;
+        if (a.lse && half == 0)
+          a.lse[(int64_t)h * a.L + tr] = l_tot > 0.f ? (st.m + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
     }
   }
   if (a.stats) {
     __syncthreads();
-    unsigned long long se = st.sel;
+    unsigned long long se = sel;
     for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
     if (lane == 0) {
-      atomicAdd(&stat_lds[0], (unsigned long long)exec_tiles * 32ull * kTileK);
-      atomicAdd(&stat_lds[1], se);
+      atomicAdd(&sstat[0], (unsigned long long)exec_tiles * 32ull * kTileK);
+      atomicAdd(&sstat[1], se);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      atomicAdd(&a.stats[0], stat_lds[0]);
-      atomicAdd(&a.stats[1], stat_lds[1]);
+      atomicAdd(&a.stats[0], sstat[0]);
+      atomicAdd(&a.stats[1], sstat[1]);
     }
   }
 }
@@ -651,9 +859,6 @@ struct AuxArgs {
   uint32_t* col_bits;
   int32_t* runs;
   int32_t* run_cnt;
-  int32_t* vl;
-  int32_t* vl_cnt;
-  int64_t c0, n_qt;
   int32_t dense;
   uint64_t head_mask;
 };
@@ -661,8 +866,8 @@ struct AuxArgs {
 constexpr int kAuxThreads = 1024;
 
 // Per head: offset / column bitmaps and the slash runs (consecutive offsets
-// at most 128 apart).  Indices outside [0, n_ctx) are ignored; indices must
-// be ascending.
+// at most kRunGap apart).  Indices outside [0, n_ctx) are ignored; indices
+// must be ascending.
 __global__ void __launch_bounds__(kAuxThreads) aux_kernel(AuxArgs a) {
   const int h = blockIdx.x;
   if (!((a.head_mask >> h) & 1)) return;
@@ -698,7 +903,7 @@ __global__ void __launch_bounds__(kAuxThreads) aux_kernel(AuxArgs a) {
     if (v >= 0 && v < a.n_ctx) atomicOr(&cb[v >> 5], 1u << (v & 31));
   }
   // runs: a run starts at the first valid offset and wherever the gap to the
-  // previous valid offset exceeds the query tile height
+  // previous valid offset exceeds kRunGap
   __shared__ int s_wave[kAuxThreads / 64];
   __shared__ int s_carry;
   __shared__ int s_last;  // previous valid offset carried across batches
@@ -721,7 +926,7 @@ __global__ void __launch_bounds__(kAuxThreads) aux_kernel(AuxArgs a) {
         prev = (pv >= 0 && pv < a.n_ctx) ? pv : -1;
       }
     }
-    const bool start = valid && (prev < 0 || o - prev > kTileQ);
+    const bool start = valid && (prev < 0 || o - prev > kRunGap);
     const uint64_t bal = __ballot(start);
     if (lane == 0) s_wave[w] = __popcll(bal);
     __syncthreads();
@@ -759,7 +964,7 @@ __global__ void __launch_bounds__(kAuxThreads) aux_kernel(AuxArgs a) {
           const int32_t q = so[i + 1];
           nx = (q >= 0 && q < a.n_ctx) ? q : -1;
         }
-        if (nx < 0 || nx - o > kTileQ) {
+        if (nx < 0 || nx - o > kRunGap) {
           int lo = 0, hi = nr - 1;
           while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -774,56 +979,148 @@ __global__ void __launch_bounds__(kAuxThreads) aux_kernel(AuxArgs a) {
   if (tid == 0) a.run_cnt[h] = nr;
 }
 
-constexpr int kVlThreads = 256;
+struct PlanArgs {
+  const int32_t* vert_idx;
+  const int32_t* vert_cnt;
+  int32_t max_vert;
+  const int32_t* runs;
+  const int32_t* run_cnt;
+  int32_t max_runs;
+  int64_t n_ctx, c0;
+  int32_t n_rb, n_sub, nw, G;
+  int64_t ubw;
+  uint32_t* ubits;
+  int32_t* vl;
+  int32_t* vl_cnt;
+  int32_t dense;
+  uint64_t head_mask;
+};
 
-// Per (query tile, head): the verticals v <= the tile's last row that no
-// slash span of the tile covers (no selected offset in [r0 - v, r0 + 127 -
-// v]), ascending.
-__global__ void __launch_bounds__(kVlThreads) vert_list_kernel(AuxArgs a) {
-  const int64_t qt = blockIdx.x;
-  const int h = blockIdx.y;
-  if (!((a.head_mask >> h) & 1) || a.dense) return;
-  const int64_t r0 = a.c0 + qt * kTileQ;
-  const int64_t rlast = r0 + kTileQ - 1 < a.n_ctx - 1 ? r0 + kTileQ - 1 : a.n_ctx - 1;
-  const int nv = min(a.vert_cnt[h], a.max_vert);
-  const int32_t* vo = a.vert_idx + (int64_t)h * a.max_vert;
-  const uint32_t* ob = a.off_bits + (int64_t)h * a.n_words + kBitPad;
-  int32_t* out = a.vl + ((int64_t)h * a.n_qt + qt) * a.max_vert;
-  __shared__ int s_wave[kVlThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int total = 0;
-  for (int b0 = 0; b0 < nv; b0 += kVlThreads) {
-    if (vo[b0] > rlast) break;
-    const int i = b0 + tid;
-    bool keep = false;
-    int32_t v = 0;
-    if (i < nv) {
-      v = vo[i];
-      if (v >= 0 && v <= rlast) {
-        const int64_t olo = r0 - v > 0 ? r0 - v : 0;
-        keep = !any_bits(ob, olo, r0 + kTileQ - 1 - v);
-      }
-    }
-    const uint64_t bal = __ballot(keep);
-    __syncthreads();
-    if (lane == 0) s_wave[w] = __popcll(bal);
-    __syncthreads();
-    int base = total, tot = 0;
-    for (int x = 0; x < kVlThreads / 64; ++x) {
-      if (x < w) base += s_wave[x];
-      tot += s_wave[x];
-    }
-    if (keep) {
-      const int below = (int)__builtin_amdgcn_mbcnt_hi(
-          (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      out[base + below] = v;
-    }
-    total += tot;
+constexpr int kPlanThreads = 256;
+
+// Set bits [g0, g1] of an LDS bitmap.
+__device__ __forceinline__ void set_bits(uint32_t* bm, int32_t g0, int32_t g1) {
+  for (int32_t wi = g0 >> 5; wi <= (g1 >> 5); ++wi) {
+    const int32_t lo = max(g0, wi * 32) - wi * 32, hi = min(g1, wi * 32 + 31) - wi * 32;
+    const uint32_t m = (hi == 31 ? 0xFFFFFFFFu : ((1u << (hi + 1)) - 1u)) & ~((1u << lo) - 1u);
+    atomicOr(&bm[wi], m);
   }
-  if (tid == 0) a.vl_cnt[(int64_t)h * a.n_qt + qt] = total;
+}
+
+// Per (row block, KV sub-group): the granules any of its heads' slash runs
+// reach in the row block, and per head the verticals (<= the block's last
+// row) in unmarked granules, ascending.
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
+  extern __shared__ uint32_t bm[];
+  const int rb = blockIdx.x, wgg = blockIdx.y;
+  const int g = wgg / a.n_sub, sub = wgg % a.n_sub;
+  const int h_first = g * a.G + sub * a.nw;
+  const int n_here = min(a.nw, a.G - sub * a.nw);
+  const int64_t r0 = a.c0 + (int64_t)rb * kRowBlock;
+  const int64_t rlast = r0 + kRowBlock - 1 < a.n_ctx - 1 ? r0 + kRowBlock - 1 : a.n_ctx - 1;
+  const int32_t glast = (int32_t)(rlast / kGranule);
+  const int32_t nwords = glast / 32 + 1;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nwords; i += kPlanThreads) bm[i] = 0u;
+  __syncthreads();
+  for (int hh = 0; hh < n_here; ++hh) {
+    const int h = h_first + hh;
+    if (!((a.head_mask >> h) & 1)) continue;
+    if (a.dense) {
+      const uint32_t last = glast % 32 == 31 ? 0xFFFFFFFFu : (1u << (glast % 32 + 1)) - 1u;
+      for (int i = tid; i < nwords; i += kPlanThreads)
+        atomicOr(&bm[i], i < nwords - 1 ? 0xFFFFFFFFu : last);
+      continue;
+    }
+    const int nr = min(a.run_cnt[h], a.max_runs);
+    const int32_t* rr = a.runs + (int64_t)h * a.max_runs * 2;
+    for (int i = tid; i < nr; i += kPlanThreads) {
+      const int64_t oa = rr[2 * i], ob = rr[2 * i + 1];
+      if (oa > rlast) continue;
+      const int64_t lo = r0 - ob > 0 ? r0 - ob : 0, hi = rlast - oa;
+      set_bits(bm, (int32_t)(lo / kGranule), (int32_t)(hi / kGranule));
+    }
+  }
+  __syncthreads();
+  uint32_t* dst = a.ubits + ((int64_t)wgg * a.n_rb + rb) * a.ubw;
+  for (int i = tid; i < nwords; i += kPlanThreads) dst[i] = bm[i];
+  if (a.dense) {
+    for (int hh = tid; hh < n_here; hh += kPlanThreads)
+      a.vl_cnt[(int64_t)(h_first + hh) * a.n_rb + rb] = 0;
+    return;
+  }
+  __shared__ int s_wave[kPlanThreads / 64];
+  const int lane = tid & 63, w = tid >> 6;
+  for (int hh = 0; hh < n_here; ++hh) {
+    const int h = h_first + hh;
+    if (!((a.head_mask >> h) & 1)) continue;
+    const int nv = min(a.vert_cnt[h], a.max_vert);
+    const int32_t* vo = a.vert_idx + (int64_t)h * a.max_vert;
+    int32_t* out = a.vl + ((int64_t)h * a.n_rb + rb) * a.max_vert;
+    int total = 0;
+    for (int b0 = 0; b0 < nv; b0 += kPlanThreads) {
+      if (vo[b0] > rlast) break;
+      const int i = b0 + tid;
+      bool keep = false;
+      int32_t v = 0;
+      if (i < nv) {
+        v = vo[i];
+        if (v >= 0 && v <= rlast) {
+          const int32_t gi = v / kGranule;
+          keep = !((bm[gi >> 5] >> (gi & 31)) & 1u);
+        }
+      }
+      const uint64_t bal = __ballot(keep);
+      __syncthreads();
+      if (lane == 0) s_wave[w] = __popcll(bal);
+      __syncthreads();
+      int base = total, tot = 0;
+      for (int x = 0; x < kPlanThreads / 64; ++x) {
+        if (x < w) base += s_wave[x];
+        tot += s_wave[x];
+      }
+      if (keep) {
+        const int below = (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        out[base + below] = v;
+      }
+      total += tot;
+    }
+    if (tid == 0) a.vl_cnt[(int64_t)h * a.n_rb + rb] = total;
+  }
+}
+
+template <int D, int NW>
+int launch_attn(const AttnArgs& a, int64_t grid, size_t dyn_lds, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * (NW + 1)), dyn_lds, s,
+                     a);
+  return check_launch("sparse attention");
+}
+
+template <int D>
+int launch_attn_nw(const AttnArgs& a, int nw, int64_t grid, size_t dyn_lds, hipStream_t s) {
+  switch (nw) {
+    case 1: return launch_attn<D, 1>(a, grid, dyn_lds, s);
+    case 2: return launch_attn<D, 2>(a, grid, dyn_lds, s);
+    case 3: return launch_attn<D, 3>(a, grid, dyn_lds, s);
+    case 4: return launch_attn<D, 4>(a, grid, dyn_lds, s);
+    case 5: return launch_attn<D, 5>(a, grid, dyn_lds, s);
+    case 6: return launch_attn<D, 6>(a, grid, dyn_lds, s);
+    case 7: return launch_attn<D, 7>(a, grid, dyn_lds, s);
+    default: return fail(LCSR_ENOTSUP, "%d query heads per workgroup", nw);
+  }
 }
 
 }  // namespace
+
+// Largest context the attention supports: the row block's granule bitmap
+// shares the 160 KB of LDS with the four K/V stages.
+int64_t attn_max_context(int64_t head_dim) {
+  const int64_t stages = kStages * (head_dim == 128 ? Buf<128>::kBytes : Buf<64>::kBytes);
+  const int64_t rings = kRing * 16;  // descriptors
+  const int64_t words = (160 * 1024 - stages - rings - 64) / 4;
+  return words * 32 * kGranule;
+}
 
 int build_pattern_aux(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head_mask,
                       bool dense, const AttnLayout& L, char* ws, hipStream_t s) {
@@ -840,24 +1137,42 @@ int build_pattern_aux(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64
   a.col_bits = reinterpret_cast<uint32_t*>(ws + L.o_col_bits);
   a.runs = reinterpret_cast<int32_t*>(ws + L.o_runs);
   a.run_cnt = reinterpret_cast<int32_t*>(ws + L.o_run_cnt);
-  a.vl = reinterpret_cast<int32_t*>(ws + L.o_vl);
-  a.vl_cnt = reinterpret_cast<int32_t*>(ws + L.o_vl_cnt);
-  a.c0 = p.chunk_start;
-  a.n_qt = L.n_qt;
   a.dense = dense ? 1 : 0;
   a.head_mask = head_mask;
   hipLaunchKernelGGL(aux_kernel, dim3(p.n_heads), dim3(kAuxThreads), 0, s, a);
   int rc = check_launch("pattern aux");
-  if (rc || dense || !L.with_vl) return rc;
-  hipLaunchKernelGGL(vert_list_kernel, dim3((unsigned)L.n_qt, p.n_heads), dim3(kVlThreads), 0,
-                     s, a);
-  return check_launch("vertical lists");
+  if (rc || !L.with_plan) return rc;
+  PlanArgs b{};
+  b.vert_idx = pat.vert_idx;
+  b.vert_cnt = pat.vert_cnt;
+  b.max_vert = dense ? 1 : pat.max_vert;
+  b.runs = a.runs;
+  b.run_cnt = a.run_cnt;
+  b.max_runs = dense ? 1 : pat.max_slash;
+  b.n_ctx = L.n_ctx;
+  b.c0 = p.chunk_start;
+  b.n_rb = (int32_t)L.n_rb;
+  b.n_sub = (int32_t)L.n_sub;
+  b.nw = (int32_t)L.nw;
+  b.G = p.n_heads / p.n_kv_heads;
+  b.ubw = L.ubw;
+  b.ubits = reinterpret_cast<uint32_t*>(ws + L.o_union);
+  b.vl = reinterpret_cast<int32_t*>(ws + L.o_vl);
+  b.vl_cnt = reinterpret_cast<int32_t*>(ws + L.o_vl_cnt);
+  b.dense = dense ? 1 : 0;
+  b.head_mask = head_mask;
+  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)L.n_rb, (unsigned)L.n_wgg), dim3(kPlanThreads),
+                     (size_t)L.ubw * 4, s, b);
+  return check_launch("attention plan");
 }
 
 int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head_mask,
                   void* out, int32_t out_dtype, int64_t o_sh, int64_t o_st, float* lse,
                   int64_t* stats, bool dense, char* ws, hipStream_t s) {
   const AttnLayout L = attn_layout(p, dense ? 1 : pat.max_vert, dense ? 1 : pat.max_slash, true);
+  if (L.n_ctx > attn_max_context(p.head_dim))
+    return fail(LCSR_ENOTSUP, "attention supports contexts up to %lld tokens at head_dim %d",
+                (long long)attn_max_context(p.head_dim), p.head_dim);
   FreqTable ft;
   int rc = build_freq_table(&p.rope, p.head_dim, &ft);
   if (rc) return rc;
@@ -879,19 +1194,22 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t h
   a.c0 = p.chunk_start;
   a.L = p.chunk_len;
   a.n_ctx = L.n_ctx;
-  a.period = d.period;
-  a.n_qt = L.n_qt;
-  a.n_blocks = (int64_t)p.n_heads * a.n_qt;
+  // a DCA chunk longer than the context changes nothing (every key and query
+  // is in chunk 0); capping it keeps the chunk edges inside int32
+  a.period = d.period ? std::min<int64_t>(d.period, (L.n_ctx + kTileK) / kTileK * kTileK) : 0;
   a.scale_log2 = p.sm_scale * kLog2e;
   a.off_bits = reinterpret_cast<const uint32_t*>(ws + L.o_off_bits);
   a.col_bits = reinterpret_cast<const uint32_t*>(ws + L.o_col_bits);
   a.n_words = L.n_words;
-  a.runs = reinterpret_cast<const int32_t*>(ws + L.o_runs);
-  a.run_cnt = reinterpret_cast<const int32_t*>(ws + L.o_run_cnt);
-  a.max_runs = dense ? 1 : pat.max_slash;
+  a.ubits = reinterpret_cast<const uint32_t*>(ws + L.o_union);
+  a.ubw = L.ubw;
   a.vl = reinterpret_cast<const int32_t*>(ws + L.o_vl);
   a.vl_cnt = reinterpret_cast<const int32_t*>(ws + L.o_vl_cnt);
   a.max_vert = dense ? 1 : pat.max_vert;
+  a.n_rb = (int32_t)L.n_rb;
+  a.n_sub = (int32_t)L.n_sub;
+  a.nw = (int32_t)L.nw;
+  a.n_wgg = (int32_t)L.n_wgg;
   a.dense = dense ? 1 : 0;
   a.head_mask = head_mask;
   a.out = out;
@@ -900,26 +1218,11 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t h
   a.o_st = o_st;
   a.lse = lse;
   a.stats = reinterpret_cast<unsigned long long*>(stats);
-  const int64_t grid = (a.n_blocks + 7) / 8 * 8;
-  // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
-  static const hipError_t attr_rc[2] = {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<64>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)attn_smem_bytes<64>()),
-      hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<128>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)attn_smem_bytes<128>())};
-  if (attr_rc[p.head_dim == 128 ? 1 : 0] != hipSuccess)
-    return fail(LCSR_EHIP, "cannot raise the LDS limit of the attention kernel: %s",
-                hipGetErrorString(attr_rc[p.head_dim == 128 ? 1 : 0]));
-  if (p.head_dim == 128) {
-    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)grid), dim3(kThreads),
-                       attn_smem_bytes<128>(), s, a);
-  } else {
-    hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)grid), dim3(kThreads),
-                       attn_smem_bytes<64>(), s, a);
-  }
-  return check_launch("sparse attention");
+  const int64_t nb = L.n_wgg * L.n_rb;
+  const int64_t grid = (nb + 7) / 8 * 8;
+  const size_t dyn = (size_t)L.ubw * 4;
+  if (p.head_dim == 128) return launch_attn_nw<128>(a, (int)L.nw, grid, dyn, s);
+  return launch_attn_nw<64>(a, (int)L.nw, grid, dyn, s);
 }
 
 }  // namespace lcsr

@@ -27,8 +27,10 @@ constexpr int kMaxHeads = 64;
 constexpr int kMaxHalfDim = 64;          // head_dim <= 128 for attention
 constexpr int kMaxRopeHalf = 128;        // head_dim <= 256 for rope_yarn_apply
 constexpr int kMaxGroup = 16;            // n_heads / n_kv_heads
-constexpr int kTileQ = 128;              // query rows per attention workgroup
+constexpr int kRowBlock = 32;            // query rows per attention workgroup
 constexpr int kTileK = 64;               // keys per tile (attention, estimate)
+constexpr int kGranule = 16;             // keys per bit of a row block's key-span bitmap
+constexpr int kMaxAttnWaves = 7;         // query heads per attention workgroup (+1 loader wave)
 constexpr int kEstRows = 64;             // largest last_q
 constexpr int kBitPad = 8;               // zero words before and after each head's bitmap
 
@@ -142,9 +144,14 @@ struct EstimateLayout {
   size_t q_est, part, lse, vscore, sscore, diag, total;
 };
 struct AttnLayout {
-  int64_t n_ctx, n_words, n_var, n_qt;
-  bool with_vl;  // per-tile leftover vertical lists (attention only)
-  size_t o_q_rot, o_off_bits, o_col_bits, o_runs, o_run_cnt, o_vl, o_vl_cnt, total;
+  int64_t n_ctx, n_words, n_var;
+  int64_t n_rb;      // query row blocks of kRowBlock rows
+  int64_t n_sub;     // workgroups per KV group (heads split into groups of <= 8)
+  int64_t nw;        // query heads (waves) per workgroup
+  int64_t n_wgg;     // KV head x sub-group
+  int64_t ubw;       // 32-bit words of one row block's granule bitmap
+  bool with_plan;    // attention: union bitmaps and leftover vertical lists
+  size_t o_q_rot, o_off_bits, o_col_bits, o_runs, o_run_cnt, o_union, o_vl, o_vl_cnt, total;
 };
 EstimateLayout estimate_layout(const lcsr_problem_t& p);
 AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_slash,
