@@ -55,7 +55,8 @@ EstimateLayout estimate_layout(const lcsr_problem_t& p) {
   L.vscore = align256((size_t)H * L.n_ctx * sizeof(float));
   L.sscore = L.vscore;
   L.diag = align256((size_t)H * L.n_diag * 2 * 64 * sizeof(float));
-  L.total = L.q_est + L.part + L.lse + L.vscore + L.sscore + L.diag;
+  L.topk = align256(topk_workspace(L.n_ctx, (int)H));
+  L.total = L.q_est + L.part + L.lse + L.vscore + L.sscore + L.diag + L.topk;
   return L;
 }
 

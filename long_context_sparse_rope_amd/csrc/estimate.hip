@@ -330,10 +330,6 @@ __global__ void est_slash_reduce(EstArgs a) {
 
 }  // namespace
 
-int launch_topk(const float* scores, int64_t n, int64_t score_stride, int n_heads,
-                uint64_t head_mask, const int32_t* budget, int32_t* idx, int32_t max_k,
-                int32_t* cnt, hipStream_t s);
-
 int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
                  const lcsr_pattern_t& pat, float* vscore, float* sscore,
                  bool select_only, char* ws, hipStream_t s) {
@@ -350,6 +346,8 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
   float* ss_ws = reinterpret_cast<float*>(cur);
   cur += L.sscore;
   float* diag = reinterpret_cast<float*>(cur);
+  cur += L.diag;
+  void* topk_ws = cur;
   float* vsc = vscore ? vscore : vs_ws;
   float* ssc = sscore ? sscore : ss_ws;
   const int64_t c1 = L.n_ctx;
@@ -408,11 +406,23 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     rc = check_launch("estimate slash reduce");
     if (rc) return rc;
   }
-  int rc = launch_topk(vsc, c1, c1, p.n_heads, hs.mask, hs.n_vert, pat.vert_idx, pat.max_vert,
-                       pat.vert_cnt, s);
-  if (rc) return rc;
-  return launch_topk(ssc, c1, c1, p.n_heads, hs.mask, hs.n_slash, pat.slash_idx, pat.max_slash,
-                     pat.slash_cnt, s);
+  TopkRequest r{};
+  r.scores[0] = vsc;
+  r.scores[1] = ssc;
+  r.idx[0] = pat.vert_idx;
+  r.idx[1] = pat.slash_idx;
+  r.cnt[0] = pat.vert_cnt;
+  r.cnt[1] = pat.slash_cnt;
+  r.max_k[0] = pat.max_vert;
+  r.max_k[1] = pat.max_slash;
+  r.budget[0] = hs.n_vert;
+  r.budget[1] = hs.n_slash;
+  r.n = c1;
+  r.stride = c1;
+  r.n_heads = (int)p.n_heads;
+  r.head_mask = hs.mask;
+  r.ws = topk_ws;
+  return launch_topk(r, s);
 }
 
 }  // namespace lcsr

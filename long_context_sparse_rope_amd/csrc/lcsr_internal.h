@@ -141,7 +141,7 @@ namespace lcsr {
 // Byte layout of the caller's workspace for each call (host side).
 struct EstimateLayout {
   int64_t n_ctx, n_tiles, n_kc, n_split, n_diag;
-  size_t q_est, part, lse, vscore, sscore, diag, total;
+  size_t q_est, part, lse, vscore, sscore, diag, topk, total;
 };
 struct AttnLayout {
   int64_t n_ctx, n_words, n_var;
@@ -163,6 +163,21 @@ struct HeadSet {
   int32_t n_vert[kMaxHeads];  // budgets (estimate)
   int32_t n_slash[kMaxHeads];
 };
+
+// Top-k of the vertical (set 0) and slash (set 1) score rows of every head.
+struct TopkRequest {
+  const float* scores[2];  // [n_heads][stride]
+  int32_t* idx[2];         // [n_heads][max_k[set]]
+  int32_t* cnt[2];         // [n_heads]
+  int32_t max_k[2];
+  const int32_t* budget[2];  // host arrays of n_heads budgets
+  int64_t n, stride;
+  int n_heads;
+  uint64_t head_mask;
+  void* ws;                // topk_workspace(n, n_heads) bytes
+};
+size_t topk_workspace(int64_t n, int n_heads);
+int launch_topk(const TopkRequest& r, hipStream_t s);
 
 int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
                  const lcsr_pattern_t& pat, float* vscore, float* sscore,

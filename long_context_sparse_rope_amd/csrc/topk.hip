@@ -1,29 +1,52 @@
-// Deterministic top-k of a score row, ties to the lower index, written in
+// Deterministic top-k of score rows, ties to the lower index, written in
 // ascending index order (page: "論文解説: Qwen2.5-1M" (0h-n0.github.io),
 // 疎アテンション: critical vertical and slash lines are chosen dynamically;
 // the order and the tie rule are ours: score descending, index ascending).
 //
-// One workgroup of 16 waves per head.  Scores are mapped to order-preserving
-// unsigned keys; a 4-round 8-bit radix select finds the exact key T of the
-// k-th largest score and how many ties at T are needed; then each wave
-// compacts one contiguous segment of the row with ballots, so the output is
-// ascending and every decision is integer-exact.
+// Whole-chip radix select over every row at once (the vertical and the slash
+// scores of every head).  Scores map to order-preserving unsigned keys and
+// each row is cut into slices of kSlice keys, one workgroup per slice:
+//   hist(l), l = 0, 1, 2   keys that match the prefix found so far are
+//                          counted by their next 12, 12, 8 bits in LDS; the
+//                          non-zero bins are added to the row's histogram;
+//   pick(l)                one workgroup per row finds the bin that holds the
+//                          k-th largest key and extends the prefix;
+//   count                  per slice: keys above T and equal to T, where T is
+//                          the exact key of the k-th largest score;
+//   compact                each slice writes its selected indices after those
+//                          of the slices before it, in ascending order; ties
+//                          at T are taken from the lowest indices.
+// Every decision is on integers, so the result does not depend on timing.
 #include "lcsr_internal.h"
 
 namespace lcsr {
 
 namespace {
 
-constexpr int kTopkWaves = 16;
+constexpr int kSlice = 16384;                 // keys per workgroup
+constexpr int kThreads = 256;
+constexpr int kPerThread = kSlice / kThreads;  // 64
+constexpr int kBins = 4096;
+constexpr int kLevels = 3;
+
+enum : uint32_t { kModeSelect = 0, kModeAll = 1, kModeNone = 2 };
+
+struct TopkSet {
+  const float* scores;  // [H][stride]
+  int32_t* idx;         // [H][max_k]
+  int32_t* cnt;         // [H]
+  int32_t max_k;
+  int32_t budget[kMaxHeads];
+};
 
 struct TopkArgs {
-  const float* scores;
+  TopkSet set[2];
   int64_t n, stride;
   uint64_t head_mask;
-  int32_t budget[kMaxHeads];
-  int32_t* idx;
-  int32_t max_k;
-  int32_t* cnt;
+  int32_t n_heads, n_slices;
+  uint32_t* hist;    // [2][H][kLevels][kBins]
+  uint32_t* state;   // [2][H][4]: prefix, prefix mask, remaining, mode | k << 2
+  uint32_t* counts;  // [2][H][n_slices][2]: above T, equal to T
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -37,120 +60,290 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__global__ void __launch_bounds__(64 * kTopkWaves) topk_kernel(TopkArgs a) {
-  const int h = blockIdx.x;
-  if (!((a.head_mask >> h) & 1)) return;
-  const float* sc = a.scores + (int64_t)h * a.stride;
-  int32_t* out = a.idx + (int64_t)h * a.max_k;
-  const int64_t n = a.n;
-  const int64_t k = a.budget[h] < n ? a.budget[h] : n;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int nthr = blockDim.x;
+__device__ __forceinline__ int level_shift(int l) { return l == 0 ? 20 : (l == 1 ? 8 : 0); }
+__device__ __forceinline__ uint32_t level_mask(int l) { return l == 2 ? 0xFFu : 0xFFFu; }
 
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_rem;
-  __shared__ uint32_t s_gt[kTopkWaves], s_eq[kTopkWaves];
+__device__ __forceinline__ int64_t row_k(const TopkArgs& a, int set, int h) {
+  const int64_t b = a.set[set].budget[h];
+  return b < a.n ? (b > 0 ? b : 0) : a.n;
+}
 
-  if (k >= n) {  // every index is selected
-    for (int64_t i = tid; i < n; i += nthr) out[i] = (int32_t)i;
-    for (int64_t i = n + tid; i < a.max_k; i += nthr) out[i] = -1;
-    if (tid == 0) a.cnt[h] = (int32_t)n;
-    return;
+__device__ __forceinline__ bool row_live(const TopkArgs& a, int h) {
+  return (a.head_mask >> h) & 1;
+}
+
+// ------------------------------------------------------------- histogram
+__global__ void __launch_bounds__(kThreads) topk_hist(TopkArgs a, int level) {
+  const int slice = blockIdx.x, h = blockIdx.y, set = blockIdx.z;
+  if (!row_live(a, h)) return;
+  const int64_t row = (int64_t)set * a.n_heads + h;
+  uint32_t prefix = 0, pmask = 0;
+  if (level == 0) {
+    const int64_t k = row_k(a, set, h);
+    if (k == 0 || k >= a.n) return;
+  } else {
+    const uint32_t* st = a.state + row * 4;
+    if ((st[3] & 3u) != kModeSelect) return;
+    prefix = st[0];
+    pmask = st[1];
   }
-  if (k == 0) {
-    for (int64_t i = tid; i < a.max_k; i += nthr) out[i] = -1;
-    if (tid == 0) a.cnt[h] = 0;
-    return;
-  }
-
-  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256; b += nthr) hist[b] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += nthr) {
+  __shared__ uint32_t hist[kBins];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kBins / kThreads; ++j) hist[j * kThreads + tid] = 0;
+  __syncthreads();
+  const int shift = level_shift(level);
+  const uint32_t bmask = level_mask(level);
+  const float* sc = a.set[set].scores + h * a.stride;
+  const int64_t s0 = (int64_t)slice * kSlice;
+  const int64_t s1 = s0 + kSlice < a.n ? s0 + kSlice : a.n;
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t i = s0 + (int64_t)j * kThreads + tid;
+    if (i < s1) {
       const uint32_t key = order_key(sc[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & bmask], 1u);
     }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t cum = 0, digit = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hist[b] >= rem) {
-          digit = (uint32_t)b;
-          break;
-        }
-        cum += hist[b];
-      }
-      s_rem = rem - cum;
-      s_prefix = prefix | (digit << shift);
-    }
-    __syncthreads();
-    rem = s_rem;
-    prefix = s_prefix;
-    pmask |= 0xFFu << shift;
-    __syncthreads();
   }
-  const uint32_t T = prefix;      // key of the k-th largest score
-  const uint32_t need_eq = rem;   // ties at T to keep, lowest indices first
+  __syncthreads();
+  uint32_t* hg = a.hist + (row * kLevels + level) * kBins;
+#pragma unroll
+  for (int j = 0; j < kBins / kThreads; ++j) {
+    const int b = j * kThreads + tid;
+    if (hist[b]) atomicAdd(&hg[b], hist[b]);
+  }
+}
 
-  // contiguous segment of the row for this wave (multiple of 64 long)
-  const int64_t seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) / 64 * 64;
-  const int64_t s0 = (int64_t)w * seg;
-  const int64_t s1 = s0 + seg < n ? s0 + seg : n;
+// ------------------------------------------------------------- pick a bin
+// Thread t owns the 16 bins [kBins - 16 (t + 1), kBins - 16 t): thread 0 the
+// largest keys.  An exclusive scan over threads gives the count above each
+// range; the thread whose range holds the rem-th largest key walks it.
+__global__ void __launch_bounds__(kThreads) topk_pick(TopkArgs a, int level) {
+  const int h = blockIdx.x, set = blockIdx.y;
+  if (!row_live(a, h)) return;
+  const int64_t row = (int64_t)set * a.n_heads + h;
+  uint32_t* st = a.state + row * 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t prefix = 0, pmask = 0, rem;
+  if (level == 0) {
+    const int64_t k = row_k(a, set, h);
+    const uint32_t mode = k == 0 ? kModeNone : (k >= a.n ? kModeAll : kModeSelect);
+    if (mode != kModeSelect) {
+      if (tid == 0) {
+        st[0] = 0;
+        st[1] = 0;
+        st[2] = 0;
+        st[3] = mode | ((uint32_t)k << 2);
+      }
+      return;
+    }
+    rem = (uint32_t)k;
+  } else {
+    if ((st[3] & 3u) != kModeSelect) return;
+    prefix = st[0];
+    pmask = st[1];
+    rem = st[2];
+  }
+  const uint32_t* hg = a.hist + (row * kLevels + level) * kBins;
+  constexpr int kPer = kBins / kThreads;
+  const int top = kBins - kPer * tid;  // bins [top - kPer, top)
+  uint32_t v[kPer];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    v[j] = hg[top - 1 - j];
+    sum += v[j];
+  }
+  // inclusive scan within the wave, then over the four waves
+  uint32_t inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  __shared__ uint32_t wsum[kThreads / 64];
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  uint32_t above = inc - sum;
+  for (int u = 0; u < w; ++u) above += wsum[u];
+  if (above < rem && above + sum >= rem) {
+    uint32_t cum = above, digit = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (cum + v[j] >= rem) {
+        digit = (uint32_t)(top - 1 - j);
+        break;
+      }
+      cum += v[j];
+    }
+    const int shift = level_shift(level);
+    st[0] = prefix | (digit << shift);
+    st[1] = pmask | (level_mask(level) << shift);
+    st[2] = rem - cum;
+    if (level == 0) st[3] = kModeSelect | ((uint32_t)row_k(a, set, h) << 2);
+  }
+}
+
+// ------------------------------------------------------------- count
+__global__ void __launch_bounds__(kThreads) topk_count(TopkArgs a) {
+  const int slice = blockIdx.x, h = blockIdx.y, set = blockIdx.z;
+  if (!row_live(a, h)) return;
+  const int64_t row = (int64_t)set * a.n_heads + h;
+  const uint32_t* st = a.state + row * 4;
+  if ((st[3] & 3u) != kModeSelect) return;
+  const uint32_t T = st[0];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* sc = a.set[set].scores + h * a.stride;
+  const int64_t s0 = (int64_t)slice * kSlice;
+  const int64_t s1 = s0 + kSlice < a.n ? s0 + kSlice : a.n;
   uint32_t gt = 0, eq = 0;
-  for (int64_t base = s0; base < s1; base += 64) {
-    const int64_t i = base + lane;
-    const uint32_t key = i < s1 ? order_key(sc[i]) : 0u;
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t i = s0 + (int64_t)j * kThreads + tid;
     const bool valid = i < s1;
+    const uint32_t key = valid ? order_key(sc[i]) : 0u;
     gt += __popcll(__ballot(valid && key > T));
     eq += __popcll(__ballot(valid && key == T));
   }
+  __shared__ uint32_t wc[kThreads / 64][2];
   if (lane == 0) {
-    s_gt[w] = gt;
-    s_eq[w] = eq;
+    wc[w][0] = gt;
+    wc[w][1] = eq;
   }
   __syncthreads();
-  uint32_t eq_before = 0, out_base = 0;
-  for (int v = 0; v < w; ++v) {
-    const uint32_t take = need_eq > eq_before ? (need_eq - eq_before < s_eq[v] ? need_eq - eq_before
-                                                                               : s_eq[v])
-                                              : 0u;
-    out_base += s_gt[v] + take;
-    eq_before += s_eq[v];
+  if (tid == 0) {
+    uint32_t g = 0, e = 0;
+    for (int u = 0; u < kThreads / 64; ++u) {
+      g += wc[u][0];
+      e += wc[u][1];
+    }
+    uint32_t* c = a.counts + (row * a.n_slices + slice) * 2;
+    c[0] = g;
+    c[1] = e;
+  }
+}
+
+__device__ __forceinline__ uint32_t take_eq(uint32_t need, uint32_t before, uint32_t eq) {
+  if (need <= before) return 0u;
+  return need - before < eq ? need - before : eq;
+}
+
+// ------------------------------------------------------------- compact
+// Wave w of the slice owns keys [s0 + 4096 w, s0 + 4096 (w + 1)), lane-
+// interleaved in steps of 64, held in registers between the count and the
+// write.
+__global__ void __launch_bounds__(kThreads) topk_compact(TopkArgs a) {
+  const int slice = blockIdx.x, h = blockIdx.y, set = blockIdx.z;
+  if (!row_live(a, h)) return;
+  const int64_t row = (int64_t)set * a.n_heads + h;
+  const TopkSet& S = a.set[set];
+  const uint32_t* st = a.state + row * 4;
+  const uint32_t mode = st[3] & 3u;
+  const int64_t k = st[3] >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t* out = S.idx + (int64_t)h * S.max_k;
+  const int64_t s0 = (int64_t)slice * kSlice;
+  const int64_t s1 = s0 + kSlice < a.n ? s0 + kSlice : a.n;
+  if (slice == 0) {
+    for (int64_t i = k + tid; i < S.max_k; i += kThreads) out[i] = -1;
+    if (tid == 0) S.cnt[h] = (int32_t)k;
+  }
+  if (mode == kModeNone) return;
+  if (mode == kModeAll) {
+    for (int64_t i = s0 + tid; i < s1; i += kThreads) out[i] = (int32_t)i;
+    return;
+  }
+  const uint32_t T = st[0], need_eq = st[2];
+  // selected keys and ties at T in the slices before this one
+  const uint32_t* cnts = a.counts + row * a.n_slices * 2;
+  uint32_t base = 0, eq_before = 0;
+  for (int u = 0; u < slice; ++u) {
+    const uint32_t g = cnts[u * 2], e = cnts[u * 2 + 1];
+    base += g + take_eq(need_eq, eq_before, e);
+    eq_before += e;
+  }
+  constexpr int kPerWave = kSlice / (kThreads / 64);
+  constexpr int kSteps = kPerWave / 64;
+  const int64_t w0 = s0 + (int64_t)w * kPerWave;
+  const float* sc = S.scores + h * a.stride;
+  uint32_t key[kSteps];
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    const int64_t i = w0 + j * 64 + lane;
+    key[j] = i < s1 ? order_key(sc[i]) : 0u;  // key 0 ranks below every score
+    gt += __popcll(__ballot(i < s1 && key[j] > T));
+    eq += __popcll(__ballot(i < s1 && key[j] == T));
+  }
+  __shared__ uint32_t wc[kThreads / 64][2];
+  if (lane == 0) {
+    wc[w][0] = gt;
+    wc[w][1] = eq;
+  }
+  __syncthreads();
+  for (int u = 0; u < w; ++u) {
+    base += wc[u][0] + take_eq(need_eq, eq_before, wc[u][1]);
+    eq_before += wc[u][1];
   }
   uint32_t eq_seen = 0, sel_seen = 0;
-  for (int64_t base = s0; base < s1; base += 64) {
-    const int64_t i = base + lane;
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    const int64_t i = w0 + j * 64 + lane;
     const bool valid = i < s1;
-    const uint32_t key = valid ? order_key(sc[i]) : 0u;
-    const bool is_eq = valid && key == T;
+    const bool is_eq = valid && key[j] == T;
     const uint64_t eq_mask = __ballot(is_eq);
     const uint32_t rank = eq_before + eq_seen + lanes_below(eq_mask);
-    const bool sel = valid && (key > T || (is_eq && rank < need_eq));
+    const bool sel = valid && (key[j] > T || (is_eq && rank < need_eq));
     const uint64_t sel_mask = __ballot(sel);
-    if (sel) out[out_base + sel_seen + lanes_below(sel_mask)] = (int32_t)i;
+    if (sel) out[base + sel_seen + lanes_below(sel_mask)] = (int32_t)i;
     eq_seen += __popcll(eq_mask);
     sel_seen += __popcll(sel_mask);
   }
-  for (int64_t i = k + tid; i < a.max_k; i += nthr) out[i] = -1;
-  if (tid == 0) a.cnt[h] = (int32_t)k;
 }
 
 }  // namespace
 
-int launch_topk(const float* scores, int64_t n, int64_t score_stride, int n_heads,
-                uint64_t head_mask, const int32_t* budget, int32_t* idx, int32_t max_k,
-                int32_t* cnt, hipStream_t s) {
+size_t topk_workspace(int64_t n, int n_heads) {
+  const int64_t n_slices = (n + kSlice - 1) / kSlice;
+  const size_t hist = (size_t)2 * n_heads * kLevels * kBins * 4;
+  const size_t state = (size_t)2 * n_heads * 4 * 4;
+  const size_t counts = (size_t)2 * n_heads * (n_slices > 0 ? n_slices : 1) * 2 * 4;
+  return ((hist + 255) & ~(size_t)255) + ((state + 255) & ~(size_t)255) +
+         ((counts + 255) & ~(size_t)255);
+}
+
+int launch_topk(const TopkRequest& r, hipStream_t s) {
   TopkArgs a{};
-  a.scores = scores;
-  a.n = n;
-  a.stride = score_stride;
-  a.head_mask = head_mask;
-  for (int h = 0; h < n_heads; ++h) a.budget[h] = budget[h];
-  a.idx = idx;
-  a.max_k = max_k;
-  a.cnt = cnt;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_heads), dim3(64 * kTopkWaves), 0, s, a);
+  for (int z = 0; z < 2; ++z) {
+    a.set[z].scores = r.scores[z];
+    a.set[z].idx = r.idx[z];
+    a.set[z].cnt = r.cnt[z];
+    a.set[z].max_k = r.max_k[z];
+    for (int h = 0; h < r.n_heads; ++h) a.set[z].budget[h] = r.budget[z][h];
+  }
+  a.n = r.n;
+  a.stride = r.stride;
+  a.head_mask = r.head_mask;
+  a.n_heads = r.n_heads;
+  const int64_t n_slices = (r.n + kSlice - 1) / kSlice;
+  if (n_slices > 65535) return fail(LCSR_ENOTSUP, "top-k over more than %lld scores",
+                                    (long long)65535 * kSlice);
+  a.n_slices = (int32_t)(n_slices > 0 ? n_slices : 1);
+  char* cur = static_cast<char*>(r.ws);
+  const size_t hist = (size_t)2 * r.n_heads * kLevels * kBins * 4;
+  a.hist = reinterpret_cast<uint32_t*>(cur);
+  cur += (hist + 255) & ~(size_t)255;
+  a.state = reinterpret_cast<uint32_t*>(cur);
+  cur += ((size_t)2 * r.n_heads * 4 * 4 + 255) & ~(size_t)255;
+  a.counts = reinterpret_cast<uint32_t*>(cur);
+  int rc = launch_fill_zero(a.hist, hist, s);  // a kernel: capturable
+  if (rc) return rc;
+  const dim3 rows((unsigned)a.n_slices, (unsigned)r.n_heads, 2u);
+  const dim3 pick((unsigned)r.n_heads, 2u);
+  for (int l = 0; l < kLevels; ++l) {
+    hipLaunchKernelGGL(topk_hist, rows, dim3(kThreads), 0, s, a, l);
+    hipLaunchKernelGGL(topk_pick, pick, dim3(kThreads), 0, s, a, l);
+  }
+  hipLaunchKernelGGL(topk_count, rows, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(topk_compact, rows, dim3(kThreads), 0, s, a);
   return check_launch("topk");
 }
 

@@ -60,12 +60,15 @@ def test_dca_positions(chunk, local, start, n):
 
 
 # ---------------------------------------------------------------- selection
-@pytest.mark.parametrize("n,k", [(1000, 32), (4096, 1000), (50, 64), (100000, 6096), (37, 0)])
+@pytest.mark.parametrize("n,k", [(1000, 32), (4096, 1000), (50, 64), (100000, 6096), (37, 0),
+                                 (3 * 16384 + 5, 4000), (1 << 20, 6096), (70000, 70000)])
 def test_topk_select_only_bit_exact(n, k):
     rng = np.random.default_rng(n + k)
     H = 3
     v = rng.random((H, n)).astype(np.float32)
     v[:, ::7] = np.float32(0.5)                 # many exact ties
+    v[0, 1::11] = -v[0, 1::11]                  # negative scores
+    v[0, 2::13] = np.float32(-0.0)              # -0 ranks as +0
     v[1] = np.round(v[1] * 8) / 8               # coarse values: heavy ties
     s = rng.random((H, n)).astype(np.float32) ** 4
     s[2, :] = 0.0                               # all-equal head
