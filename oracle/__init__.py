@@ -29,7 +29,7 @@ the exact YaRN frequency ramp between beta_slow and beta_fast (the pages'
 snippet is garbled; only its end points and monotonicity are pinned).
 """
 
-from .rope import (bf16_round, rope_inv_freq, yarn_inv_freq, yarn_mscale,
+from .rope import (bf16_round, bf16_round64, rope_inv_freq, yarn_inv_freq, yarn_mscale,
                    softmax_scale, rope_rotate, rope_apply)
 from .dca import (dca_position_maps, dca_chunk_of, query_positions,
                   relative_positions)
@@ -39,7 +39,7 @@ from .estimate import estimate_scores, select_top, select_pattern
 from .refine import refine_budgets
 
 __all__ = [
-    "bf16_round", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",
+    "bf16_round", "bf16_round64", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",
     "softmax_scale", "rope_rotate", "rope_apply",
     "dca_position_maps", "dca_chunk_of", "query_positions",
     "relative_positions",

@@ -12,7 +12,7 @@ caller passes the KeyContext of that KV head.
 import numpy as np
 
 from .dca import dca_position_maps, query_positions
-from .rope import rope_rotate
+from .rope import bf16_round64, rope_rotate
 
 
 class KeyContext:
@@ -21,9 +21,21 @@ class KeyContext:
     K and V are [N, D].  Rotated keys are computed once per context and
     cached: at DCA key positions (attention) and at the plain token index
     (the continuous positions used for pattern selection).
+
+    operands="fp64" keeps rotated keys and queries exact.  operands="bf16"
+    takes the attention's precision statement, bf16 operands with fp32
+    accumulation, at its word: the rotated keys (the K cache, stored once at
+    the DCA key position: [Qwen2.5-1M explainer] 推論フレームワーク) and the
+    rotated queries enter the QK^T products as bfloat16, each rounded to the
+    nearest (ties to even) from its exact fp64 rotation.  Every other step
+    stays fp64.  Reading: in a bf16 model the RoPE output has the model's
+    dtype, and the interface fixes the cache as bf16.
     """
 
-    def __init__(self, K, V, inv_freq, dca_chunk=0, dca_local=0):
+    def __init__(self, K, V, inv_freq, dca_chunk=0, dca_local=0, operands="fp64"):
+        if operands not in ("fp64", "bf16"):
+            raise ValueError("operands must be 'fp64' or 'bf16'")
+        self.operands = operands
         self.K = np.asarray(K, dtype=np.float64)
         self.V = None if V is None else np.asarray(V, dtype=np.float64)
         self.inv_freq = np.asarray(inv_freq, dtype=np.float64)
@@ -32,23 +44,36 @@ class KeyContext:
         self._k_dca = None
         self._k_cont = None
 
+    def operand(self, x):
+        """A rotated vector as it enters a QK^T product."""
+        return bf16_round64(x) if self.operands == "bf16" else x
+
     @property
     def n_keys(self):
         return self.K.shape[0]
 
+    def _pk(self):
+        return dca_position_maps(np.arange(self.n_keys), self.dca_chunk,
+                                 self.dca_local)["pk"]
+
     def k_dca(self):
-        """Keys rotated at the DCA key position P_k(j)."""
+        """Keys rotated at the DCA key position P_k(j), as the cache holds them."""
         if self._k_dca is None:
-            pk = dca_position_maps(np.arange(self.n_keys), self.dca_chunk,
-                                   self.dca_local)["pk"]
-            self._k_dca = rope_rotate(self.K, pk, self.inv_freq)
+            k = rope_rotate(self.K, self._pk(), self.inv_freq)
+            self._k_dca = self.operand(k)
         return self._k_dca
 
     def k_cont(self):
-        """Keys rotated at their own index j (continuous positions)."""
+        """Keys rotated at their own index j (continuous positions).
+
+        From a bf16 cache, the cached key turns on by j - P_k(j), a multiple
+        of the key period: R(j) k = R(j - P_k(j)) R(P_k(j)) k."""
         if self._k_cont is None:
-            self._k_cont = rope_rotate(self.K, np.arange(self.n_keys),
-                                       self.inv_freq)
+            idx = np.arange(self.n_keys)
+            if self.operands == "bf16":
+                self._k_cont = rope_rotate(self.k_dca(), idx - self._pk(), self.inv_freq)
+            else:
+                self._k_cont = rope_rotate(self.K, idx, self.inv_freq)
         return self._k_cont
 
 
@@ -67,7 +92,7 @@ def attention_logits(q_row, i, ctx, js, sm_scale):
     keys = ctx.k_dca()
     for p in np.unique(pq):
         sel = pq == p
-        q_rot = rope_rotate(np.asarray(q_row, np.float64), p, ctx.inv_freq)
+        q_rot = ctx.operand(rope_rotate(np.asarray(q_row, np.float64), p, ctx.inv_freq))
         out[sel] = keys[js[sel]] @ q_rot
     return sm_scale * out
 

@@ -35,7 +35,7 @@ def estimate_scores(q_rows, rows, ctx, n_keys, sm_scale):
     """(v, s): vertical scores over keys [0, n_keys) and slash scores over
     offsets [0, n_keys) for one query head."""
     rows = np.asarray(rows, dtype=np.int64)
-    q_rot = rope_rotate(np.asarray(q_rows, np.float64), rows, ctx.inv_freq)
+    q_rot = ctx.operand(rope_rotate(np.asarray(q_rows, np.float64), rows, ctx.inv_freq))
     keys = ctx.k_cont()[:n_keys]
     logits = sm_scale * (q_rot @ keys.T)
     logits[rows[:, None] < np.arange(n_keys)[None, :]] = -np.inf

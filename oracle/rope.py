@@ -13,14 +13,27 @@ def bf16_round(x):
 
     The library stores rotated keys, rotated queries and probabilities in
     bfloat16 for the matrix cores and converts fp32 inputs to bf16 on entry;
-    the oracle applies this rounding only to *inputs* (the tiny fp32 config),
-    never to its own intermediates.
+    the oracle applies this rounding to *inputs* (the tiny fp32 config) and,
+    through bf16_round64, to the K cache, whose bf16 type the interface fixes;
+    never to its other intermediates.
     """
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     bits = a.view(np.uint32).astype(np.uint64)
     lsb = (bits >> 16) & 1
     rounded = ((bits + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
     return rounded.view(np.float32).reshape(a.shape)
+
+
+def bf16_round64(x):
+    """Round float64 values straight to the nearest bfloat16 (ties to even),
+    returned as float64, with no float32 step in between.
+
+    bfloat16 keeps 8 significant bits: with x = m 2^e and 1/2 <= |m| < 1,
+    the result is round_half_even(256 m) 2^(e - 8).  Used for the bf16 K
+    cache, which stores keys after their rotation.
+    """
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(m * 256.0), e - 8)
 
 
 def rope_inv_freq(head_dim, base):

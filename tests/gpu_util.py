@@ -66,10 +66,12 @@ def compare(gpu, ref, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
 
 
 def lse_compare(gpu, ref, tol=2e-2):
+    """lse within tol (a scalar or one bound per row)."""
     g = np.asarray(gpu, np.float64)
     r = np.asarray(ref, np.float64)
     both_inf = np.isneginf(g) & np.isneginf(r)
     with np.errstate(invalid="ignore"):
         d = np.abs(np.where(both_inf, 0.0, g - r))
-    assert d.max() <= tol, f"lse max diff {d.max():.3e}"
+    assert np.all(d <= tol), f"lse max diff {d.max():.3e} (worst excess {np.max(d - tol):.3e})"
     return d.max()
+

@@ -109,7 +109,8 @@ def test_estimate_scores_and_selection_tiny(c0, lc):
                           layer.sm_scale, [32], [64], layer.pattern, vert_score=vs,
                           slash_score=ss)
     qo, ko, _ = oracle_inputs(q, k, v)
-    ctx = oracle.KeyContext(ko[0, :c1], None, oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local)
+    ctx = oracle.KeyContext(ko[0, :c1], None, oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local,
+                            operands="bf16")
     rows = oracle.estimate.estimate_rows(c0, lc, 64)
     rv, rs = oracle.estimate_scores(qo[0, rows], rows, ctx, c1, layer.sm_scale)
     gv, gs = host64(vs[0]), host64(ss[0])
@@ -162,7 +163,7 @@ def _attn_case(cfg, c0, lc, verts, slashes, dense=False, out_dtype=torch.float32
     sizes_total = 0
     for h in range(H):
         ctx = oracle.KeyContext(ko[h // G, :c1], vo[h // G, :c1], th, cfg.dca_chunk,
-                                cfg.dca_local)
+                                cfg.dca_local, operands="bf16")
         rows = np.arange(c0, c1)
         if dense:
             ro, rl = oracle.dense_causal_rows(qo[h, c0:c1], rows, ctx, layer.sm_scale)
@@ -190,7 +191,8 @@ def test_attention_tiny_oracle_pattern():
     cfg = TINY
     q, k, v = synth.generate(cfg)
     qo, ko, _ = oracle_inputs(q, k, v)
-    ctx = oracle.KeyContext(ko[0], None, oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local)
+    ctx = oracle.KeyContext(ko[0], None, oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local,
+                            operands="bf16")
     rows = oracle.estimate.estimate_rows(0, 1024, 64)
     rv, rs = oracle.estimate_scores(qo[0, rows], rows, ctx, 1024, oracle.softmax_scale(64, 1.0))
     vsel, ssel = oracle.select_pattern(rv, rs, 32, 64)
@@ -239,7 +241,8 @@ def test_recall_tiny():
     lf, ls, rc = layer.recall(q, 0, rows)
     verts, slashes = layer.pattern.lists()
     qo, ko, vo = oracle_inputs(q, k, v)
-    ctx = oracle.KeyContext(ko[0], vo[0], oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local)
+    ctx = oracle.KeyContext(ko[0], vo[0], oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local,
+                            operands="bf16")
     r = rows.cpu().numpy().astype(np.int64)
     of, os_, orc = oracle.attention_recall(qo[0, r], r, ctx, verts[0].numpy(), slashes[0].numpy(),
                                            layer.sm_scale)

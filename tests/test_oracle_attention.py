@@ -171,3 +171,42 @@ def test_recall_properties():
         cs = oracle.critical_set(i, v1, s1)
         assert r1[a] == pytest.approx(p[cs].sum(), rel=1e-12)
     assert np.all(full >= sp)
+
+
+@pytest.mark.parametrize("chunk,local", [(0, 0), (12, 4)])
+def test_bf16_operands(chunk, local):
+    """operands="bf16": the cached keys are the bf16 roundings of the exact
+    rotated keys (representable, within half an ulp); continuous-position
+    keys rotate back to the pre-RoPE keys within that rounding; with the
+    rotation switched off and bf16 inputs the rounding is a no-op, so both
+    modes agree exactly (nothing else is rounded); with it on they differ by
+    no more than the operand rounding allows."""
+    rng = np.random.default_rng(21)
+    n, d = 40, 8
+    K = oracle.bf16_round(rng.normal(size=(n, d))).astype(np.float64)
+    V = rng.normal(size=(n, d))
+    Q = oracle.bf16_round(rng.normal(size=(n, d))).astype(np.float64)
+    th = oracle.rope_inv_freq(d, 100.0)
+    exact = oracle.KeyContext(K, V, th, chunk, local)
+    bf = oracle.KeyContext(K, V, th, chunk, local, operands="bf16")
+    kd, ke = bf.k_dca(), exact.k_dca()
+    assert np.array_equal(oracle.bf16_round64(kd), kd)
+    assert np.all(np.abs(kd - ke) <= np.ldexp(1.0, np.frexp(ke)[1] - 9))
+    back = oracle.rope_rotate(bf.k_cont(), -np.arange(n), th)
+    assert np.max(np.abs(back - K)) <= 2.0 ** -8 * np.max(np.abs(K)) * 2
+    if chunk == 0:
+        assert np.array_equal(bf.k_cont(), kd)
+    rows = np.arange(n)
+    oe, le = oracle.dense_causal_rows(Q, rows, exact, 0.4)
+    ob, lb = oracle.dense_causal_rows(Q, rows, bf, 0.4)
+    # logits move by at most 2 * 2^-8 * sm |q| |k| (both operands rounded)
+    bound = 2 * 2.0 ** -8 * 0.4 * np.linalg.norm(Q, axis=1) * np.max(np.linalg.norm(K, axis=1))
+    assert np.max(np.abs(oe - ob)) > 0 and np.all(np.abs(le - lb) <= bound)
+    zero = np.zeros(d // 2)
+    a = oracle.KeyContext(K, V, zero, chunk, local)
+    b = oracle.KeyContext(K, V, zero, chunk, local, operands="bf16")
+    oa, la = oracle.sparse_rows(Q, rows, a, [0, 3], [0, 1, 5], 0.4)[:2]
+    ob2, lb2 = oracle.sparse_rows(Q, rows, b, [0, 3], [0, 1, 5], 0.4)[:2]
+    assert np.array_equal(oa, ob2) and np.array_equal(la, lb2)
+    with pytest.raises(ValueError):
+        oracle.KeyContext(K, V, th, operands="fp16")

@@ -122,3 +122,25 @@ def test_bf16_round_ties_and_library():
     x = (rng.normal(size=10000) * 10.0 ** rng.integers(-5, 5, 10000)).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(oracle.bf16_round(x), ref)
+
+
+def test_bf16_round64_ties_and_library():
+    """Direct fp64 -> bf16 rounding: the same ties as the fp32 path, the same
+    result as torch on float32-representable values, and no double rounding
+    on values that lie just off a tie in fp64."""
+    got = oracle.bf16_round64(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0]))
+    assert got.tolist() == [1.0, 1 + 2 ** -6, -1.0, 0.0]
+    rng = np.random.default_rng(5)
+    x = (rng.normal(size=10000) * 10.0 ** rng.integers(-5, 5, 10000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    np.testing.assert_array_equal(oracle.bf16_round64(x.astype(np.float64)), ref)
+    # just above a tie in fp64, but a tie once squeezed through fp32 first
+    y = 1 + 2 ** -8 + 2 ** -40
+    assert oracle.bf16_round64(np.array([y]))[0] == 1 + 2 ** -7
+    assert oracle.bf16_round(np.array([y], dtype=np.float32))[0] == 1.0
+    # every result has at most 8 significant bits and lies within half an ulp
+    z = rng.normal(size=5000) * 3.0
+    r = oracle.bf16_round64(z)
+    m, e = np.frexp(r)
+    assert np.all(m * 256 == np.round(m * 256))
+    assert np.all(np.abs(r - z) <= np.ldexp(1.0, np.frexp(z)[1] - 9))
