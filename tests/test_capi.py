@@ -1,0 +1,173 @@
+"""The C ABI on a host without a GPU: the library loads, exports every
+function include/lcsr.h declares, sizes workspaces, and rejects invalid
+arguments with the documented status before it launches anything (every
+call below fails validation, so no pointer is ever dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_rope_amd import _capi as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # 16-byte aligned stand-in for a device pointer (never read)
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "lcsr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(lcsr_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return C.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    assert set(names) == set(C.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def problem(**kw):
+    p = C.lcsr_problem_t()
+    p.q, p.k_cache, p.v_cache = FAKE, FAKE, FAKE
+    p.q_dtype = C.LCSR_BF16
+    p.n_heads, p.n_kv_heads, p.head_dim = 28, 4, 128
+    p.q_stride_h, p.q_stride_t = 32768 * 128, 128
+    p.kv_stride_h, p.kv_stride_t = 1 << 27, 128
+    p.chunk_start, p.chunk_len = 32768, 32768
+    p.rope.base, p.rope.yarn_factor, p.rope.orig_max_pos = 1e7, 1.0, 262144
+    p.rope.beta_fast, p.rope.beta_slow = 32.0, 1.0
+    p.sm_scale = 0.0884
+    for k, v in kw.items():
+        if k.startswith("dca_"):
+            setattr(p.dca, k[4:], v)
+        else:
+            setattr(p, k, v)
+    return p
+
+
+def pattern(max_vert=1000, max_slash=6096):
+    t = C.lcsr_pattern_t()
+    t.vert_idx = t.vert_cnt = t.slash_idx = t.slash_cnt = FAKE
+    t.max_vert, t.max_slash = max_vert, max_slash
+    return t
+
+
+def err(lib):
+    return lib.lcsr_last_error().decode()
+
+
+def test_workspace_bytes(lib):
+    p = problem()
+    for which in (C.LCSR_WS_ESTIMATE, C.LCSR_WS_ATTN, C.LCSR_WS_RECALL):
+        assert lib.lcsr_workspace_bytes(which, ctypes.byref(p), 1000, 6096) > 0
+    # the estimate's workspace grows with the context
+    big = problem(chunk_start=1015808)
+    assert (lib.lcsr_workspace_bytes(C.LCSR_WS_ESTIMATE, ctypes.byref(big), 1000, 6096) >
+            lib.lcsr_workspace_bytes(C.LCSR_WS_ESTIMATE, ctypes.byref(p), 1000, 6096))
+    bad = problem(n_kv_heads=3)
+    assert lib.lcsr_workspace_bytes(C.LCSR_WS_ATTN, ctypes.byref(bad), 1000, 6096) == 0
+    assert "n_kv_heads" in err(lib)
+    assert lib.lcsr_workspace_bytes(7, ctypes.byref(p), 1, 1) == 0
+
+
+def attn(lib, p, pat=None, out=FAKE, out_dtype=C.LCSR_FP32, ws=FAKE, ws_bytes=1 << 40,
+         flags=0, o_sh=32768 * 128, o_st=128):
+    return lib.lcsr_vs_sparse_attn_prefill(
+        ctypes.byref(p), None if pat is None else ctypes.byref(pat), None, out, out_dtype,
+        o_sh, o_st, None, None, flags, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,code,text", [
+    ("q", None, C.LCSR_EINVAL, "NULL"),
+    ("q", FAKE + 4, C.LCSR_EINVAL, "aligned"),
+    ("n_kv_heads", 3, C.LCSR_EINVAL, "multiple"),
+    ("head_dim", 96, C.LCSR_ENOTSUP, "head_dim"),
+    ("n_heads", 128, C.LCSR_ENOTSUP, "n_heads"),
+    ("q_stride_t", 100, C.LCSR_EINVAL, "strides"),
+    ("chunk_len", -1, C.LCSR_EINVAL, ">= 0"),
+    ("sm_scale", 0.0, C.LCSR_EINVAL, "sm_scale"),
+    ("dca_chunk", 262144, C.LCSR_EINVAL, "local"),   # with local = chunk (below)
+])
+def test_attention_rejects(lib, field, value, code, text):
+    kw = {field: value}
+    if field == "dca_chunk":
+        kw["dca_local"] = 262144          # local must be < chunk
+    p = problem(**kw)
+    assert attn(lib, p, pattern()) == code
+    assert text in err(lib)
+
+
+def test_attention_rejects_other_arguments(lib):
+    p = problem()
+    assert attn(lib, p, None) == C.LCSR_EINVAL                      # no pattern, not dense
+    assert attn(lib, p, pattern(), out=None) == C.LCSR_EINVAL
+    assert attn(lib, p, pattern(), out_dtype=7) == C.LCSR_EINVAL
+    assert attn(lib, p, pattern(), o_st=64) == C.LCSR_EINVAL
+    need = lib.lcsr_workspace_bytes(C.LCSR_WS_ATTN, ctypes.byref(p), 1000, 6096)
+    assert attn(lib, p, pattern(), ws_bytes=need - 1) == C.LCSR_EWORKSPACE
+    assert str(need) in err(lib)
+    assert attn(lib, p, pattern(), ws=None) == C.LCSR_EWORKSPACE
+    # DCA period and chunk start must be tile multiples
+    q = problem(dca_chunk=262144, dca_local=32760)
+    assert attn(lib, q, pattern()) == C.LCSR_ENOTSUP
+    # the context cap (the row block's key bitmap lives in LDS)
+    huge = problem(chunk_start=(1 << 30) - 32768)
+    assert attn(lib, huge, pattern()) == C.LCSR_ENOTSUP
+    assert "contexts up to" in err(lib)
+
+
+def test_estimate_and_recall_reject(lib):
+    p = problem()
+    nv = (ctypes.c_int32 * 28)(*([1000] * 28))
+    ns = (ctypes.c_int32 * 28)(*([6096] * 28))
+    pat = pattern()
+
+    def est(last_q=64, n_vert=nv, flags=0, vs=None, ws=FAKE, ws_bytes=1 << 40):
+        return lib.lcsr_vs_pattern_estimate(ctypes.byref(p), last_q, n_vert, ns, None,
+                                            ctypes.byref(pat), vs, None, flags, ws, ws_bytes,
+                                            None)
+
+    assert est(last_q=0) == C.LCSR_EINVAL
+    assert est(last_q=65) == C.LCSR_EINVAL
+    over = (ctypes.c_int32 * 28)(*([1001] + [1000] * 27))
+    assert est(n_vert=over) == C.LCSR_EINVAL and "budget" in err(lib)
+    assert est(flags=C.LCSR_EST_SELECT_ONLY) == C.LCSR_EINVAL
+    assert est(ws_bytes=16) == C.LCSR_EWORKSPACE
+    rows = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.lcsr_attn_recall_check(ctypes.byref(p), ctypes.byref(pat), None, rows, -1,
+                                      FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == C.LCSR_EINVAL
+    assert lib.lcsr_attn_recall_check(ctypes.byref(p), ctypes.byref(pat), None, None, 2,
+                                      FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == C.LCSR_EINVAL
+
+
+def test_rope_and_dca_reject(lib):
+    rope = C.lcsr_rope_t(1e4, 1.0, 262144, 32.0, 1.0, 0)
+    call = lib.lcsr_rope_yarn_apply
+    ok = dict(x=FAKE, x_dtype=C.LCSR_BF16, xsh=1024 * 64, xst=64, y=2 * FAKE, ysh=1024 * 64,
+              yst=64, nh=1, nt=1024, hd=64, pos=FAKE)
+
+    def r(**kw):
+        a = dict(ok, **kw)
+        return call(a["x"], a["x_dtype"], a["xsh"], a["xst"], a["y"], a["ysh"], a["yst"], a["nh"],
+                    a["nt"], a["hd"], a["pos"], ctypes.byref(rope), 1.0, 0, None)
+
+    assert r(x=None) == C.LCSR_EINVAL
+    assert r(pos=None) == C.LCSR_EINVAL
+    assert r(hd=63) == C.LCSR_EINVAL
+    assert r(hd=512) == C.LCSR_EINVAL
+    assert r(x_dtype=5) == C.LCSR_EINVAL
+    assert r(nt=-1) == C.LCSR_EINVAL
+    dca = C.lcsr_dca_t(256, 256)
+    assert lib.lcsr_dca_positions(0, 16, ctypes.byref(dca), FAKE, None, None, None,
+                                  None) == C.LCSR_EINVAL
+    dca = C.lcsr_dca_t(256, 64)
+    assert lib.lcsr_dca_positions(0, -1, ctypes.byref(dca), FAKE, None, None, None,
+                                  None) == C.LCSR_EINVAL
