@@ -12,9 +12,10 @@ build runs on one GPU.
 """
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -31,6 +32,32 @@ from synth.configs import CONFIGS  # noqa: E402
 METRIC = ("ms + effective TFLOP/s per 1M-token sparse prefill (one layer); "
           "% bf16 MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+CSRC = os.path.join(ROOT, "long_context_sparse_rope_amd", "csrc")
+# sources of the kernels one vs_sparse_attn_prefill call launches
+ATTN_SOURCES = ("attn.hip", "rope.hip", "lcsr_internal.h")
+
+
+def attn_source_digest():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(workload):
+    """HBM bytes per attention call from the committed rocprofv3 counter
+    summary, or None when it was taken on other sources or another workload
+    (the counters cannot be read live)."""
+    path = os.path.join(ROOT, "profiles", f"vs_sparse_attn_prefill_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    dig = re.search(r"attention source digest: `([0-9a-f]+)`", text)
+    val = re.search(r"HBM bytes per call \(scaled\): ([0-9.eE+]+)", text)
+    if not dig or not val or dig.group(1) != attn_source_digest():
+        return None
+    return float(val.group(1))
 
 
 def make_layer(cfg, dev):
@@ -84,7 +111,9 @@ def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
     attention rows of the last chunk (first query head, the GPU's own
     pattern), as many as fit in about `budget_s` seconds."""
     import oracle
-    threads = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max(blas) if blas else 1
     c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
     c1 = c0 + lc
     h, g = 0, 0
@@ -98,7 +127,7 @@ def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
     ctx.k_dca()
     setup_s = time.perf_counter() - t_setup
     rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(np.arange(c0, c1), size=4096, replace=False))
+    rows = np.sort(rng.choice(np.arange(c0, c1), size=16384, replace=False))
     qh = q[h, rows].float().cpu().numpy().astype(np.float64)
     sm = layer.sm_scale
     done, pairs = 0, 0
@@ -111,6 +140,7 @@ def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
     el = time.perf_counter() - t0
     flops = 4.0 * cfg.head_dim * pairs
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
             "sample": (f"fp64 sparse attention of {done} sampled rows of the last 32K chunk "
                        f"(query head 0, GPU pattern), {el:.1f} s after {setup_s:.1f} s of "
                        f"key rotation; {pairs} critical pairs"),
@@ -168,7 +198,8 @@ def main():
     eff = alg_flops / (ms_step * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "vs_sparse_attn_prefill (pattern aux + attention)",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": counted_traffic(cfg.name), "traffic_unit": "bytes per call",
                 "executed_tflops": round(exec_rate, 2),
                 "executed_frac": round(exec_rate / PEAK_BF16_TFLOPS, 4),
                 "avg_call_ms": round(attn_ms_call, 4)}
@@ -187,6 +218,7 @@ def main():
         "executed_tflop_per_step": round(exe_flops / 1e12, 3),
         "waste_ratio": round(exe_pairs / max(sel_pairs, 1), 3),
         "roofline": roofline,
+        "attn_source_digest": attn_source_digest(),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)

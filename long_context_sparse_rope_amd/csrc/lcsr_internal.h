@@ -95,7 +95,8 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, double inv_freq,
 // Position of token t (0-based within the call):
 //   kPosArray:   pos[t]
 //   kPosAffine:  t + pos_offset
-//   kPosDca:     dca_query_pos(t + pos_offset, variant)
+//   kPosDca:     dca_query_pos(t + pos_offset, v) for the n_var variants
+//                v = 0 .. n_var - 1, written at dst + v * dst_vs
 //   kNoRotate:   no rotation (conversion and scale only)
 enum PosMode : int32_t { kPosArray = 0, kPosAffine = 1, kPosDca = 2, kNoRotate = 3 };
 struct RotateArgs {
@@ -103,12 +104,12 @@ struct RotateArgs {
   int32_t src_dtype;
   int64_t src_sh, src_st;
   uint16_t* dst;
-  int64_t dst_sh, dst_st;
+  int64_t dst_vs, dst_sh, dst_st;
   int64_t n_heads, n_tok, head_dim;
   const int32_t* pos;
   int64_t pos_offset;
   int32_t mode;
-  int32_t variant;
+  int32_t n_var;
   DcaParams dca;
   float scale;
 };

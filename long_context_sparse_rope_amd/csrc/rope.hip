@@ -56,30 +56,40 @@ __device__ __forceinline__ float load_elem(const void* base, int32_t dtype, int6
   return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
 }
 
-// One thread per (token, pair); the angle is shared by every head.
+// One thread per (token, pair); the angle is shared by every head.  In
+// kPosDca mode the thread writes the n_var DCA query variants of its pair
+// (intra, successive, inter) from one read of the input.  kTag only names
+// the launch site in profiles: 0 the RoPE call, 1 the attention's query
+// variants, 2 the estimate rows.
+template <int kTag>
 __global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft) {
   const int64_t half = a.head_dim / 2;
   const int64_t tok_per_block = 256 / half;
   const int64_t t = (int64_t)blockIdx.x * tok_per_block + threadIdx.x / half;
   const int64_t p = threadIdx.x % half;
   if (threadIdx.x >= tok_per_block * half || t >= a.n_tok) return;
-  float c = 1.0f, s = 0.0f;
+  const int nv = a.mode == kPosDca ? a.n_var : 1;
+  float c[3] = {1.0f, 1.0f, 1.0f}, s[3] = {0.0f, 0.0f, 0.0f};
   if (a.mode != kNoRotate) {
-    int64_t pos;
-    if (a.mode == kPosArray) pos = a.pos[t];
-    else if (a.mode == kPosAffine) pos = t + a.pos_offset;
-    else pos = dca_query_pos(t + a.pos_offset, a.variant, a.dca);
-    rope_cos_sin(pos, ft.inv_freq[p], &c, &s);
+    for (int v = 0; v < nv; ++v) {
+      int64_t pos;
+      if (a.mode == kPosArray) pos = a.pos[t];
+      else if (a.mode == kPosAffine) pos = t + a.pos_offset;
+      else pos = dca_query_pos(t + a.pos_offset, v, a.dca);
+      rope_cos_sin(pos, ft.inv_freq[p], &c[v], &s[v]);
+    }
   }
   for (int64_t h = 0; h < a.n_heads; ++h) {
     const int64_t so = h * a.src_sh + t * a.src_st;
     const float x1 = load_elem(a.src, a.src_dtype, so + p);
     const float x2 = load_elem(a.src, a.src_dtype, so + p + half);
-    const float y1 = (x1 * c - x2 * s) * a.scale;
-    const float y2 = (x2 * c + x1 * s) * a.scale;
-    uint16_t* d = a.dst + h * a.dst_sh + t * a.dst_st;
-    d[p] = f32_to_bf16(y1);
-    d[p + half] = f32_to_bf16(y2);
+    for (int v = 0; v < nv; ++v) {
+      const float y1 = (x1 * c[v] - x2 * s[v]) * a.scale;
+      const float y2 = (x2 * c[v] + x1 * s[v]) * a.scale;
+      uint16_t* d = a.dst + v * a.dst_vs + h * a.dst_sh + t * a.dst_st;
+      d[p] = f32_to_bf16(y1);
+      d[p + half] = f32_to_bf16(y2);
+    }
   }
 }
 
@@ -110,13 +120,22 @@ int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
   return check_launch("fill_zero");
 }
 
-int launch_rotate(const RotateArgs& a, const FreqTable& ft, hipStream_t s) {
+namespace {
+template <int kTag>
+int launch_rotate_tagged(const RotateArgs& a, const FreqTable& ft, hipStream_t s) {
   if (a.n_tok == 0 || a.n_heads == 0) return LCSR_OK;
+  if (a.mode == kPosDca && (a.n_var < 1 || a.n_var > 3))
+    return fail(LCSR_EINVAL, "rotate: 1 to 3 DCA query variants");
   const int64_t half = a.head_dim / 2;
   const int64_t tok_per_block = 256 / half;
   const int64_t blocks = (a.n_tok + tok_per_block - 1) / tok_per_block;
-  hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
+  hipLaunchKernelGGL(rotate_kernel<kTag>, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
   return check_launch("rotate");
+}
+}  // namespace
+
+int launch_rotate(const RotateArgs& a, const FreqTable& ft, hipStream_t s) {
+  return launch_rotate_tagged<0>(a, ft, s);
 }
 
 int launch_dca_positions(int64_t tok_start, int64_t n_tok, const DcaParams& d,
@@ -133,27 +152,24 @@ int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
                              const DcaParams& d, uint16_t* dst, int n_var,
                              hipStream_t s) {
   const int64_t D = p.head_dim, L = p.chunk_len, H = p.n_heads;
-  for (int v = 0; v < n_var; ++v) {
-    RotateArgs a{};
-    a.src = p.q;
-    a.src_dtype = p.q_dtype;
-    a.src_sh = p.q_stride_h;
-    a.src_st = p.q_stride_t;
-    a.dst = dst + (int64_t)v * H * L * D;
-    a.dst_sh = L * D;
-    a.dst_st = D;
-    a.n_heads = H;
-    a.n_tok = L;
-    a.head_dim = D;
-    a.pos_offset = p.chunk_start;
-    a.mode = kPosDca;
-    a.variant = v;
-    a.dca = d;
-    a.scale = 1.0f;
-    int rc = launch_rotate(a, ft, s);
-    if (rc) return rc;
-  }
-  return LCSR_OK;
+  RotateArgs a{};
+  a.src = p.q;
+  a.src_dtype = p.q_dtype;
+  a.src_sh = p.q_stride_h;
+  a.src_st = p.q_stride_t;
+  a.dst = dst;
+  a.dst_vs = H * L * D;
+  a.dst_sh = L * D;
+  a.dst_st = D;
+  a.n_heads = H;
+  a.n_tok = L;
+  a.head_dim = D;
+  a.pos_offset = p.chunk_start;
+  a.mode = kPosDca;
+  a.n_var = n_var;
+  a.dca = d;
+  a.scale = 1.0f;
+  return launch_rotate_tagged<1>(a, ft, s);
 }
 
 int launch_rotate_q_estimate(const lcsr_problem_t& p, const FreqTable& ft,
@@ -178,7 +194,7 @@ int launch_rotate_q_estimate(const lcsr_problem_t& p, const FreqTable& ft,
     a.pos_offset = row0 - (int64_t)c * d.period;
     a.mode = kPosAffine;
     a.scale = 1.0f;
-    int rc = launch_rotate(a, ft, s);
+    int rc = launch_rotate_tagged<2>(a, ft, s);
     if (rc) return rc;
   }
   return LCSR_OK;
