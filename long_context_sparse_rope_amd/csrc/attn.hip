@@ -341,26 +341,24 @@ __device__ __forceinline__ void dma4_v(const void* addr, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(addr), "{m0}"(lds) : "memory");
 }
 
-// Loads of one tile issued by one wave: P per wave (the last waves repeat one
-// of their loads, so every wave issues the same count and can wait for its
-// own loads with a fixed vmcnt).
-template <int D, int NW>
+// Every direct-to-LDS load of one tile, issued by the walker wave into the
+// stage at LDS address `dst`: load i fills rows (i mod M) * R .. + R - 1 of K
+// (i < M) or V (M = loads per matrix, R rows per load); padding rows past
+// t.n repeat the last key.  For gathered tiles the keys of each load's rows
+// come from scalar loads, and one more load copies the tile's keys into the
+// stage (for the masks); span tiles issue the same count (the extra load
+// copies 256 bytes of the first K row there), so the walker can wait for a
+// tile with a fixed vmcnt.
+template <int D>
 struct Issue {
-  static constexpr int P = (Buf<D>::kInstr + NW - 1) / NW;
+  static constexpr int kPerTile = Buf<D>::kInstr + 1;
 };
 
-// This wave's share of the direct-to-LDS loads of one tile into the stage at
-// LDS address `dst`.  Load i of the tile fills rows (i mod M) * R .. + R - 1
-// of K (i < M) or V (M = loads per matrix, R rows per load); padding rows
-// past t.n repeat the last key.  For gathered tiles the keys of each load's
-// rows come from scalar loads, and wave 0 also copies the tile's keys into
-// the stage (for the masks).
-template <int D, int NW>
-__device__ __forceinline__ void issue_share(const char* kg, const char* vg, uint32_t kvst_b,
-                                            const Tile& t, const int32_t* vl, uint32_t dst,
-                                            int w, int lane) {
+template <int D>
+__device__ __forceinline__ void issue_tile(const char* kg, const char* vg, uint32_t kvst_b,
+                                           const Tile& t, const int32_t* vl, uint32_t dst,
+                                           int lane) {
   using B = Buf<D>;
-  constexpr int P = Issue<D, NW>::P;
   constexpr int M = B::kInstrPerMat, R = B::kRowsPerInstr;
   const int sub = lane / B::kChunks;  // row within a load
   const int cl = lane % B::kChunks;   // LDS slot of this lane's 16 bytes
@@ -368,9 +366,7 @@ __device__ __forceinline__ void issue_share(const char* kg, const char* vg, uint
     const char* kb = kg + (int64_t)t.ks * kvst_b;
     const char* vb = vg + (int64_t)t.ks * kvst_b;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      int gi = p * NW + w;
-      if (gi >= B::kInstr) gi = w;
+    for (int gi = 0; gi < B::kInstr; ++gi) {
       const bool isv = gi >= M;
       const int gm = isv ? gi - M : gi;
       const int row = gm * R + sub;
@@ -379,11 +375,10 @@ __device__ __forceinline__ void issue_share(const char* kg, const char* vg, uint
       dma16_s(isv ? vb : kb, rr * kvst_b + (uint32_t)chunk * 16u,
               dst + (isv ? B::kKBytes : 0) + gm * 1024);
     }
+    dma4_v(kb + (lane & (D / 2 - 1)) * 4, dst + B::kKeyOff);
   } else {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      int gi = p * NW + w;
-      if (gi >= B::kInstr) gi = w;
+    for (int gi = 0; gi < B::kInstr; ++gi) {
       const bool isv = gi >= M;
       const int gm = isv ? gi - M : gi;
       // keys of the R rows of this load (uniform), then this lane's one
@@ -399,7 +394,7 @@ __device__ __forceinline__ void issue_share(const char* kg, const char* vg, uint
       dma16_v((isv ? vg : kg) + (int64_t)key * kvst_b + chunk * 16,
               dst + (isv ? B::kKBytes : 0) + gm * 1024);
     }
-    if (w == 0) dma4_v(vl + t.ks + (lane < t.n ? lane : t.n - 1), dst + B::kKeyOff);
+    dma4_v(vl + t.ks + (lane < t.n ? lane : t.n - 1), dst + B::kKeyOff);
   }
 }
 
@@ -436,62 +431,57 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // One (wave, key tile) step on the stage `smem`.  With `masked`, mword is the
-// 64-bit key mask of this lane's row.  A wave with nothing in the tile
-// (act false) skips the QK product and the softmax but still runs the PV
-// product with zero weights: the O accumulators then go through the same
-// instructions on every path, and the compiler keeps them in place (a branch
-// around the PV product makes it copy them between register sets).
-// `after_qk` runs once the QK products are issued (scalar loads issued there
-// land during the softmax).
+// 64-bit key mask of this lane's row.  act0 / act1: the wave has pairs in key
+// half 0 / 1 of the tile; an empty half skips its QK product and its
+// softmax, and enters the PV product with zero weights (the O accumulators
+// then go through the same instructions on every path, and the compiler
+// keeps them in place: a branch around the PV product makes it copy them
+// between register sets).  `after_qk` runs once the QK products are issued
+// (scalar loads issued there land during the softmax).
 template <int D, typename F>
 __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
-                                          const LaneConst<D>& c, WaveState<D>& st, bool act,
-                                          bool masked, uint64_t mword, int half, F&& after_qk) {
+                                          const LaneConst<D>& c, WaveState<D>& st, bool act0,
+                                          bool act1, bool masked, uint64_t mword, int half,
+                                          F&& after_qk) {
   constexpr int RB = Buf<D>::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-row blocks of O^T
+  const bool act[2] = {act0, act1};
   f32x16 acc[2];
   float mx = -INFINITY;
-  if (act) {
-    // the K fragments of each 32-key half are requested together, so the LDS
-    // latency is paid once per half, not once per MFMA
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 kf[KS];
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!act[kb]) continue;
+    bf16x8 kf[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kf[s] = *reinterpret_cast<const bf16x8*>(smem + c.k_rd[s] + kb * 32 * RB);
-      acc[kb] = (f32x16){};
+    for (int s = 0; s < KS; ++s)
+      kf[s] = *reinterpret_cast<const bf16x8*>(smem + c.k_rd[s] + kb * 32 * RB);
+    // keep the reads ahead of the products (else the scheduler waits for each
+    // read next to its MFMA)
+    __builtin_amdgcn_sched_barrier(0);
+    acc[kb] = (f32x16){};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], st.q[s], acc[kb], 0, 0, 0);
-    }
-    after_qk();
+    for (int s = 0; s < KS; ++s)
+      acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], st.q[s], acc[kb], 0, 0, 0);
     // key k of the tile sits in register r of block kb: k = 32 kb + 8 (r / 4)
     // + 4 half + r % 4
     if (__builtin_expect(masked, 0)) {
-      const uint64_t mh = mword >> (4 * half);
+      const uint32_t word = (uint32_t)((mword >> (4 * half)) >> (32 * kb));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t word = (uint32_t)(mh >> (32 * kb));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // all ones where the key is kept, zero where it is masked
-          const uint32_t keep =
-              (uint32_t)__builtin_amdgcn_sbfe((int)word, 8 * (r >> 2) + (r & 3), 1);
-          acc[kb][r] = __uint_as_float((__float_as_uint(acc[kb][r]) & keep) |
-                                       (0xFF800000u & ~keep));
-        }
+      for (int r = 0; r < 16; ++r) {
+        // all ones where the key is kept, zero where it is masked
+        const uint32_t keep =
+            (uint32_t)__builtin_amdgcn_sbfe((int)word, 8 * (r >> 2) + (r & 3), 1);
+        acc[kb][r] =
+            __uint_as_float((__float_as_uint(acc[kb][r]) & keep) | (0xFF800000u & ~keep));
       }
     }
     // row max of the raw scores (the scale is positive)
-    mx = fmaxf(acc[0][0], acc[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, acc[0][r]), acc[1][r]);
-    mx = max_halves(mx) * a.scale_log2;
-  } else {
-    after_qk();
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[kb][r]), acc[kb][r + 1]);
   }
+  after_qk();
+  if (act0 || act1) mx = max_halves(mx) * a.scale_log2;
   if (__builtin_expect(__ballot(mx > st.m + kRescaleSlack) != 0ull, 0)) {
     const float m_new = fmaxf(st.m, mx);
     const float alpha = (st.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
@@ -503,30 +493,28 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
     st.m = m_new;
   }
   bf16x8 pf[4];
-  if (act) {
-    const float msub = (st.m == -INFINITY) ? 0.f : st.m;
+  const float msub = (st.m == -INFINITY) ? 0.f : st.m;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float psum = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < 4; ++s) {
+    if (act[s >> 1]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         pf[s][e] = (__bf16)__builtin_amdgcn_exp2f(
             fmaf(acc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msub));
-    // row sum of the bf16 weights the PV product uses
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float psum = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
+      // row sum of the bf16 weights the PV product uses
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const bf16x2 pr = {pf[s][e], pf[s][e + 1]};
         psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
       }
-    st.l += psum;
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) pf[s] = (bf16x8){};
+    } else {
+      pf[s] = (bf16x8){};
+    }
   }
+  st.l += psum;
   // O^T += V^T P^T; each lane receives V[16 s + 4 half + r][d0 + j] (r = 0..3
   // for the first transpose load, +8 for the second), the k-order of its P
   // fragment
@@ -539,14 +527,20 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
     __builtin_memcpy(&vf, vv, 16);
     return vf;
   };
+  // V fragments of k-step s + 1 are read while the products of s run
+  bf16x8 vf[2][DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) vf[0][db] = load_v(0, db);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    bf16x8 vf[DB];
+    if (s < 3) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vf[db] = load_v(s, db);
+      for (int db = 0; db < DB; ++db) vf[(s + 1) & 1][db] = load_v(s + 1, db);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[s], st.o[db], 0, 0, 0);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s & 1][db], pf[s], st.o[db], 0, 0, 0);
   }
 }
 
@@ -642,7 +636,7 @@ __device__ __forceinline__ Tile read_desc(const int4* slot) {
 template <int D, int NW>
 __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
   using B = Buf<D>;
-  constexpr int P = Issue<D, NW>::P;  // loads per tile per computing wave
+  constexpr int kPerTile = Issue<D>::kPerTile;  // walker loads per tile
   __shared__ __attribute__((aligned(16))) char stage[kStages][B::kBytes];
   __shared__ int4 ring[kRing];
   __shared__ unsigned long long sstat[2];
@@ -702,11 +696,41 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
       if (!e && n_tiles < 0) n_tiles = j;
       if (lane == 0) ring[j & (kRing - 1)] = e ? pack_desc(t) : make_int4(0, 0, 0, 0);
     };
+    // K / V of every tile: tile i + 2 is loaded while tile i is multiplied
+    // (its stage last held tile i - 2); at most two tiles are in flight, so
+    // the vmcnt counter covers them
+    const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
+    const char* vg = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
+    const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+    const uint32_t stage0 = lds_addr(&stage[0][0]);
+    auto issue = [&](const Tile& tt, int j) {
+      if (tt.n > 0) {
+        const int32_t* vl =
+            a.vl + ((int64_t)(h_first + (tt.wave < 0 ? 0 : tt.wave)) * a.n_rb + rb) * a.max_vert;
+        issue_tile<D>(kg, vg, kvst_b, tt, vl,
+                      stage0 + (uint32_t)((j & (kStages - 1)) * B::kBytes), lane);
+      }
+    };
+    // wait until only the loads of tile `ahead` may still be in flight
+    auto land = [&](const Tile& ahead) {
+      if (ahead.n > 0) wait_vm<kPerTile>();
+      else wait_vm<0>();
+    };
     for (int j = 0; j < 4; ++j) publish(j);
-    ring_barrier();  // descriptors 0 .. 3 published
+    {
+      const Tile ta = read_desc(&ring[0]), tb = read_desc(&ring[1]);
+      issue(ta, 0);
+      issue(tb, 1);
+      land(tb);
+    }
+    ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
     for (int i = 0; n_tiles < 0 || i < n_tiles; ++i) {
-      ring_barrier();  // step i
+      // the consumers multiply tile i
+      const Tile tn = read_desc(&ring[(i + 2) & (kRing - 1)]);
+      issue(tn, i + 2);
       publish(i + 4);
+      land(tn);
+      ring_barrier();  // tile i done, tile i + 1 in its stage
     }
   } else {
     // ---------------- consumers: wave w multiplies for head h
@@ -714,18 +738,6 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     const bool live = w < n_here && ((a.head_mask >> h) & 1);
     const int32_t my_row = i0 + (lane & 31);
     const int32_t qchunk = period ? i0 / period : 0;
-    const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
-    const char* vg = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
-    const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
-    const uint32_t stage0 = lds_addr(&stage[0][0]);
-    auto list_of = [&](const Tile& tt) {
-      return a.vl + ((int64_t)(h_first + (tt.wave < 0 ? 0 : tt.wave)) * a.n_rb + rb) * a.max_vert;
-    };
-    auto issue = [&](const Tile& tt, int j) {
-      if (tt.n > 0)
-        issue_share<D, NW>(kg, vg, kvst_b, tt, list_of(tt),
-                           stage0 + (uint32_t)((j & (kStages - 1)) * B::kBytes), w, lane);
-    };
     LaneConst<D> lc;
     lane_consts<D>(lc, lane);
     WaveState<D> st;
@@ -742,14 +754,8 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         C = load_win(colb, tt.ks);
       }
     };
-    ring_barrier();  // descriptors 0 .. 3 published
+    ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
     Tile t0 = read_desc(&ring[0]);
-    {
-      const Tile t1 = read_desc(&ring[1]), t2 = read_desc(&ring[2]);
-      issue(t0, 0);
-      issue(t1, 1);
-      issue(t2, 2);
-    }
     // DCA relation of a tile (the same for every wave: all share the rows)
     auto var_of = [&](const Tile& tt) {
       const int32_t rel = qchunk - tt.kchunk;
@@ -758,16 +764,9 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     Win W0{}, C0{}, W1{}, C1{};
     load_windows(t0, W0, C0);
     int i = 0;
-    // one step per tile (tile i in stage i mod 4)
+    // one step per tile (tile i in stage i mod 4), then the step's barrier
     auto step = [&]() {
-      // this wave's loads of tile i have landed (i + 1 and i + 2 may be in flight)
       const Tile t1 = read_desc(&ring[(i + 1) & (kRing - 1)]);
-      const Tile t2 = read_desc(&ring[(i + 2) & (kRing - 1)]);
-      if (t2.n > 0) wait_vm<2 * P>();
-      else if (t1.n > 0) wait_vm<P>();
-      else wait_vm<0>();
-      ring_barrier();  // tile i is in its stage for every wave; stage i - 1 is free
-      issue(read_desc(&ring[(i + 3) & (kRing - 1)]), i + 3);
       const char* bc = stage[i & (kStages - 1)];
       // this wave's key mask for the tile; act: any pair, full: all 64 x 32
       uint64_t mword = 0;
@@ -776,14 +775,19 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
       else if (live && t0.wave == w)
         mword = gather_mask(t0, reinterpret_cast<const int32_t*>(bc + B::kKeyOff), my_row);
       const bool row_ok = my_row <= rlast;
-      const bool act = __ballot(mword != 0 && row_ok) != 0;
-      const bool masked = __ballot(mword == ~0ull || !row_ok) != ~0ull;
+      if (!row_ok) mword = 0;
+      const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+      const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+      const bool act = act0 || act1;
+      const bool masked = __ballot(mword == ~0ull) != ~0ull;
       // the next tile's windows are requested during this tile's softmax
-      wave_tile<D>(a, bc, lc, st, act, masked, mword, half, [&] { load_windows(t1, W1, C1); });
+      wave_tile<D>(a, bc, lc, st, act0, act1, masked, mword, half,
+                   [&] { load_windows(t1, W1, C1); });
       if (act) {
         ++exec_tiles;
         if (half == 0 && row_ok) sel += (uint32_t)__popcll(mword);
       }
+      ring_barrier();  // tile i done, tile i + 1 in its stage
       t0 = t1;
       W0 = W1;
       C0 = C1;
