@@ -8,7 +8,7 @@
 // softmax: deepseekmodel.com long-context architecture page, §3.2.
 //
 // Work decomposition (our design; the pages give no kernel):
-//  * a workgroup = the query heads of one KV head (up to 8, one wave each)
+//  * a workgroup = the query heads of one KV head (up to 7, one wave each)
 //    x one block of 32 query rows; every wave multiplies the same K/V tiles,
 //    so a tile is read from HBM once for all heads of the group;
 //  * a planning kernel marks, per (KV group, row block), the 16-key granules
@@ -432,11 +432,8 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 // One (wave, key tile) step on the stage `smem`.  With `masked`, mword is the
 // 64-bit key mask of this lane's row.  act0 / act1: the wave has pairs in key
-// half 0 / 1 of the tile; an empty half skips its QK product and its
-// softmax, and enters the PV product with zero weights (the O accumulators
-// then go through the same instructions on every path, and the compiler
-// keeps them in place: a branch around the PV product makes it copy them
-// between register sets).  `after_qk` runs once the QK products are issued
+// half 0 / 1 of the tile; an empty half skips its QK product, its softmax
+// and its two k-steps of the PV product.  `after_qk` runs once the QK products are issued
 // (scalar loads issued there land during the softmax).
 template <int D, typename F>
 __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
@@ -527,20 +524,22 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
     __builtin_memcpy(&vf, vv, 16);
     return vf;
   };
-  // V fragments of k-step s + 1 are read while the products of s run
-  bf16x8 vf[2][DB];
+  // each key half with pairs: its two k-steps, V fragments read together
 #pragma unroll
-  for (int db = 0; db < DB; ++db) vf[0][db] = load_v(0, db);
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!act[kb]) continue;
+    bf16x8 vf[2][DB];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < 3) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) vf[(s + 1) & 1][db] = load_v(s + 1, db);
-    }
+      for (int db = 0; db < DB; ++db) vf[j][db] = load_v(2 * kb + j, db);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s & 1][db], pf[s], st.o[db], 0, 0, 0);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j][db], pf[2 * kb + j], st.o[db],
+                                                           0, 0, 0);
   }
 }
 
@@ -604,6 +603,18 @@ __device__ __forceinline__ void wait_vm() {
 // accesses across.
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// The head waves' barrier at the end of a step: every LDS read they issued
+// has been consumed by then (the products waited for it), so only scalar
+// loads of the next tile's windows can be outstanding, and those need not
+// land before the barrier.  A stage is refilled two barriers after the step
+// that reads it, so reads that the compiler moves past this barrier still
+// complete in time.
+__device__ __forceinline__ void step_barrier() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
@@ -787,7 +798,7 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         ++exec_tiles;
         if (half == 0 && row_ok) sel += (uint32_t)__popcll(mword);
       }
-      ring_barrier();  // tile i done, tile i + 1 in its stage
+      step_barrier();  // tile i done, tile i + 1 in its stage
       t0 = t1;
       W0 = W1;
       C0 = C1;
