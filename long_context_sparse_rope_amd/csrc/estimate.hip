@@ -42,30 +42,95 @@ struct EstArgs {
   float* diag;            // [H][n_diag][2][64]
   int64_t n_diag;
   uint64_t head_mask;
+  int32_t n_sub, nw;      // workgroups per KV head, query heads (waves) per workgroup
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxEstGroup = 8;  // one wave per query head of a KV group
+constexpr int kMaxEstWaves = 7;  // query heads per workgroup (+1 loader wave)
+constexpr int kEstStages = 4;    // LDS ring of key tiles
 
+// A 64-key tile of K in LDS: 16-byte chunk c of row r sits at slot
+// c ^ (r mod 16) of the row (no padding, bank-spread fragment reads).
 template <int D>
 struct KTile {
-  static constexpr int kStride = D + 8;  // bf16 elements per LDS row (16 B pad)
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kBytes = kTileK * kRowBytes;
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;  // rows one 64-lane load fills
+  static constexpr int kInstr = kTileK / kRowsPerInstr;   // loads per tile
 };
 
-// Cooperative load of the 64-key tile starting at key k0 into LDS (rows past
-// n_ctx are zero).  Every thread of the block takes part.
 template <int D>
-__device__ __forceinline__ void load_k_tile(const EstArgs& a, int g, int64_t k0,
-                                            uint16_t* ks) {
-  constexpr int kChunks = D / 8;  // 16-byte chunks per key row
-  const int nthr = blockDim.x;
-  const uint16_t* base = a.k + (int64_t)g * a.kv_sh;
-  for (int c = threadIdx.x; c < kTileK * kChunks; c += nthr) {
-    const int r = c / kChunks, col = (c % kChunks) * 8;
-    const int64_t key = k0 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < a.n_ctx) v = *reinterpret_cast<const u32x4*>(base + key * a.kv_st + col);
-    *reinterpret_cast<u32x4*>(ks + r * KTile<D>::kStride + col) = v;
+__device__ __forceinline__ int kslot(int chunk, int row) {
+  return (chunk ^ (row & 15)) & (KTile<D>::kChunks - 1);
+}
+
+__device__ __forceinline__ uint32_t est_lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// global -> LDS, 16 bytes per lane; M0 holds the LDS byte address of lane 0's
+// 16 bytes.  No register results, so nothing is left in flight in a VGPR.
+__device__ __forceinline__ void est_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N), other counters untouched.
+template <int N>
+__device__ __forceinline__ void est_wait_vm() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier of the key ring: LDS reads and writes of this wave retire
+// first (lgkmcnt(0)); no release fence (that would wait for every load in
+// flight).  The loader waits for a tile's loads (vmcnt) before arriving.
+__device__ __forceinline__ void est_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Loader wave: streams the workgroup's key tiles [t_begin, t_end) of KV head
+// g into the ring (tile i in stage i mod 4), two tiles ahead of the heads;
+// rows past n_ctx repeat the last key (those keys are masked).  Arrives at
+// one barrier before the first tile and one after each tile, like the heads.
+template <int D>
+__device__ void est_loader(const EstArgs& a, int g, int64_t t_begin, int64_t t_end,
+                           char* ring, int lane) {
+  using T = KTile<D>;
+  constexpr int R = T::kRowsPerInstr;
+  const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
+  const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+  const uint32_t ring0 = est_lds_addr(ring);
+  const int sub = lane / T::kChunks, cl = lane % T::kChunks;
+  auto issue = [&](int64_t i) {
+    const int64_t t = t_begin + i;
+    if (t >= t_end) return;
+    const int64_t k0 = t * kTileK;
+    const int32_t n = (int32_t)(a.n_ctx - k0 < kTileK ? a.n_ctx - k0 : kTileK);
+    const char* kb = kg + k0 * kvst_b;
+    const uint32_t dst = ring0 + (uint32_t)((i & (kEstStages - 1)) * T::kBytes);
+#pragma unroll
+    for (int gi = 0; gi < T::kInstr; ++gi) {
+      const int row = gi * R + sub;
+      const uint32_t rr = (uint32_t)(row < n ? row : n - 1);
+      est_dma16(kb, rr * kvst_b + (uint32_t)kslot<D>(cl, row) * 16u, dst + gi * 1024);
+    }
+  };
+  auto land = [&](int64_t ahead) {  // only tile `ahead` may still be in flight
+    if (t_begin + ahead < t_end) est_wait_vm<T::kInstr>();
+    else est_wait_vm<0>();
+  };
+  issue(0);
+  issue(1);
+  land(1);
+  est_barrier();
+  for (int64_t i = 0; t_begin + i < t_end; ++i) {
+    issue(i + 2);
+    land(i + 2);
+    est_barrier();
   }
 }
 
@@ -82,11 +147,14 @@ __device__ __forceinline__ void load_q_frags(const EstArgs& a, int h, int64_t c,
           base + (int64_t)(b * 32 + (lane & 31)) * D + s * 16 + 8 * (lane >> 5));
 }
 
+// K fragment s of key block kb: lane -> key row 32 kb + lane % 32, chunk
+// 2 s + lane / 32.
 template <int D>
-__device__ __forceinline__ bf16x8 k_frag(const uint16_t* ks, int kb, int s) {
+__device__ __forceinline__ bf16x8 k_frag(const char* ks, int kb, int s) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + (lane & 31)) * KTile<D>::kStride +
-                                          s * 16 + 8 * (lane >> 5));
+  const int row = kb * 32 + (lane & 31);
+  return *reinterpret_cast<const bf16x8*>(ks + row * KTile<D>::kRowBytes +
+                                          kslot<D>(2 * s + (lane >> 5), row) * 16);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -97,25 +165,31 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // ------------------------------------------------------------------ pass 1
 template <int D>
-__global__ void __launch_bounds__(512) est_pass1(EstArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK * KTile<D>::kStride];
-  const int g = blockIdx.y, split = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = g * a.G + w;
-  const bool active = (a.head_mask >> h) & 1;
+__global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) {
+  __shared__ __attribute__((aligned(16))) char ring[kEstStages][KTile<D>::kBytes];
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / a.n_sub, sub = blockIdx.y % a.n_sub;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n_here = min(a.nw, a.G - sub * a.nw);
   const int64_t t_begin = (int64_t)split * a.tiles_per_split;
   const int64_t t_end = t_begin + a.tiles_per_split < a.n_tiles ? t_begin + a.tiles_per_split
                                                                  : a.n_tiles;
+  if (w == a.nw) {
+    est_loader<D>(a, g, t_begin, t_end, &ring[0][0], lane);
+    return;
+  }
+  const int h = g * a.G + sub * a.nw + w;
+  const bool active = w < n_here && ((a.head_mask >> h) & 1);
   bf16x8 qf[2][D / 16];
   int64_t cur_c = -1;
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   const int half = lane >> 5;
-  for (int64_t t = t_begin; t < t_end; ++t) {
+  est_barrier();  // the first tile is in its stage
+  for (int64_t i = 0; t_begin + i < t_end; ++i) {
+    const int64_t t = t_begin + i;
     const int64_t k0 = t * kTileK;
-    __syncthreads();
-    load_k_tile<D>(a, g, k0, ks);
-    __syncthreads();
-    if (!active) continue;
+    const char* ks = ring[i & (kEstStages - 1)];
+    if (active) {
     const int64_t c = a.period ? k0 / a.period : 0;
     if (c != cur_c) {
       load_q_frags<D>(a, h, c, qf);
@@ -158,6 +232,8 @@ __global__ void __launch_bounds__(512) est_pass1(EstArgs a) {
       l[b] = l[b] * exp2f(m[b] - mx) + sum;
       m[b] = mx;
     }
+    }
+    est_barrier();  // tile i done, tile i + 1 in its stage
   }
   if (!active) return;
 #pragma unroll
@@ -195,110 +271,125 @@ __global__ void est_combine(EstArgs a) {
 
 // ------------------------------------------------------------------ pass 2
 // Diagonal sums of a 32x32 block held in the S = Q K^T layout (lane -> key
-// column n = lane % 32, register r -> query row 8(r/4) + 4(lane/32) + r%4):
-// out[d + 31] = sum_m X[m][m - d], d in [-31, 31], m ascending.
-__device__ __forceinline__ void diag_record(const float (&x)[16], float* scratch,
-                                            float* dst) {
+// column n = lane % 32, register r -> query row m = 8(r/4) + 4(lane/32) +
+// r%4): dst[d + 31] = sum_m X[m][m - d], d in [-31, 31] (dst[63] = 0).
+// Lane t of each half pulls, for each of its half's rows m, the value of
+// diagonal t (key n = m - t) or of diagonal t - 32 (key n = m - t + 32) with a
+// lane permute; the two halves are then added, lower half first.  The order
+// of the sums is fixed, so the records are reproducible.
+__device__ __forceinline__ void diag_record(const float (&x)[16], float* dst) {
   const int lane = threadIdx.x & 63;
-  const int n = lane & 31, half = lane >> 5;
+  const int t = lane & 31, half = lane >> 5;
+  float pos = 0.f, neg = 0.f;  // diagonal t, diagonal t - 32
 #pragma unroll
-  for (int r = 0; r < 16; ++r) scratch[(8 * (r >> 2) + 4 * half + (r & 3)) * 33 + n] = x[r];
-  wave_lds_sync();
-  if (lane < 63) {
-    const int d = lane - 31;
-    const int m0 = d > 0 ? d : 0, m1 = d < 0 ? 31 + d : 31;
-    float s = 0.f;
-    for (int mm = m0; mm <= m1; ++mm) s += scratch[mm * 33 + (mm - d)];
-    dst[lane] = s;
-  } else {
-    dst[63] = 0.f;
+  for (int r = 0; r < 16; ++r) {
+    const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+    const int src = (half << 5) | ((m - t) & 31);
+    const float v =
+        __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x[r])));
+    if (m >= t) pos += v;
+    else neg += v;
   }
-  wave_lds_sync();
+  const float pos_o = __shfl_xor(pos, 32), neg_o = __shfl_xor(neg, 32);
+  if (half == 0) {
+    dst[t + 31] = pos + pos_o;
+    if (t > 0) dst[t - 1] = neg + neg_o;
+    else dst[63] = 0.f;
+  }
 }
 
 template <int D>
-__global__ void __launch_bounds__(512) est_pass2(EstArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK * KTile<D>::kStride];
-  __shared__ float scratch_all[kMaxEstGroup][32 * 33];
-  const int g = blockIdx.y, split = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = g * a.G + w;
-  const bool active = (a.head_mask >> h) & 1;
-  const int half = lane >> 5;
-  float* scratch = scratch_all[w];
+__global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) {
+  __shared__ __attribute__((aligned(16))) char ring[kEstStages][KTile<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) float lse_all[kMaxEstWaves][kEstRows];
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / a.n_sub, sub = blockIdx.y % a.n_sub;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n_here = min(a.nw, a.G - sub * a.nw);
   const int64_t t_begin = (int64_t)split * a.tiles_per_split;
   const int64_t t_end = t_begin + a.tiles_per_split < a.n_tiles ? t_begin + a.tiles_per_split
                                                                  : a.n_tiles;
+  if (w == a.nw) {
+    est_loader<D>(a, g, t_begin, t_end, &ring[0][0], lane);
+    return;
+  }
+  const int h = g * a.G + sub * a.nw + w;
+  const bool active = w < n_here && ((a.head_mask >> h) & 1);
+  const int half = lane >> 5;
   bf16x8 qf[2][D / 16];
   int64_t cur_c = -1;
-  // log2-sum-exp of this lane's rows (INFINITY for padding rows -> p = 0)
-  float lse[2][16];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      lse[b][r] = active ? a.lse2[h * kEstRows + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3)]
-                         : INFINITY;
+  // log2-sum-exp of the wave's 64 rows (INFINITY for padding rows -> p = 0),
+  // kept in LDS: rows 8 j + 4 half .. + 3 of block b are one 16-byte read
+  float* lse = lse_all[w];
+  lse[lane] = active ? a.lse2[h * kEstRows + lane] : INFINITY;
   float* vout = a.vscore + (int64_t)h * a.n_ctx;
   float* drec = a.diag + (int64_t)h * a.n_diag * 2 * 64;
-  for (int64_t t = t_begin; t < t_end; ++t) {
+  est_barrier();  // the first tile is in its stage
+  for (int64_t i = 0; t_begin + i < t_end; ++i) {
+    const int64_t t = t_begin + i;
     const int64_t k0 = t * kTileK;
-    __syncthreads();
-    load_k_tile<D>(a, g, k0, ks);
-    __syncthreads();
-    if (!active) continue;
+    const char* ks = ring[i & (kEstStages - 1)];
+    if (active) {
     const int64_t c = a.period ? k0 / a.period : 0;
     if (c != cur_c) {
       load_q_frags<D>(a, h, c, qf);
       cur_c = c;
     }
     const bool edge = (k0 + kTileK - 1 > a.row0);
-    float p[2][2][16];  // [kb][b][r]
+    // probabilities of the 32x32 block (row block b, key block kb)
+    auto block_p = [&](int kb, int b, float (&pp)[16]) {
+      f32x16 acc = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int s = 0; s < D / 16; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[b][s], k_frag<D>(ks, kb, s), acc, 0,
+                                                      0, 0);
+      const int64_t key = k0 + kb * 32 + (lane & 31);
+      float lr[16];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x16 acc = {};
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(&lr[4 * j]) =
+            *reinterpret_cast<const float4*>(lse + b * 32 + 8 * j + 4 * half);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[b][s], k_frag<D>(ks, kb, s), acc,
-                                                        0, 0, 0);
-        const int64_t key = k0 + kb * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = exp2f(acc[r] * a.scale_log2 - lse[b][r]);
-          if (edge) {
-            const int64_t row = a.row0 + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > row || key >= a.n_ctx) v = 0.f;
-          }
-          p[kb][b][r] = v;
+      for (int r = 0; r < 16; ++r) {
+        float v = exp2f(acc[r] * a.scale_log2 - lr[r]);
+        if (edge) {
+          const int64_t row = a.row0 + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > row || key >= a.n_ctx) v = 0.f;
         }
+        pp[r] = v;
       }
-    // vertical scores: fixed order (b = 0 rows, then b = 1 rows; lower half first)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    };
+    // vertical scores of key block kb: fixed order (b = 0 rows, then b = 1
+    // rows; lower half first)
+    auto vertical = [&](int kb, const float (&p0)[16], const float (&p1)[16]) {
       float s = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int r = 0; r < 16; ++r) s += p0[r];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += p[kb][b][r];
+      for (int r = 0; r < 16; ++r) s += p1[r];
       const float o = __shfl_xor(s, 32);
       const float tot = half ? o + s : s + o;
       const int64_t key = k0 + kb * 32 + (lane & 31);
       if (half == 0 && key < a.n_ctx) vout[key] = tot;
+    };
+    // diagonal records (index e + 1): e = 2t holds blocks (0,0) + (1,1),
+    // e = 2t + 1 slot 0 the block (b 0, kb 1), e = 2t - 1 slot 1 the block
+    // (b 1, kb 0)
+    float p00[16], p01[16];  // [b][r] of key block 0
+    block_p(0, 0, p00);
+    block_p(0, 1, p01);
+    vertical(0, p00, p01);
+    diag_record(p01, drec + ((2 * t) * 2 + 1) * 64);
+    float p10[16], p11[16];
+    block_p(1, 0, p10);
+    block_p(1, 1, p11);
+    vertical(1, p10, p11);
+    diag_record(p10, drec + ((2 * t + 2) * 2 + 0) * 64);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p00[r] += p11[r];
+    diag_record(p00, drec + ((2 * t + 1) * 2 + 0) * 64);
     }
-    // diagonal records: e = 2t (blocks (0,0) + (1,1)), e = 2t + 1 (b=0, kb=1,
-    // slot 0), e = 2t - 1 (b=1, kb=0, slot 1); record index e + 1
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = p[0][0][r] + p[1][1][r];
-    diag_record(x, scratch, drec + ((2 * t + 1) * 2 + 0) * 64);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = p[1][0][r];
-    diag_record(x, scratch, drec + ((2 * t + 2) * 2 + 0) * 64);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = p[0][1][r];
-    diag_record(x, scratch, drec + ((2 * t) * 2 + 1) * 64);
+    est_barrier();  // tile i done, tile i + 1 in its stage
   }
 }
 
@@ -351,8 +442,6 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
   float* vsc = vscore ? vscore : vs_ws;
   float* ssc = sscore ? sscore : ss_ws;
   const int64_t c1 = L.n_ctx;
-  if (!select_only && p.n_heads / p.n_kv_heads > kMaxEstGroup)
-    return fail(LCSR_ENOTSUP, "the estimate supports n_heads / n_kv_heads <= %d", kMaxEstGroup);
   if (!select_only) {
     FreqTable ft;
     int rc = build_freq_table(&p.rope, p.head_dim, &ft);
@@ -388,8 +477,11 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     if (rc) return rc;
     rc = launch_rotate_q_estimate(p, ft, d, row0, n_rows, (int)L.n_kc, q_est, s);
     if (rc) return rc;
-    const dim3 grid((unsigned)L.n_split, (unsigned)p.n_kv_heads);
-    const dim3 block((unsigned)(64 * a.G));
+    // a workgroup = up to kMaxEstWaves query heads of one KV head + a loader
+    a.n_sub = (a.G + kMaxEstWaves - 1) / kMaxEstWaves;
+    a.nw = (a.G + a.n_sub - 1) / a.n_sub;
+    const dim3 grid((unsigned)L.n_split, (unsigned)(p.n_kv_heads * a.n_sub));
+    const dim3 block((unsigned)(64 * (a.nw + 1)));
     if (p.head_dim == 128) hipLaunchKernelGGL(est_pass1<128>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(est_pass1<64>, grid, block, 0, s, a);
     rc = check_launch("estimate pass 1");
