@@ -256,17 +256,30 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
   }
 }
 
-__global__ void est_combine(EstArgs a) {
-  const int h = blockIdx.x, r = threadIdx.x;
-  if (!((a.head_mask >> h) & 1) || r >= kEstRows) return;
+// Row logsumexp from the split partials: thread (part, r) reduces splits
+// part, part + 4, ... of row r; the four parts are then merged in order.
+__global__ void __launch_bounds__(256) est_combine(EstArgs a) {
+  const int h = blockIdx.x, r = threadIdx.x & 63, part = threadIdx.x >> 6;
+  if (!((a.head_mask >> h) & 1)) return;
+  __shared__ float pm[4][kEstRows], pl[4][kEstRows];
   const float* p = a.part + ((int64_t)h * a.n_split * kEstRows + r) * 2;
   float mm = -INFINITY;
-  for (int z = 0; z < a.n_split; ++z) mm = fmaxf(mm, p[(int64_t)z * kEstRows * 2]);
+  for (int z = part; z < a.n_split; z += 4) mm = fmaxf(mm, p[(int64_t)z * kEstRows * 2]);
   float ll = 0.f;
   if (mm != -INFINITY)
-    for (int z = 0; z < a.n_split; ++z)
+    for (int z = part; z < a.n_split; z += 4)
       ll += p[(int64_t)z * kEstRows * 2 + 1] * exp2f(p[(int64_t)z * kEstRows * 2] - mm);
-  a.lse2[h * kEstRows + r] = (r < a.n_rows && ll > 0.f) ? mm + log2f(ll) : INFINITY;
+  pm[part][r] = mm;
+  pl[part][r] = ll;
+  __syncthreads();
+  if (part != 0) return;
+  float M = pm[0][r];
+  for (int u = 1; u < 4; ++u) M = fmaxf(M, pm[u][r]);
+  float L = 0.f;
+  if (M != -INFINITY)
+    for (int u = 0; u < 4; ++u)
+      if (pm[u][r] != -INFINITY) L += pl[u][r] * exp2f(pm[u][r] - M);
+  a.lse2[h * kEstRows + r] = (r < a.n_rows && L > 0.f) ? M + log2f(L) : INFINITY;
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -486,7 +499,7 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     else hipLaunchKernelGGL(est_pass1<64>, grid, block, 0, s, a);
     rc = check_launch("estimate pass 1");
     if (rc) return rc;
-    hipLaunchKernelGGL(est_combine, dim3(p.n_heads), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(est_combine, dim3(p.n_heads), dim3(256), 0, s, a);
     rc = check_launch("estimate combine");
     if (rc) return rc;
     if (p.head_dim == 128) hipLaunchKernelGGL(est_pass2<128>, grid, block, 0, s, a);

@@ -93,6 +93,59 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft)
   }
 }
 
+// The same rotation, four pairs per thread with 8-byte loads and stores (bf16
+// input, 8-byte aligned rows): pairs p0 .. p0 + 3 of one token.
+template <int kTag>
+__global__ void __launch_bounds__(256) rotate4_kernel(RotateArgs a, FreqTable ft) {
+  const int64_t half = a.head_dim / 2;
+  const int64_t groups = half / 4;  // pair groups per token
+  const int64_t tok_per_block = 256 / groups;
+  const int64_t t = (int64_t)blockIdx.x * tok_per_block + threadIdx.x / groups;
+  const int64_t p0 = (threadIdx.x % groups) * 4;
+  if (threadIdx.x >= tok_per_block * groups || t >= a.n_tok) return;
+  const int nv = a.mode == kPosDca ? a.n_var : 1;
+  float c[3][4], s[3][4];
+#pragma unroll
+  for (int v = 0; v < 3; ++v)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[v][j] = 1.0f;
+      s[v][j] = 0.0f;
+    }
+  if (a.mode != kNoRotate) {
+    for (int v = 0; v < nv; ++v) {
+      int64_t pos;
+      if (a.mode == kPosArray) pos = a.pos[t];
+      else if (a.mode == kPosAffine) pos = t + a.pos_offset;
+      else pos = dca_query_pos(t + a.pos_offset, v, a.dca);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rope_cos_sin(pos, ft.inv_freq[p0 + j], &c[v][j], &s[v][j]);
+    }
+  }
+  const uint16_t* src = static_cast<const uint16_t*>(a.src);
+  for (int64_t h = 0; h < a.n_heads; ++h) {
+    const int64_t so = h * a.src_sh + t * a.src_st + p0;
+    const uint2 u1 = *reinterpret_cast<const uint2*>(src + so);
+    const uint2 u2 = *reinterpret_cast<const uint2*>(src + so + half);
+    const float x1[4] = {__uint_as_float(u1.x << 16), __uint_as_float(u1.x & 0xFFFF0000u),
+                         __uint_as_float(u1.y << 16), __uint_as_float(u1.y & 0xFFFF0000u)};
+    const float x2[4] = {__uint_as_float(u2.x << 16), __uint_as_float(u2.x & 0xFFFF0000u),
+                         __uint_as_float(u2.y << 16), __uint_as_float(u2.y & 0xFFFF0000u)};
+    for (int v = 0; v < nv; ++v) {
+      float y1[4], y2[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y1[j] = (x1[j] * c[v][j] - x2[j] * s[v][j]) * a.scale;
+        y2[j] = (x2[j] * c[v][j] + x1[j] * s[v][j]) * a.scale;
+      }
+      uint16_t* d = a.dst + v * a.dst_vs + h * a.dst_sh + t * a.dst_st + p0;
+      *reinterpret_cast<uint2*>(d) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+      *reinterpret_cast<uint2*>(d + half) =
+          make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+    }
+  }
+}
+
 __global__ void dca_positions_kernel(int64_t tok_start, int64_t n_tok, DcaParams d,
                                      int32_t* pk, int32_t* pi, int32_t* ps, int32_t* pn) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -127,6 +180,17 @@ int launch_rotate_tagged(const RotateArgs& a, const FreqTable& ft, hipStream_t s
   if (a.mode == kPosDca && (a.n_var < 1 || a.n_var > 3))
     return fail(LCSR_EINVAL, "rotate: 1 to 3 DCA query variants");
   const int64_t half = a.head_dim / 2;
+  // 8-byte accesses when every row start is 8-byte aligned
+  const bool wide = a.src_dtype == LCSR_BF16 && a.head_dim % 8 == 0 && a.head_dim <= 256 &&
+                    ((uintptr_t)a.src & 7) == 0 && ((uintptr_t)a.dst & 7) == 0 &&
+                    a.src_sh % 4 == 0 && a.src_st % 4 == 0 && a.dst_sh % 4 == 0 &&
+                    a.dst_st % 4 == 0 && a.dst_vs % 4 == 0;
+  if (wide) {
+    const int64_t tok_per_block = 256 / (half / 4);
+    const int64_t blocks = (a.n_tok + tok_per_block - 1) / tok_per_block;
+    hipLaunchKernelGGL(rotate4_kernel<kTag>, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
+    return check_launch("rotate");
+  }
   const int64_t tok_per_block = 256 / half;
   const int64_t blocks = (a.n_tok + tok_per_block - 1) / tok_per_block;
   hipLaunchKernelGGL(rotate_kernel<kTag>, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
