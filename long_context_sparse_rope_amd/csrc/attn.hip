@@ -430,22 +430,26 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One (wave, key tile) step on the stage `smem`.  With `masked`, mword is the
-// 64-bit key mask of this lane's row.  act0 / act1: the wave has pairs in key
-// half 0 / 1 of the tile; an empty half skips its QK product, its softmax
-// and its two k-steps of the PV product.  `after_qk` runs once the QK products are issued
+// Scores of one (wave, key tile) step on the stage `smem`, into the bf16
+// weights pf of the tile's PV product.  With `masked`, mword is the 64-bit key
+// mask of this lane's row.  act0 / act1: the wave has pairs in key half 0 / 1
+// of the tile; an empty half skips its QK product and its softmax (its
+// weights are zero).  `mid` runs once the QK products are issued (a wave that
+// multiplies the previous tile's PV product there overlaps those MFMAs with
+// this tile's softmax; a rescale of O for this tile's row max then applies
+// after that product, as the online softmax requires).  `after_qk` runs next
 // (scalar loads issued there land during the softmax).
-template <int D, typename F>
-__device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
-                                          const LaneConst<D>& c, WaveState<D>& st, bool act0,
-                                          bool act1, bool masked, uint64_t mword, int half,
-                                          F&& after_qk) {
+template <int D, typename M, typename F>
+__device__ __forceinline__ void wave_scores(const AttnArgs& a, const char* smem,
+                                            const LaneConst<D>& c, WaveState<D>& st,
+                                            bool act0, bool act1, bool masked, uint64_t mword,
+                                            int half, bf16x8 (&pf)[4], M&& mid,
+                                            F&& after_qk) {
   constexpr int RB = Buf<D>::kRowBytes;
   constexpr int KS = D / 16;  // k-steps of the QK product
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   const bool act[2] = {act0, act1};
   f32x16 acc[2];
-  float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     if (!act[kb]) continue;
@@ -460,6 +464,13 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], st.q[s], acc[kb], 0, 0, 0);
+  }
+  mid();
+  after_qk();
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!act[kb]) continue;
     // key k of the tile sits in register r of block kb: k = 32 kb + 8 (r / 4)
     // + 4 half + r % 4
     if (__builtin_expect(masked, 0)) {
@@ -477,7 +488,6 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[kb][r]), acc[kb][r + 1]);
   }
-  after_qk();
   if (act0 || act1) mx = max_halves(mx) * a.scale_log2;
   if (__builtin_expect(__ballot(mx > st.m + kRescaleSlack) != 0ull, 0)) {
     const float m_new = fmaxf(st.m, mx);
@@ -489,7 +499,6 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
       for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     st.m = m_new;
   }
-  bf16x8 pf[4];
   const float msub = (st.m == -INFINITY) ? 0.f : st.m;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -512,6 +521,16 @@ __device__ __forceinline__ void wave_tile(const AttnArgs& a, const char* smem,
     }
   }
   st.l += psum;
+}
+
+// The PV product of one tile: O^T += V^T P^T over the key halves with pairs.
+template <int D>
+__device__ __forceinline__ void wave_pv(const char* smem, const LaneConst<D>& c,
+                                        WaveState<D>& st, const bf16x8 (&pf)[4], bool act0,
+                                        bool act1) {
+  constexpr int RB = Buf<D>::kRowBytes;
+  constexpr int DB = D / 32;
+  const bool act[2] = {act0, act1};
   // O^T += V^T P^T; each lane receives V[16 s + 4 half + r][d0 + j] (r = 0..3
   // for the first transpose load, +8 for the second), the k-order of its P
   // fragment
@@ -775,8 +794,20 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     Win W0{}, C0{}, W1{}, C1{};
     load_windows(t0, W0, C0);
     int i = 0;
+    // The second wave on a SIMD (waves 4 .. 6 share SIMDs with waves 0 .. 2)
+    // multiplies each tile's PV product one step late, during its next
+    // tile's softmax: the two waves of a SIMD then alternate between the
+    // matrix cores and the vector ALUs instead of contending for the same
+    // unit at the same time.  The previous tile's stage is intact during the
+    // step (it is refilled after the step's barrier).
+    bf16x8 pf_prev[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pf_prev[s] = (bf16x8){};
+    bool pa0 = false, pa1 = false;
+    const char* bc_prev = stage[0];
     // one step per tile (tile i in stage i mod 4), then the step's barrier
-    auto step = [&]() {
+    auto step = [&](auto lag) {
+      constexpr bool kLag = decltype(lag)::value;
       const Tile t1 = read_desc(&ring[(i + 1) & (kRing - 1)]);
       const char* bc = stage[i & (kStages - 1)];
       // this wave's key mask for the tile; act: any pair, full: all 64 x 32
@@ -792,13 +823,30 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
       const bool act = act0 || act1;
       const bool masked = __ballot(mword == ~0ull) != ~0ull;
       // the next tile's windows are requested during this tile's softmax
-      wave_tile<D>(a, bc, lc, st, act0, act1, masked, mword, half,
-                   [&] { load_windows(t1, W1, C1); });
+      bf16x8 pf[4];
+      if constexpr (kLag) {
+        wave_scores<D>(a, bc, lc, st, act0, act1, masked, mword, half, pf,
+                       [&] { wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1); },
+                       [&] { load_windows(t1, W1, C1); });
+#pragma unroll
+        for (int s = 0; s < 4; ++s) pf_prev[s] = pf[s];
+        pa0 = act0;
+        pa1 = act1;
+        bc_prev = bc;
+      } else {
+        wave_scores<D>(a, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
+                       [&] { load_windows(t1, W1, C1); });
+        wave_pv<D>(bc, lc, st, pf, act0, act1);
+      }
       if (act) {
         ++exec_tiles;
         if (half == 0 && row_ok) sel += (uint32_t)__popcll(mword);
       }
-      step_barrier();  // tile i done, tile i + 1 in its stage
+      // tile i done, tile i + 1 in its stage; a late wave's reads of the
+      // previous stage retire before the barrier (that stage is refilled
+      // right after it)
+      if constexpr (kLag) ring_barrier();
+      else step_barrier();
       t0 = t1;
       W0 = W1;
       C0 = C1;
@@ -807,16 +855,22 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     // tiles come in runs of one DCA relation (keys ascend, so it changes at
     // most twice per walk); the query variant is loaded once per run, outside
     // the inner loop
-    while (t0.n > 0) {
-      const int var = var_of(t0);
-      if (live) {
-        load_q<D>(a, h, i0, var, st);
-        wait_vm<0>();
+    auto run = [&](auto lag) {
+      while (t0.n > 0) {
+        const int var = var_of(t0);
+        if (live) {
+          load_q<D>(a, h, i0, var, st);
+          wait_vm<0>();
+        }
+        do {
+          step(lag);
+        } while (t0.n > 0 && var_of(t0) == var);
       }
-      do {
-        step();
-      } while (t0.n > 0 && var_of(t0) == var);
-    }
+      // a late wave's last PV product (the last stage is not refilled)
+      if constexpr (decltype(lag)::value) wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1);
+    };
+    if (w >= 4) run(std::true_type{});
+    else run(std::false_type{});
 
     // ---------------- epilogue
     if (live) {
