@@ -106,6 +106,33 @@ def run_step(layer, cfg, q, k, v, out, stats, timer=None):
             timer.mark("end")
 
 
+def dense_baseline(cfg, layer, q, k, v, contexts):
+    """Full causal attention (every key, same DCA logits) of one 32K chunk
+    ending at each context length: the dense denominator of the sparse
+    speedup.  The KV cache already holds the whole prompt (from the timed
+    steps), so each point times one lcsr_vs_sparse_attn_prefill call with
+    LCSR_ATTN_DENSE on the chunk's own rows."""
+    out = {}
+    for c1 in contexts:
+        c1 = int(min(c1, cfg.seq_len)) // cfg.prefill_chunk * cfg.prefill_chunk
+        c0 = c1 - cfg.prefill_chunk
+        o = torch.empty((cfg.n_heads, cfg.prefill_chunk, cfg.head_dim), dtype=torch.bfloat16,
+                        device=q.device)
+        stats = torch.zeros(2, dtype=torch.int64, device=q.device)
+        layer.attend(q[:, c0:c1], c0, out=o, dense=True)          # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.attend(q[:, c0:c1], c0, out=o, stats=stats, dense=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        pairs = stats.cpu().tolist()[1]
+        out[str(c1)] = {"ms": round(ms, 3), "pairs": pairs,
+                        "tflops": round(4.0 * cfg.head_dim * pairs / (ms * 1e-3) / 1e12, 2)}
+    return out
+
+
 def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
     """Time the fp64 oracle on a bounded sample of the same workload: sparse
     attention rows of the last chunk (first query head, the GPU's own
@@ -155,6 +182,8 @@ def main():
     ap.add_argument("--config", default="7b_1m_dca")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--dense-ctx", default="196608,589824,1048576",
+                    help="context lengths of the dense one-chunk points ('' for none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
@@ -220,6 +249,10 @@ def main():
         "roofline": roofline,
         "attn_source_digest": attn_source_digest(),
     }
+    if args.dense_ctx:
+        print("[bench] dense one-chunk points", file=sys.stderr, flush=True)
+        rec["dense_chunk"] = dense_baseline(cfg, layer, q, k, v,
+                                            [int(x) for x in args.dense_ctx.split(",")])
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, layer, q, k, v, args.cpu_seconds)

@@ -123,6 +123,15 @@ def run_layer(name):
         hist = layer.refine_chunk(qc, c0, rows_t, out[:, :lc], lse=lse[:, :lc])
         res["refine"] = {"history": [h.numpy() for h in hist], "base": (base_v, base_s),
                          "after": (list(layer.n_vert), list(layer.n_slash)), "c1": c0 + lc}
+    if name == "7b_1m_dca":
+        # dense mode (every causal key, same DCA logits) on the last chunk
+        c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
+        layer.attend(q[:, c0:c0 + lc], c0, out=out[:, :lc], lse=lse[:, :lc], dense=True)
+        rows = np.array([c0, c0 + 1, c0 + lc // 2, c0 + lc - 1], dtype=np.int64)
+        ri = torch.as_tensor(rows - c0, device=DEV)
+        res["dense"] = {"rows": rows, "out": out[:, ri].cpu().numpy(),
+                        "lse": lse[:, ri].cpu().numpy(),
+                        "q": q[:, torch.as_tensor(rows, device=DEV)].float().cpu().numpy()}
     kv_heads = sorted({h // cfg.group for h in oracle_heads(cfg)})
     res["k"] = {g: k[g].float().cpu().numpy() for g in kv_heads}
     res["v"] = {g: v[g].float().cpu().numpy() for g in kv_heads}
@@ -254,3 +263,18 @@ def test_recall_and_refinement_full_size():
     assert list(nv) == after_v and list(ns) == after_s
     # larger budgets select supersets of the same scores: recall cannot drop
     assert np.all(hist[1][raised] >= mean0[raised] - 1e-5)
+
+
+def test_dense_mode_1m_sampled_rows():
+    """Dense mode at the 1M context (last chunk): sampled rows against the
+    oracle's full causal attention with the same DCA logits."""
+    name = "7b_1m_dca"
+    cfg = CONFIGS[name]
+    res = run_layer(name)
+    dn = res["dense"]
+    for h in (0, cfg.n_heads - 1):
+        ctx = key_context(name, h // cfg.group)
+        ro, rl = oracle.dense_causal_rows(dn["q"][h].astype(np.float64), dn["rows"], ctx,
+                                          res["sm"])
+        compare(dn["out"][h].astype(np.float64), ro)
+        lse_compare(dn["lse"][h].astype(np.float64), rl)
