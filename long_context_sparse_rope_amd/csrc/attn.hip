@@ -24,10 +24,11 @@
 //    touch are skipped by its wave, tiles it fully covers run unmasked;
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (V^T read
 //    with the LDS transpose load ds_read_b64_tr_b16): each lane owns one
-//    query row, so the softmax max / sum and the O rescale are in-lane; the
-//    row max is only raised when it grows by more than 2^8 (the exponent
-//    bound keeps p <= 256), and the row sum adds the bf16 weights the PV
-//    product uses (v_dot2_f32_bf16);
+//    query row, so the softmax max / sum and the O rescale are in-lane; a
+//    tile's own max is taken only when a row has none yet or its weights sum
+//    above 2^64 (weights are exact for any running max; it only guards the
+//    range), and the row sum adds the bf16 weights the PV product uses
+//    (v_dot2_f32_bf16);
 //  * the DCA relation of the row block and a tile picks one of three
 //    pre-rotated query variants (intra / successive / inter).
 #include <algorithm>
@@ -42,7 +43,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr int kStages = 4;             // LDS ring of K/V tiles
 constexpr int kRunGap = kRowBlock;     // offsets at most this far apart share a run
 constexpr int kGranPerChunk = 64 * 32; // granules covered by one 64-word bitmap chunk
@@ -467,13 +467,12 @@ __device__ __forceinline__ void wave_scores(const AttnArgs& a, const char* smem,
   }
   mid();
   after_qk();
-  float mx = -INFINITY;
+  // key k of the tile sits in register r of block kb: k = 32 kb + 8 (r / 4)
+  // + 4 half + r % 4
+  if (__builtin_expect(masked, 0)) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if (!act[kb]) continue;
-    // key k of the tile sits in register r of block kb: k = 32 kb + 8 (r / 4)
-    // + 4 half + r % 4
-    if (__builtin_expect(masked, 0)) {
+    for (int kb = 0; kb < 2; ++kb) {
+      if (!act[kb]) continue;
       const uint32_t word = (uint32_t)((mword >> (4 * half)) >> (32 * kb));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -484,41 +483,57 @@ __device__ __forceinline__ void wave_scores(const AttnArgs& a, const char* smem,
             __uint_as_float((__float_as_uint(acc[kb][r]) & keep) | (0xFF800000u & ~keep));
       }
     }
-    // row max of the raw scores (the scale is positive)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[kb][r]), acc[kb][r + 1]);
   }
-  if (act0 || act1) mx = max_halves(mx) * a.scale_log2;
-  if (__builtin_expect(__ballot(mx > st.m + kRescaleSlack) != 0ull, 0)) {
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = (st.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
-    st.m = m_new;
-  }
-  const float msub = (st.m == -INFINITY) ? 0.f : st.m;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float psum = 0.f;
+  // weights 2^(l - m) against the row's running max m and their sum
+  auto weights = [&](float msub, float& psum) {
+    psum = 0.f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (act[s >> 1]) {
+    for (int s = 0; s < 4; ++s) {
+      if (act[s >> 1]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[s][e] = (__bf16)__builtin_amdgcn_exp2f(
-            fmaf(acc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msub));
-      // row sum of the bf16 weights the PV product uses
+        for (int e = 0; e < 8; ++e)
+          pf[s][e] = (__bf16)__builtin_amdgcn_exp2f(
+              fmaf(acc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msub));
+        // row sum of the bf16 weights the PV product uses
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pf[s][e], pf[s][e + 1]};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pf[s][e], pf[s][e + 1]};
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+        }
+      } else {
+        pf[s] = (bf16x8){};
       }
-    } else {
-      pf[s] = (bf16x8){};
     }
+  };
+  // The running max only guards the range: a weight is exact for any m, so
+  // the tile's own max is needed only when a row has no max yet (its first
+  // keys) or a weight may be far above 1 (sum above 2^64, well inside the
+  // range of fp32 and bf16).
+  float psum;
+  weights(st.m == -INFINITY ? 0.f : st.m, psum);
+  const bool has_key = mword != 0ull;
+  if (__builtin_expect(__ballot((st.m == -INFINITY && has_key) || !(psum <= 0x1p64f)) != 0ull,
+                       0)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (!act[kb]) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[kb][r]), acc[kb][r + 1]);
+    }
+    mx = max_halves(mx) * a.scale_log2;
+    if (mx > st.m) {
+      const float alpha = (st.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m - mx);
+      st.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+      st.m = mx;
+    }
+    weights(st.m == -INFINITY ? 0.f : st.m, psum);
   }
   st.l += psum;
 }
