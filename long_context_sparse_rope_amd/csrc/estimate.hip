@@ -372,35 +372,45 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
         pp[r] = v;
       }
     };
-    // vertical scores of key block kb: fixed order (b = 0 rows, then b = 1
-    // rows; lower half first)
-    auto vertical = [&](int kb, const float (&p0)[16], const float (&p1)[16]) {
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s += p0[r];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s += p1[r];
+    // vertical score of key block kb from this lane's partial row sum s:
+    // the two halves' rows, lower half first
+    auto vertical = [&](int kb, float s) {
       const float o = __shfl_xor(s, 32);
       const float tot = half ? o + s : s + o;
       const int64_t key = k0 + kb * 32 + (lane & 31);
       if (half == 0 && key < a.n_ctx) vout[key] = tot;
     };
-    // diagonal records (index e + 1): e = 2t holds blocks (0,0) + (1,1),
-    // e = 2t + 1 slot 0 the block (b 0, kb 1), e = 2t - 1 slot 1 the block
-    // (b 1, kb 0)
-    float p00[16], p01[16];  // [b][r] of key block 0
-    block_p(0, 0, p00);
-    block_p(0, 1, p01);
-    vertical(0, p00, p01);
-    diag_record(p01, drec + ((2 * t) * 2 + 1) * 64);
-    float p10[16], p11[16];
-    block_p(1, 0, p10);
-    block_p(1, 1, p11);
-    vertical(1, p10, p11);
-    diag_record(p10, drec + ((2 * t + 2) * 2 + 0) * 64);
+    // The four 32x32 blocks (key block kb, row block b) in the order that
+    // keeps at most two of them live: (0,0) and (1,1) first (their sum is one
+    // diagonal record), then (kb 0, b 1) and (kb 1, b 0).  Vertical sums in a
+    // fixed order: key block 0 adds its b = 0 rows then its b = 1 rows, key
+    // block 1 its b = 1 rows then its b = 0 rows.  Diagonal records (index
+    // e + 1): e = 2t holds blocks (0,0) + (1,1), e = 2t + 1 slot 0 the block
+    // (b 0, kb 1), e = 2t - 1 slot 1 the block (b 1, kb 0).
+    float pa[16], pb[16];
+    block_p(0, 0, pa);
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p00[r] += p11[r];
-    diag_record(p00, drec + ((2 * t + 1) * 2 + 0) * 64);
+    for (int r = 0; r < 16; ++r) s0 += pa[r];
+    __builtin_amdgcn_sched_barrier(0);
+    block_p(1, 1, pb);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1 += pb[r];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pa[r] += pb[r];
+    diag_record(pa, drec + ((2 * t + 1) * 2 + 0) * 64);
+    __builtin_amdgcn_sched_barrier(0);
+    block_p(0, 1, pa);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0 += pa[r];
+    vertical(0, s0);
+    diag_record(pa, drec + ((2 * t) * 2 + 1) * 64);
+    __builtin_amdgcn_sched_barrier(0);
+    block_p(1, 0, pb);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1 += pb[r];
+    vertical(1, s1);
+    diag_record(pb, drec + ((2 * t + 2) * 2 + 0) * 64);
     }
     est_barrier();  // tile i done, tile i + 1 in its stage
   }
