@@ -209,8 +209,10 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
                                                             acc[kb], 0, 0, 0);
       }
       const int64_t row = a.row0 + b * 32 + (lane & 31);
+      // row max and sum over four interleaved partial chains (fixed order),
+      // which keeps the dependent vector chains short
       float x[2][16];
-      float mx = m[b];
+      float mp[4] = {m[b], -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -221,14 +223,18 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
             if (key > row || key >= a.n_ctx) v = -INFINITY;
           }
           x[kb][r] = v;
-          mx = fmaxf(mx, v);
+          mp[r & 3] = fmaxf(mp[r & 3], v);
         }
+      const float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
       if (mx == -INFINITY) continue;
-      float sum = 0.f;
+      // exponentials below 2^-126 flush to zero (v_exp_f32); they are far
+      // below the precision of the row sum
+      float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum += exp2f(x[kb][r] - mx);
+        for (int r = 0; r < 16; ++r) sp[r & 3] += __builtin_amdgcn_exp2f(x[kb][r] - mx);
+      const float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]);
       l[b] = l[b] * exp2f(m[b] - mx) + sum;
       m[b] = mx;
     }
@@ -364,7 +370,9 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
             *reinterpret_cast<const float4*>(lse + b * 32 + 8 * j + 4 * half);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = exp2f(acc[r] * a.scale_log2 - lr[r]);
+        // probabilities below 2^-126 flush to zero (v_exp_f32): their sum
+        // over the estimate rows stays below 2^-120
+        float v = __builtin_amdgcn_exp2f(acc[r] * a.scale_log2 - lr[r]);
         if (edge) {
           const int64_t row = a.row0 + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           if (key > row || key >= a.n_ctx) v = 0.f;
