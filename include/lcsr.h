@@ -67,6 +67,7 @@ extern "C" {
 #define LCSR_WS_ESTIMATE 0
 #define LCSR_WS_ATTN 1
 #define LCSR_WS_RECALL 2
+#define LCSR_WS_DECODE 3
 
 /* Rotary embedding setup ([architecture overview] §2.4 code; YaRN from
  * [Qwen2.5-1M explainer] Length Extrapolation and [long-context blog]
@@ -222,6 +223,26 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
                                 int64_t o_stride_t, float* lse, int64_t* stats,
                                 uint32_t flags, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/* lcsr_attn_decode — decode-step attention: the sequence's newest rows,
+ * tokens i = chunk_start .. chunk_start + chunk_len - 1 (their K and V
+ * already in the caches), against every key j <= i, with the same DCA logits
+ * and temperature as the prefill ([Qwen2.5-1M explainer] Length
+ * Extrapolation: intra / successive / inter relations; アルゴリズム: weights
+ * with the DCA positions).  Dense (no pattern): a decode step reads the whole
+ * K/V prefix once and is bound by HBM bandwidth (long-context engineering
+ * page, §7.1).  out_i = softmax(l_i.) over j <= i times V; lse_i natural log.
+ *   p          chunk_start may be any token (no 64-token alignment with
+ *              DCA); (n_heads / n_kv_heads) x chunk_len <= 32
+ *   out        [H, chunk_len, D] with strides o_stride_h / o_stride_t,
+ *              out_dtype LCSR_FP32 or LCSR_BF16, 16-byte aligned
+ *   lse        fp32 [H, chunk_len] or NULL
+ *   ws         workspace >= lcsr_workspace_bytes(LCSR_WS_DECODE)
+ * Results are bitwise reproducible (the key splits merge in a fixed order).
+ * Errors: LCSR_EINVAL, LCSR_ENOTSUP, LCSR_EWORKSPACE, LCSR_EHIP. */
+int lcsr_attn_decode(const lcsr_problem_t* p, void* out, int32_t out_dtype,
+                     int64_t o_stride_h, int64_t o_stride_t, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* lcsr_attn_recall_check — attention recall of sampled rows
  * ([Qwen2.5-1M explainer] Chunked Prefill: lse_full over every j <= i,

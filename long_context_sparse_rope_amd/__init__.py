@@ -9,12 +9,12 @@ fails loudly if it has not been built.
 from . import _capi
 from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, yarn_softmax_scale,
                   rope_yarn_apply, dca_positions, vs_pattern_estimate,
-                  vs_sparse_attn_prefill, attn_recall_check, workspace_bytes)
+                  vs_sparse_attn_prefill, attn_decode, attn_recall_check, workspace_bytes)
 from .driver import ChunkedSparsePrefill
 
 _capi.load()
 
 __all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "yarn_softmax_scale",
            "rope_yarn_apply", "dca_positions", "vs_pattern_estimate",
-           "vs_sparse_attn_prefill", "attn_recall_check", "workspace_bytes",
+           "vs_sparse_attn_prefill", "attn_decode", "attn_recall_check", "workspace_bytes",
            "ChunkedSparsePrefill"]

@@ -22,10 +22,11 @@ LCSR_ATTN_DENSE = 0x1
 LCSR_WS_ESTIMATE = 0
 LCSR_WS_ATTN = 1
 LCSR_WS_RECALL = 2
+LCSR_WS_DECODE = 3
 
 EXPORTED = ("lcsr_workspace_bytes", "lcsr_last_error", "lcsr_rope_yarn_apply",
             "lcsr_dca_positions", "lcsr_vs_pattern_estimate",
-            "lcsr_vs_sparse_attn_prefill", "lcsr_attn_recall_check")
+            "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_recall_check")
 
 
 class lcsr_rope_t(ctypes.Structure):
@@ -92,6 +93,9 @@ def load():
     lib.lcsr_vs_sparse_attn_prefill.argtypes = [P(lcsr_problem_t), P(lcsr_pattern_t), vp, vp,
                                                 i32, i64, i64, vp, vp, u32, vp,
                                                 ctypes.c_size_t, vp]
+    lib.lcsr_attn_decode.restype = ctypes.c_int
+    lib.lcsr_attn_decode.argtypes = [P(lcsr_problem_t), vp, i32, i64, i64, vp, vp,
+                                     ctypes.c_size_t, vp]
     lib.lcsr_attn_recall_check.restype = ctypes.c_int
     lib.lcsr_attn_recall_check.argtypes = [P(lcsr_problem_t), P(lcsr_pattern_t), vp, vp, i32,
                                            vp, vp, vp, vp, ctypes.c_size_t, vp]

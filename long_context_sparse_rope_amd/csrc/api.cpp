@@ -97,6 +97,29 @@ AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_sl
   return L;
 }
 
+// Decode workspace: the rows' query variants, then per (KV head, key split)
+// the partial O [32][D] and (m, l) [32][2] of the 32 matrix rows.
+DecodeLayout decode_layout(const lcsr_problem_t& p) {
+  DecodeLayout L{};
+  const int64_t H = p.n_heads, D = p.head_dim;
+  L.n_ctx = p.chunk_start + p.chunk_len;
+  L.n_tiles = (L.n_ctx + kTileK - 1) / kTileK;
+  L.n_var = p.dca.chunk > 0 ? 3 : 1;
+  // about 1024 one-wave workgroups over the KV heads
+  const int64_t want = (1024 + p.n_kv_heads - 1) / (p.n_kv_heads > 0 ? p.n_kv_heads : 1);
+  L.n_split = want < L.n_tiles ? want : L.n_tiles;
+  if (L.n_split < 1) L.n_split = 1;
+  size_t off = 0;
+  L.o_q_rot = off;
+  off += align256((size_t)L.n_var * H * (p.chunk_len > 0 ? p.chunk_len : 1) * D * 2);
+  L.o_part_o = off;
+  off += align256((size_t)p.n_kv_heads * L.n_split * 32 * D * 4);
+  L.o_part_ml = off;
+  off += align256((size_t)p.n_kv_heads * L.n_split * 32 * 2 * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace lcsr
 
 using namespace lcsr;
@@ -105,7 +128,9 @@ namespace {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-int validate_problem(const lcsr_problem_t* p, bool need_v) {
+// any_start: the rows may start anywhere (decode); otherwise, with DCA, the
+// chunk must start on a 64-token tile
+int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = false) {
   if (!p) return fail(LCSR_EINVAL, "problem is NULL");
   if (!p->q || !p->k_cache || (need_v && !p->v_cache))
     return fail(LCSR_EINVAL, "q/k_cache/v_cache pointer is NULL");
@@ -136,7 +161,7 @@ int validate_problem(const lcsr_problem_t* p, bool need_v) {
     if (p->dca.local < 0 || p->dca.local >= p->dca.chunk)
       return fail(LCSR_EINVAL, "dca.local must be in [0, dca.chunk)");
     const int64_t period = p->dca.chunk - p->dca.local;
-    if (period % kTileK || p->chunk_start % kTileK)
+    if (period % kTileK || (!any_start && p->chunk_start % kTileK))
       return fail(LCSR_ENOTSUP, "with DCA, chunk - local (%lld) and chunk_start must be "
                   "multiples of %d", (long long)period, kTileK);
     if (p->dca.chunk > ((int64_t)1 << 30))
@@ -178,11 +203,12 @@ const char* lcsr_last_error(void) { return g_err; }
 
 size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert,
                             int32_t max_slash) {
-  if (!p || validate_problem(p, false) != LCSR_OK) return 0;
+  if (!p || validate_problem(p, false, which == LCSR_WS_DECODE) != LCSR_OK) return 0;
   switch (which) {
     case LCSR_WS_ESTIMATE: return estimate_layout(*p).total;
     case LCSR_WS_ATTN: return attn_layout(*p, max_vert, max_slash, true).total;
     case LCSR_WS_RECALL: return attn_layout(*p, max_vert, max_slash, false).total;
+    case LCSR_WS_DECODE: return decode_layout(*p).total;
     default: set_error("unknown workspace kind %d", which); return 0;
   }
 }
@@ -304,6 +330,29 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
   if (p->chunk_len == 0) return LCSR_OK;
   return run_attention(*p, P, hm, out, out_dtype, o_stride_h, o_stride_t, lse, stats, dense,
                        static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int lcsr_attn_decode(const lcsr_problem_t* p, void* out, int32_t out_dtype,
+                     int64_t o_stride_h, int64_t o_stride_t, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int rc = validate_problem(p, true, true);
+  if (rc) return rc;
+  const int G = p->n_heads / p->n_kv_heads;
+  if ((int64_t)G * p->chunk_len > 32)
+    return fail(LCSR_ENOTSUP, "decode takes (n_heads / n_kv_heads) x chunk_len <= 32 rows, got "
+                "%d x %lld", G, (long long)p->chunk_len);
+  if (!out || !aligned16(out)) return fail(LCSR_EINVAL, "out must be non-NULL and 16-byte aligned");
+  if (out_dtype != LCSR_FP32 && out_dtype != LCSR_BF16)
+    return fail(LCSR_EINVAL, "out_dtype must be LCSR_FP32 or LCSR_BF16");
+  if (o_stride_t < p->head_dim || o_stride_h < p->head_dim)
+    return fail(LCSR_EINVAL, "output strides must be >= head_dim");
+  const DecodeLayout L = decode_layout(*p);
+  if (!ws || ws_bytes < L.total || !aligned16(ws))
+    return fail(LCSR_EWORKSPACE, "decode needs %zu workspace bytes (16-byte aligned), got %zu",
+                L.total, ws_bytes);
+  if (p->chunk_len == 0) return LCSR_OK;
+  return run_decode(*p, out, out_dtype, o_stride_h, o_stride_t, lse, static_cast<char*>(ws),
+                    static_cast<hipStream_t>(stream));
 }
 
 int lcsr_attn_recall_check(const lcsr_problem_t* p, const lcsr_pattern_t* pat,

@@ -440,7 +440,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // after that product, as the online softmax requires).  `after_qk` runs next
 // (scalar loads issued there land during the softmax).
 template <int D, typename M, typename F>
-__device__ __forceinline__ void wave_scores(const AttnArgs& a, const char* smem,
+__device__ __forceinline__ void wave_scores(float scale_log2, const char* smem,
                                             const LaneConst<D>& c, WaveState<D>& st,
                                             bool act0, bool act1, bool masked, uint64_t mword,
                                             int half, bf16x8 (&pf)[4], M&& mid,
@@ -495,7 +495,7 @@ __device__ __forceinline__ void wave_scores(const AttnArgs& a, const char* smem,
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           pf[s][e] = (__bf16)__builtin_amdgcn_exp2f(
-              fmaf(acc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msub));
+              fmaf(acc[s >> 1][8 * (s & 1) + e], scale_log2, -msub));
         // row sum of the bf16 weights the PV product uses
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -523,7 +523,7 @@ __device__ __forceinline__ void wave_scores(const AttnArgs& a, const char* smem,
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[kb][r]), acc[kb][r + 1]);
     }
-    mx = max_halves(mx) * a.scale_log2;
+    mx = max_halves(mx) * scale_log2;
     if (mx > st.m) {
       const float alpha = (st.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m - mx);
       st.l *= alpha;
@@ -840,7 +840,7 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
       // the next tile's windows are requested during this tile's softmax
       bf16x8 pf[4];
       if constexpr (kLag) {
-        wave_scores<D>(a, bc, lc, st, act0, act1, masked, mword, half, pf,
+        wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf,
                        [&] { wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1); },
                        [&] { load_windows(t1, W1, C1); });
 #pragma unroll
@@ -849,7 +849,7 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         pa1 = act1;
         bc_prev = bc;
       } else {
-        wave_scores<D>(a, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
+        wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
                        [&] { load_windows(t1, W1, C1); });
         wave_pv<D>(bc, lc, st, pf, act0, act1);
       }
@@ -1195,6 +1195,183 @@ int launch_attn_nw(const AttnArgs& a, int nw, int64_t grid, size_t dyn_lds, hipS
   }
 }
 
+// ---------------------------------------------------------------- decode
+// Decode-step attention: the newest rows of the sequence (tokens c0 .. c0 +
+// n_q - 1, whose keys are already in the cache) against every causal key,
+// dense, with the DCA logits of the prefill (Length Extrapolation: intra /
+// successive / inter relations; blocked online softmax: deepseekmodel.com
+// §3.2).  The step reads the whole K/V prefix once, so the work is split
+// over the keys: workgroup (split, KV head) is one wave that streams its key
+// range through a two-stage K/V ring in LDS, with the G x n_q (head, row)
+// pairs of the KV group on the 32 rows of the matrix products, and writes
+// the unnormalised partial (m, l, O) of every pair; decode_combine merges
+// the splits in a fixed order.
+struct DecArgs {
+  const uint16_t* __restrict__ q_rot;  // [n_var][H][n_q][D]
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  int64_t kv_sh, kv_st;
+  int32_t H, G, n_var, n_q, n_split;
+  int64_t c0, n_ctx, period, n_tiles, tiles_per_split;
+  float scale_log2;
+  float* part_o;   // [H_kv][n_split][32][D]
+  float* part_ml;  // [H_kv][n_split][32][2]
+};
+
+constexpr int kDecStages = 2;
+
+template <int D>
+__global__ void __launch_bounds__(64) decode_kernel(DecArgs a) {
+  using B = Buf<D>;
+  constexpr int kPerTile = Issue<D>::kPerTile;
+  __shared__ __attribute__((aligned(16))) char stage[kDecStages][B::kBytes];
+  const int split = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x, half = lane >> 5;
+  const int64_t t_begin = (int64_t)split * a.tiles_per_split;
+  const int64_t t_end =
+      t_begin + a.tiles_per_split < a.n_tiles ? t_begin + a.tiles_per_split : a.n_tiles;
+  // this lane's matrix row: (head, row) pair rho; rows past G x n_q repeat a
+  // live pair's query and are never written
+  const int rho = lane & 31;
+  const bool live = rho < a.G * a.n_q;
+  const int hh = live ? rho / a.n_q : 0, r = live ? rho % a.n_q : 0;
+  const int h = g * a.G + hh;
+  const int64_t pos = a.c0 + r;
+  const int64_t qchunk = a.period ? pos / a.period : 0;
+  LaneConst<D> lc;
+  lane_consts<D>(lc, lane);
+  WaveState<D> st;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.o[db] = (f32x16){};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
+  const char* vg = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
+  const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+  const uint32_t stage0 = lds_addr(&stage[0][0]);
+  auto tile_of = [&](int64_t t) {
+    Tile x;
+    x.ks = (int32_t)(t * kTileK);
+    x.n = (int32_t)(a.n_ctx - x.ks < kTileK ? a.n_ctx - x.ks : kTileK);
+    x.wave = -1;
+    x.kchunk = a.period ? (int32_t)(x.ks / a.period) : 0;
+    x.kmax = x.ks + x.n - 1;
+    x.gran = 15;
+    return x;
+  };
+  // tile t goes into stage (t - t_begin) mod 2; the stage last held tile
+  // t - 2, whose products are done
+  auto issue = [&](int64_t t) {
+    issue_tile<D>(kg, vg, kvst_b, tile_of(t), nullptr,
+                  stage0 + (uint32_t)(((t - t_begin) & 1) * B::kBytes), lane);
+  };
+  int cur_var = -1;
+  if (t_begin < t_end) issue(t_begin);
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const bool more = t + 1 < t_end;
+    if (more) {
+      issue(t + 1);
+      wait_vm<kPerTile>();  // tile t has landed
+    } else {
+      wait_vm<0>();
+    }
+    const Tile tt = tile_of(t);
+    // the query variant of this lane's row against the tile's DCA chunk (a
+    // tile never crosses a chunk edge: the period is a multiple of 64)
+    const int64_t rel = qchunk - tt.kchunk;
+    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (int)rel);
+    if (__ballot(var != cur_var) != 0ull) {
+      const uint16_t* base =
+          a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const bf16x8*>(base + s * 16);
+      wait_vm<0>();
+      cur_var = var;
+    }
+    // keys <= this row's token; the other rows see the whole tile
+    const int64_t lim = live ? pos - tt.ks + 1 : kTileK;
+    const uint64_t mword = low_bits(lim < tt.n ? lim : tt.n);
+    const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+    const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+    const bool masked = __ballot(mword == ~0ull) != ~0ull;
+    const char* bc = stage[(t - t_begin) & 1];
+    bf16x8 pf[4];
+    wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
+    wave_pv<D>(bc, lc, st, pf, act0, act1);
+  }
+  // the split's partial for every live pair: O unnormalised, m in log2 units
+  if (live) {
+    const float l_tot = sum_halves(st.l);
+    const int64_t slot = ((int64_t)g * a.n_split + split) * 32 + rho;
+    if (half == 0) {
+      a.part_ml[slot * 2] = st.m;
+      a.part_ml[slot * 2 + 1] = l_tot;
+    }
+    float* po = a.part_o + slot * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * half;
+        *reinterpret_cast<float4*>(po + d) =
+            make_float4(st.o[db][4 * i4], st.o[db][4 * i4 + 1], st.o[db][4 * i4 + 2],
+                        st.o[db][4 * i4 + 3]);
+      }
+  }
+}
+
+// One (head, row) pair per workgroup (grid G x n_q, H_kv): the splits'
+// partials merged in split order; out = sum_s O_s 2^(m_s - M) / L and
+// lse = (M + log2 L) ln 2, with L = sum_s l_s 2^(m_s - M).
+template <int D>
+__global__ void __launch_bounds__(64) decode_combine(DecArgs a, void* out, int32_t out_dtype,
+                                                     int64_t o_sh, int64_t o_st, float* lse) {
+  const int rho = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  const int hh = rho / a.n_q, r = rho % a.n_q, h = g * a.G + hh;
+  const float* ml = a.part_ml + ((int64_t)g * a.n_split * 32 + rho) * 2;
+  const float* po = a.part_o + ((int64_t)g * a.n_split * 32 + rho) * D;
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[(int64_t)s * 64]);
+  float L = 0.f;
+  constexpr int E = D / 64;  // elements per lane
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.n_split; ++s) {
+      const float ms = ml[(int64_t)s * 64];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      L += ml[(int64_t)s * 64 + 1] * w;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += po[(int64_t)s * 32 * D + lane * E + e] * w;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = lane * E + e;
+    const float o = acc[e] * inv;
+    if (out_dtype == LCSR_FP32)
+      static_cast<float*>(out)[h * o_sh + r * o_st + d] = o;
+    else
+      static_cast<uint16_t*>(out)[h * o_sh + r * o_st + d] = f32_to_bf16(o);
+  }
+  if (lse && lane == 0) lse[(int64_t)h * a.n_q + r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+int launch_decode(const DecArgs& a, void* out, int32_t out_dtype, int64_t o_sh, int64_t o_st,
+                  float* lse, int n_kv, hipStream_t s) {
+  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)a.n_split, (unsigned)n_kv), dim3(64), 0, s,
+                     a);
+  int rc = check_launch("decode attention");
+  if (rc) return rc;
+  hipLaunchKernelGGL(decode_combine<D>, dim3((unsigned)(a.G * a.n_q), (unsigned)n_kv), dim3(64), 0,
+                     s, a, out, out_dtype, o_sh, o_st, lse);
+  return check_launch("decode combine");
+}
+
 }  // namespace
 
 // Largest context the attention supports: the row block's granule bitmap
@@ -1204,6 +1381,13 @@ int64_t attn_max_context(int64_t head_dim) {
   const int64_t rings = kRing * 16;  // descriptors
   const int64_t words = (160 * 1024 - stages - rings - 64) / 4;
   return words * 32 * kGranule;
+}
+
+// The DCA period as the attention kernels see it: a DCA chunk longer than the
+// context changes nothing (every key and query is in chunk 0); capping it
+// keeps the chunk edges inside int32.
+static int64_t attn_period(const DcaParams& d, int64_t n_ctx) {
+  return d.period ? std::min<int64_t>(d.period, (n_ctx + kTileK) / kTileK * kTileK) : 0;
 }
 
 int build_pattern_aux(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head_mask,
@@ -1278,9 +1462,7 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t h
   a.c0 = p.chunk_start;
   a.L = p.chunk_len;
   a.n_ctx = L.n_ctx;
-  // a DCA chunk longer than the context changes nothing (every key and query
-  // is in chunk 0); capping it keeps the chunk edges inside int32
-  a.period = d.period ? std::min<int64_t>(d.period, (L.n_ctx + kTileK) / kTileK * kTileK) : 0;
+  a.period = attn_period(d, L.n_ctx);
   a.scale_log2 = p.sm_scale * kLog2e;
   a.off_bits = reinterpret_cast<const uint32_t*>(ws + L.o_off_bits);
   a.col_bits = reinterpret_cast<const uint32_t*>(ws + L.o_col_bits);
@@ -1307,6 +1489,39 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t h
   const size_t dyn = (size_t)L.ubw * 4;
   if (p.head_dim == 128) return launch_attn_nw<128>(a, (int)L.nw, grid, dyn, s);
   return launch_attn_nw<64>(a, (int)L.nw, grid, dyn, s);
+}
+
+int run_decode(const lcsr_problem_t& p, void* out, int32_t out_dtype, int64_t o_sh,
+               int64_t o_st, float* lse, char* ws, hipStream_t s) {
+  const DecodeLayout L = decode_layout(p);
+  FreqTable ft;
+  int rc = build_freq_table(&p.rope, p.head_dim, &ft);
+  if (rc) return rc;
+  const DcaParams d = make_dca(&p.dca);
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(ws + L.o_q_rot);
+  rc = launch_rotate_q_variants(p, ft, d, q_rot, (int)L.n_var, s);
+  if (rc) return rc;
+  DecArgs a{};
+  a.q_rot = q_rot;
+  a.k = static_cast<const uint16_t*>(p.k_cache);
+  a.v = static_cast<const uint16_t*>(p.v_cache);
+  a.kv_sh = p.kv_stride_h;
+  a.kv_st = p.kv_stride_t;
+  a.H = p.n_heads;
+  a.G = p.n_heads / p.n_kv_heads;
+  a.n_var = (int32_t)L.n_var;
+  a.n_q = (int32_t)p.chunk_len;
+  a.n_split = (int32_t)L.n_split;
+  a.c0 = p.chunk_start;
+  a.n_ctx = L.n_ctx;
+  a.period = attn_period(d, L.n_ctx);
+  a.n_tiles = L.n_tiles;
+  a.tiles_per_split = (L.n_tiles + L.n_split - 1) / L.n_split;
+  a.scale_log2 = p.sm_scale * kLog2e;
+  a.part_o = reinterpret_cast<float*>(ws + L.o_part_o);
+  a.part_ml = reinterpret_cast<float*>(ws + L.o_part_ml);
+  if (p.head_dim == 128) return launch_decode<128>(a, out, out_dtype, o_sh, o_st, lse, p.n_kv_heads, s);
+  return launch_decode<64>(a, out, out_dtype, o_sh, o_st, lse, p.n_kv_heads, s);
 }
 
 }  // namespace lcsr

@@ -154,7 +154,12 @@ struct AttnLayout {
   bool with_plan;    // attention: union bitmaps and leftover vertical lists
   size_t o_q_rot, o_off_bits, o_col_bits, o_runs, o_run_cnt, o_union, o_vl, o_vl_cnt, total;
 };
+struct DecodeLayout {
+  int64_t n_ctx, n_tiles, n_var, n_split;
+  size_t o_q_rot, o_part_o, o_part_ml, total;
+};
 EstimateLayout estimate_layout(const lcsr_problem_t& p);
+DecodeLayout decode_layout(const lcsr_problem_t& p);
 AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_slash,
                        bool attention);
 
@@ -188,6 +193,9 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat,
                   uint64_t head_mask, void* out, int32_t out_dtype,
                   int64_t o_sh, int64_t o_st, float* lse, int64_t* stats,
                   bool dense, char* ws, hipStream_t s);
+
+int run_decode(const lcsr_problem_t& p, void* out, int32_t out_dtype, int64_t o_sh,
+               int64_t o_st, float* lse, char* ws, hipStream_t s);
 
 int run_recall(const lcsr_problem_t& p, const lcsr_pattern_t& pat,
                uint64_t head_mask, const int32_t* rows, int32_t n_rows,

@@ -246,6 +246,22 @@ def vs_sparse_attn_prefill(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale
     return out, lse
 
 
+def attn_decode(q, k_cache, v_cache, row_start, rope, dca, sm_scale, out=None,
+                out_dtype=torch.float32, lse=None, workspace=None, stream=None):
+    """Decode-step attention of the newest rows (lcsr_attn_decode): q [H, n, D]
+    holds tokens row_start .. row_start + n - 1, whose K/V are in the caches;
+    every key up to each row, DCA logits.  Returns (out [H, n, D], lse or None)."""
+    prob = _problem(q, k_cache, v_cache, row_start, rope, dca, sm_scale)
+    H, n, D = q.shape
+    if out is None:
+        out = torch.empty((H, n, D), dtype=out_dtype, device=q.device)
+    ws = _workspace(C.LCSR_WS_DECODE, prob, 0, 0, q.device, workspace)
+    _check(C.load().lcsr_attn_decode(
+        ctypes.byref(prob), out.data_ptr(), _dtype_code(out), out.stride(0), out.stride(1),
+        None if lse is None else lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out, lse
+
+
 def attn_recall_check(q, k_cache, chunk_start, rope, dca, sm_scale, pattern, rows,
                       head_mask=None, workspace=None, stream=None):
     """(lse_full, lse_sparse, recall), each [H, n_rows] (lcsr_attn_recall_check)."""

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     assert set(names) == set(C.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -146,6 +146,30 @@ def test_estimate_and_recall_reject(lib):
                                       FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == C.LCSR_EINVAL
     assert lib.lcsr_attn_recall_check(ctypes.byref(p), ctypes.byref(pat), None, None, 2,
                                       FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == C.LCSR_EINVAL
+
+
+def test_decode_workspace_and_rejects(lib):
+    # decode rows may start anywhere, also with DCA on
+    p = problem(chunk_start=1048573, chunk_len=4, dca_chunk=262144, dca_local=32768)
+    need = lib.lcsr_workspace_bytes(C.LCSR_WS_DECODE, ctypes.byref(p), 0, 0)
+    assert need > 0
+
+    def dec(pp, out=FAKE, out_dtype=C.LCSR_FP32, ws=FAKE, ws_bytes=1 << 40, o_sh=4 * 128,
+            o_st=128):
+        return lib.lcsr_attn_decode(ctypes.byref(pp), out, out_dtype, o_sh, o_st, None, ws,
+                                    ws_bytes, None)
+
+    assert dec(p, ws_bytes=need - 1) == C.LCSR_EWORKSPACE and str(need) in err(lib)
+    # 7 heads per KV head x 5 rows > 32 matrix rows
+    assert dec(problem(chunk_start=1048573, chunk_len=5)) == C.LCSR_ENOTSUP
+    assert "<= 32" in err(lib)
+    assert dec(p, out=None) == C.LCSR_EINVAL
+    assert dec(p, out_dtype=9) == C.LCSR_EINVAL
+    assert dec(p, o_st=64) == C.LCSR_EINVAL
+    assert dec(problem(head_dim=96, chunk_len=1)) == C.LCSR_ENOTSUP
+    # the prefill keeps its 64-token chunk start with DCA
+    q = problem(chunk_start=1048573, chunk_len=4, dca_chunk=262144, dca_local=32768)
+    assert attn(lib, q, pattern()) == C.LCSR_ENOTSUP
 
 
 def test_rope_and_dca_reject(lib):

@@ -132,6 +132,23 @@ def run_layer(name):
         res["dense"] = {"rows": rows, "out": out[:, ri].cpu().numpy(),
                         "lse": lse[:, ri].cpu().numpy(),
                         "q": q[:, torch.as_tensor(rows, device=DEV)].float().cpu().numpy()}
+    if name in ("7b_1m_dca", "14b_256k"):
+        # decode steps on the full cache: the newest rows (as many as fill the
+        # 32 matrix rows, then one) and, with DCA, rows across a period edge
+        nmax = 32 // cfg.group
+        cases = [(cfg.seq_len - nmax, nmax), (cfg.seq_len - 1, 1)]
+        if cfg.dca_chunk:
+            S = cfg.dca_chunk - cfg.dca_local
+            cases.append((3 * S - 2, min(4, nmax)))
+        res["decode"] = []
+        for p0, n in cases:
+            c1 = p0 + n
+            lse_d = torch.empty(H, n, device=DEV)
+            od, _ = L.attn_decode(q[:, p0:c1], layer.k_cache[:, :c1], layer.v_cache[:, :c1], p0,
+                                  layer.rope, layer.dca, sm, lse=lse_d)
+            res["decode"].append({"rows": np.arange(p0, c1), "out": od.cpu().numpy(),
+                                  "lse": lse_d.cpu().numpy(),
+                                  "q": q[:, p0:c1].float().cpu().numpy()})
     kv_heads = sorted({h // cfg.group for h in oracle_heads(cfg)})
     res["k"] = {g: k[g].float().cpu().numpy() for g in kv_heads}
     res["v"] = {g: v[g].float().cpu().numpy() for g in kv_heads}
@@ -278,3 +295,18 @@ def test_dense_mode_1m_sampled_rows():
                                           res["sm"])
         compare(dn["out"][h].astype(np.float64), ro)
         lse_compare(dn["lse"][h].astype(np.float64), rl)
+
+
+@pytest.mark.parametrize("name", ["7b_1m_dca", "14b_256k"])
+def test_decode_full_size(name):
+    """Decode steps over the whole cache (1M keys with DCA and YaRN; 256K with
+    5 query heads per KV head) against the oracle's dense causal rows."""
+    cfg = CONFIGS[name]
+    res = run_layer(name)
+    for case in res["decode"]:
+        for h in oracle_heads(cfg):
+            ctx = key_context(name, h // cfg.group)
+            ro, rl = oracle.dense_causal_rows(case["q"][h].astype(np.float64), case["rows"],
+                                              ctx, res["sm"])
+            compare(case["out"][h].astype(np.float64), ro)
+            lse_compare(case["lse"][h].astype(np.float64), rl)
