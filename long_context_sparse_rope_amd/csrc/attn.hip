@@ -1201,8 +1201,8 @@ int launch_attn_nw(const AttnArgs& a, int nw, int64_t grid, size_t dyn_lds, hipS
 // dense, with the DCA logits of the prefill (Length Extrapolation: intra /
 // successive / inter relations; blocked online softmax: deepseekmodel.com
 // §3.2).  The step reads the whole K/V prefix once, so the work is split
-// over the keys: workgroup (split, KV head) is one wave that streams its key
-// range through a two-stage K/V ring in LDS, with the G x n_q (head, row)
+// over the keys: workgroup (split, KV head) streams its key range through a
+// four-stage K/V ring in LDS and multiplies it with the G x n_q (head, row)
 // pairs of the KV group on the 32 rows of the matrix products, and writes
 // the unnormalised partial (m, l, O) of every pair; decode_combine merges
 // the splits in a fixed order.
@@ -1218,18 +1218,72 @@ struct DecArgs {
   float* part_ml;  // [H_kv][n_split][32][2]
 };
 
-constexpr int kDecStages = 2;
+constexpr int kDecStages = 5;
 
+// Workgroup: wave 0 multiplies; wave 1 loads the K tiles and wave 2 the V
+// tiles of its key range (direct-to-LDS, 16 loads per tile each, so each
+// keeps four tiles in flight under the 63-load vmcnt limit).  A stage holds
+// K then V of one tile (no key list: 32 KB at D 128, so five stages fill the
+// 160 KB of LDS).  Tile i of the range sits in stage i mod 5; at barrier i
+// tile i has landed and the products of tile i - 1 are done, so tile i + 4
+// then refills that stage.
 template <int D>
-__global__ void __launch_bounds__(64) decode_kernel(DecArgs a) {
+__global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
   using B = Buf<D>;
-  constexpr int kPerTile = Issue<D>::kPerTile;
-  __shared__ __attribute__((aligned(16))) char stage[kDecStages][B::kBytes];
+  constexpr int M = B::kInstrPerMat;  // loads per matrix and tile
+  constexpr int R = B::kRowsPerInstr;
+  constexpr int kStageBytes = 2 * B::kKBytes;
+  __shared__ __attribute__((aligned(16))) char stage[kDecStages][kStageBytes];
   const int split = blockIdx.x, g = blockIdx.y;
-  const int lane = threadIdx.x, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5;
   const int64_t t_begin = (int64_t)split * a.tiles_per_split;
   const int64_t t_end =
       t_begin + a.tiles_per_split < a.n_tiles ? t_begin + a.tiles_per_split : a.n_tiles;
+  const int n_local = t_end > t_begin ? (int)(t_end - t_begin) : 0;
+  auto tile_of = [&](int64_t t) {
+    Tile x;
+    x.ks = (int32_t)(t * kTileK);
+    x.n = (int32_t)(a.n_ctx - x.ks < kTileK ? a.n_ctx - x.ks : kTileK);
+    x.wave = -1;
+    x.kchunk = a.period ? (int32_t)(x.ks / a.period) : 0;
+    x.kmax = x.ks + x.n - 1;
+    x.gran = 15;
+    return x;
+  };
+  if (w > 0) {
+    // ---------------- loaders: wave 1 K, wave 2 V
+    const bool isv = w == 2;
+    const char* src = reinterpret_cast<const char*>((isv ? a.v : a.k) + (int64_t)g * a.kv_sh);
+    const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+    const uint32_t base = lds_addr(&stage[0][0]) + (isv ? B::kKBytes : 0);
+    const int sub = lane / B::kChunks, cl = lane % B::kChunks;
+    auto issue = [&](int i) {
+      const Tile x = tile_of(t_begin + i);
+      const char* sb = src + (int64_t)x.ks * kvst_b;
+      const uint32_t dst = base + (uint32_t)((i % kDecStages) * kStageBytes);
+#pragma unroll
+      for (int gm = 0; gm < M; ++gm) {
+        const int row = gm * R + sub;
+        const uint32_t rr = (uint32_t)(row < x.n ? row : x.n - 1);
+        const int chunk = isv ? swz_v<D>(cl, row) : swz_k<D>(cl, row);
+        dma16_s(sb, rr * kvst_b + (uint32_t)chunk * 16u, dst + gm * 1024);
+      }
+    };
+    for (int i = 0; i < kDecStages - 1 && i < n_local; ++i) issue(i);
+    for (int i = 0; i < n_local; ++i) {
+      // tile i has landed: only tiles i + 1 .. i + 3 may still be in flight
+      const int ahead = n_local - 1 - i;
+      if (ahead >= 3) wait_vm<3 * M>();
+      else if (ahead == 2) wait_vm<2 * M>();
+      else if (ahead == 1) wait_vm<M>();
+      else wait_vm<0>();
+      step_barrier();
+      if (i + kDecStages - 1 < n_local) issue(i + kDecStages - 1);
+    }
+    return;
+  }
+  // ---------------- wave 0: the products
   // this lane's matrix row: (head, row) pair rho; rows past G x n_q repeat a
   // live pair's query and are never written
   const int rho = lane & 31;
@@ -1245,46 +1299,18 @@ __global__ void __launch_bounds__(64) decode_kernel(DecArgs a) {
   for (int db = 0; db < D / 32; ++db) st.o[db] = (f32x16){};
   st.m = -INFINITY;
   st.l = 0.f;
-  const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
-  const char* vg = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
-  const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
-  const uint32_t stage0 = lds_addr(&stage[0][0]);
-  auto tile_of = [&](int64_t t) {
-    Tile x;
-    x.ks = (int32_t)(t * kTileK);
-    x.n = (int32_t)(a.n_ctx - x.ks < kTileK ? a.n_ctx - x.ks : kTileK);
-    x.wave = -1;
-    x.kchunk = a.period ? (int32_t)(x.ks / a.period) : 0;
-    x.kmax = x.ks + x.n - 1;
-    x.gran = 15;
-    return x;
-  };
-  // tile t goes into stage (t - t_begin) mod 2; the stage last held tile
-  // t - 2, whose products are done
-  auto issue = [&](int64_t t) {
-    issue_tile<D>(kg, vg, kvst_b, tile_of(t), nullptr,
-                  stage0 + (uint32_t)(((t - t_begin) & 1) * B::kBytes), lane);
-  };
   int cur_var = -1;
-  if (t_begin < t_end) issue(t_begin);
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const bool more = t + 1 < t_end;
-    if (more) {
-      issue(t + 1);
-      wait_vm<kPerTile>();  // tile t has landed
-    } else {
-      wait_vm<0>();
-    }
-    const Tile tt = tile_of(t);
+  for (int i = 0; i < n_local; ++i) {
+    step_barrier();  // tile i in its stage; the stage of tile i - 1 is released
+    const Tile tt = tile_of(t_begin + i);
     // the query variant of this lane's row against the tile's DCA chunk (a
     // tile never crosses a chunk edge: the period is a multiple of 64)
     const int64_t rel = qchunk - tt.kchunk;
     const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (int)rel);
     if (__ballot(var != cur_var) != 0ull) {
-      const uint16_t* base =
-          a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
+      const uint16_t* qb = a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const bf16x8*>(base + s * 16);
+      for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const bf16x8*>(qb + s * 16);
       wait_vm<0>();
       cur_var = var;
     }
@@ -1294,7 +1320,7 @@ __global__ void __launch_bounds__(64) decode_kernel(DecArgs a) {
     const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
     const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
     const bool masked = __ballot(mword == ~0ull) != ~0ull;
-    const char* bc = stage[(t - t_begin) & 1];
+    const char* bc = stage[i % kDecStages];
     bf16x8 pf[4];
     wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
     wave_pv<D>(bc, lc, st, pf, act0, act1);
@@ -1363,7 +1389,7 @@ __global__ void __launch_bounds__(64) decode_combine(DecArgs a, void* out, int32
 template <int D>
 int launch_decode(const DecArgs& a, void* out, int32_t out_dtype, int64_t o_sh, int64_t o_st,
                   float* lse, int n_kv, hipStream_t s) {
-  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)a.n_split, (unsigned)n_kv), dim3(64), 0, s,
+  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)a.n_split, (unsigned)n_kv), dim3(192), 0, s,
                      a);
   int rc = check_launch("decode attention");
   if (rc) return rc;
