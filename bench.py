@@ -32,6 +32,7 @@ from synth.configs import CONFIGS  # noqa: E402
 METRIC = ("ms + effective TFLOP/s per 1M-token sparse prefill (one layer); "
           "% bf16 MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 CSRC = os.path.join(ROOT, "long_context_sparse_rope_amd", "csrc")
 # sources of the kernels one vs_sparse_attn_prefill call launches
 ATTN_SOURCES = ("attn.hip", "rope.hip", "lcsr_internal.h")
@@ -133,6 +134,40 @@ def dense_baseline(cfg, layer, q, k, v, contexts):
     return out
 
 
+def decode_points(cfg, layer, q, row_counts, reps=20):
+    """Decode step over the full KV cache (left by the timed steps): the last
+    n rows of the prompt against every key up to each, one lcsr_attn_decode
+    call (the query rotations, the split-K kernel and the combine), median of
+    `reps` calls timed with HIP events on the current stream.  The K and V
+    caches are read once per call: 2 x H_kv x N x D bf16 bytes."""
+    res = {}
+    n_ctx = cfg.seq_len
+    kv_bytes = 2 * cfg.n_kv_heads * n_ctx * cfg.head_dim * 2
+    for n in row_counts:
+        p0 = n_ctx - n
+        qs = q[:, p0:n_ctx]
+        o = torch.empty((cfg.n_heads, n, cfg.head_dim), dtype=torch.float32, device=q.device)
+        ws = torch.empty(L.workspace_bytes(L._capi.LCSR_WS_DECODE, qs, layer.k_cache, p0, layer.rope, layer.dca),
+                         dtype=torch.uint8, device=q.device)
+        call = lambda: L.attn_decode(qs, layer.k_cache, layer.v_cache, p0, layer.rope, layer.dca,
+                                     layer.sm_scale, out=o, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        gbs = kv_bytes / (ms * 1e-3) / 1e9
+        res[str(n)] = {"ms": round(ms, 4), "kv_bytes": kv_bytes, "GB/s": round(gbs, 1),
+                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
+
+
 def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
     """Time the fp64 oracle on a bounded sample of the same workload: sparse
     attention rows of the last chunk (first query head, the GPU's own
@@ -184,6 +219,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--dense-ctx", default="196608,589824,1048576",
                     help="context lengths of the dense one-chunk points ('' for none)")
+    ap.add_argument("--decode-rows", default="1,4",
+                    help="rows per decode-step point over the full cache ('' for none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
@@ -253,6 +290,10 @@ def main():
         print("[bench] dense one-chunk points", file=sys.stderr, flush=True)
         rec["dense_chunk"] = dense_baseline(cfg, layer, q, k, v,
                                             [int(x) for x in args.dense_ctx.split(",")])
+    if args.decode_rows:
+        print("[bench] decode-step points", file=sys.stderr, flush=True)
+        rec["decode"] = decode_points(cfg, layer, q,
+                                      [int(x) for x in args.decode_rows.split(",")])
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, layer, q, k, v, args.cpu_seconds)

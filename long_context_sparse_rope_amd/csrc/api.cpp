@@ -106,7 +106,7 @@ DecodeLayout decode_layout(const lcsr_problem_t& p) {
   L.n_tiles = (L.n_ctx + kTileK - 1) / kTileK;
   L.n_var = p.dca.chunk > 0 ? 3 : 1;
   // one workgroup per compute unit (256) over the KV heads
-  const int64_t want = (256 + p.n_kv_heads - 1) / (p.n_kv_heads > 0 ? p.n_kv_heads : 1);
+  const int64_t want = (kMaxDecSplit + p.n_kv_heads - 1) / (p.n_kv_heads > 0 ? p.n_kv_heads : 1);
   L.n_split = want < L.n_tiles ? want : L.n_tiles;
   if (L.n_split < 1) L.n_split = 1;
   size_t off = 0;

@@ -1346,44 +1346,77 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
   }
 }
 
-// One (head, row) pair per workgroup (grid G x n_q, H_kv): the splits'
-// partials merged in split order; out = sum_s O_s 2^(m_s - M) / L and
-// lse = (M + log2 L) ln 2, with L = sum_s l_s 2^(m_s - M).
+// One (head, row) pair per workgroup of 256 threads (grid G x n_q, H_kv):
+// out = sum_s O_s 2^(m_s - M) / L and lse = (M + log2 L) ln 2, with
+// L = sum_s l_s 2^(m_s - M) and M the largest m_s.  One thread per split
+// forms its weight; the O rows are summed by D/4 float4 columns x 256/(D/4)
+// split groups, then the group sums are added in group order, so the result
+// does not depend on timing.
 template <int D>
-__global__ void __launch_bounds__(64) decode_combine(DecArgs a, void* out, int32_t out_dtype,
-                                                     int64_t o_sh, int64_t o_st, float* lse) {
-  const int rho = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+__global__ void __launch_bounds__(256) decode_combine(DecArgs a, void* out, int32_t out_dtype,
+                                                      int64_t o_sh, int64_t o_st, float* lse) {
+  constexpr int C = D / 4;     // float4 columns of a row
+  constexpr int NG = 256 / C;  // split groups
+  __shared__ float wsplit[kMaxDecSplit];
+  __shared__ float wmax[4], wsum[4];
+  __shared__ float4 gsum[NG][C];
+  const int rho = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int hh = rho / a.n_q, r = rho % a.n_q, h = g * a.G + hh;
-  const float* ml = a.part_ml + ((int64_t)g * a.n_split * 32 + rho) * 2;
-  const float* po = a.part_o + ((int64_t)g * a.n_split * 32 + rho) * D;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[(int64_t)s * 64]);
-  float L = 0.f;
-  constexpr int E = D / 64;  // elements per lane
-  float acc[E];
+  const int64_t base = (int64_t)g * a.n_split * 32 + rho;
+  const float ms = tid < a.n_split ? a.part_ml[(base + (int64_t)tid * 32) * 2] : -INFINITY;
+  const float ls = tid < a.n_split ? a.part_ml[(base + (int64_t)tid * 32) * 2 + 1] : 0.f;
+  float mx = ms;
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = ml[(int64_t)s * 64];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      L += ml[(int64_t)s * 64 + 1] * w;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) wmax[wv] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+  wsplit[tid] = w;
+  float lw = ls * w;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += po[(int64_t)s * 32 * D + lane * E + e] * w;
+  for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
+  if (lane == 0) wsum[wv] = lw;
+  __syncthreads();
+  const float L = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  // a split without keys for this row holds O = 0 and weight 0
+  const int c = tid % C, grp = tid / C;
+  const float4* po = reinterpret_cast<const float4*>(a.part_o + base * D) + c;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int s = grp; s < a.n_split; s += NG) {
+    const float4 x = po[(int64_t)s * 32 * C];
+    const float ww = wsplit[s];
+    acc.x += ww * x.x;
+    acc.y += ww * x.y;
+    acc.z += ww * x.z;
+    acc.w += ww * x.w;
+  }
+  gsum[grp][c] = acc;
+  __syncthreads();
+  if (tid < C) {
+    float4 t = gsum[0][tid];
+#pragma unroll
+    for (int k = 1; k < NG; ++k) {
+      const float4 y = gsum[k][tid];
+      t.x += y.x;
+      t.y += y.y;
+      t.z += y.z;
+      t.w += y.w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float o[4] = {t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+    const int64_t ob = h * o_sh + r * o_st + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (out_dtype == LCSR_FP32)
+        static_cast<float*>(out)[ob + e] = o[e];
+      else
+        static_cast<uint16_t*>(out)[ob + e] = f32_to_bf16(o[e]);
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int d = lane * E + e;
-    const float o = acc[e] * inv;
-    if (out_dtype == LCSR_FP32)
-      static_cast<float*>(out)[h * o_sh + r * o_st + d] = o;
-    else
-      static_cast<uint16_t*>(out)[h * o_sh + r * o_st + d] = f32_to_bf16(o);
-  }
-  if (lse && lane == 0) lse[(int64_t)h * a.n_q + r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (lse && tid == 0) lse[(int64_t)h * a.n_q + r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 template <int D>
@@ -1393,8 +1426,8 @@ int launch_decode(const DecArgs& a, void* out, int32_t out_dtype, int64_t o_sh, 
                      a);
   int rc = check_launch("decode attention");
   if (rc) return rc;
-  hipLaunchKernelGGL(decode_combine<D>, dim3((unsigned)(a.G * a.n_q), (unsigned)n_kv), dim3(64), 0,
-                     s, a, out, out_dtype, o_sh, o_st, lse);
+  hipLaunchKernelGGL(decode_combine<D>, dim3((unsigned)(a.G * a.n_q), (unsigned)n_kv), dim3(256),
+                     0, s, a, out, out_dtype, o_sh, o_st, lse);
   return check_launch("decode combine");
 }
 
@@ -1525,7 +1558,7 @@ int run_decode(const lcsr_problem_t& p, void* out, int32_t out_dtype, int64_t o_
   if (rc) return rc;
   const DcaParams d = make_dca(&p.dca);
   uint16_t* q_rot = reinterpret_cast<uint16_t*>(ws + L.o_q_rot);
-  rc = launch_rotate_q_variants(p, ft, d, q_rot, (int)L.n_var, s);
+  rc = launch_rotate_q_variants(p, ft, d, q_rot, (int)L.n_var, s, true);
   if (rc) return rc;
   DecArgs a{};
   a.q_rot = q_rot;

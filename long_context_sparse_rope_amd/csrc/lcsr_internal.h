@@ -33,6 +33,7 @@ constexpr int kGranule = 16;             // keys per bit of a row block's key-sp
 constexpr int kMaxAttnWaves = 7;         // query heads per attention workgroup (+1 loader wave)
 constexpr int kEstRows = 64;             // largest last_q
 constexpr int kBitPad = 8;               // zero words before and after each head's bitmap
+constexpr int kMaxDecSplit = 256;        // key splits of the decode step per KV head
 
 // fp64 inverse frequencies, built on the host from lcsr_rope_t.
 struct FreqTable {
@@ -126,7 +127,7 @@ int launch_dca_positions(int64_t tok_start, int64_t n_tok, const DcaParams& d,
 // dst[v][h][t][D] bf16.
 int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
                              const DcaParams& d, uint16_t* dst, int n_var,
-                             hipStream_t s);
+                             hipStream_t s, bool decode = false);
 
 // Estimate rows rotated at continuous positions for each key DCA chunk c:
 // dst[c][h][r][D] with position (row - c * S).

@@ -62,7 +62,7 @@ __device__ __forceinline__ float load_elem(const void* base, int32_t dtype, int6
 // the launch site in profiles: 0 the RoPE call, 1 the attention's query
 // variants, 2 the estimate rows.
 template <int kTag>
-__global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft) {
+__global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft, int hpb) {
   const int64_t half = a.head_dim / 2;
   const int64_t tok_per_block = 256 / half;
   const int64_t t = (int64_t)blockIdx.x * tok_per_block + threadIdx.x / half;
@@ -79,7 +79,9 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft)
       rope_cos_sin(pos, ft.inv_freq[p], &c[v], &s[v]);
     }
   }
-  for (int64_t h = 0; h < a.n_heads; ++h) {
+  const int64_t h0 = (int64_t)blockIdx.y * hpb;
+  const int64_t h1 = h0 + hpb < a.n_heads ? h0 + hpb : a.n_heads;
+  for (int64_t h = h0; h < h1; ++h) {
     const int64_t so = h * a.src_sh + t * a.src_st;
     const float x1 = load_elem(a.src, a.src_dtype, so + p);
     const float x2 = load_elem(a.src, a.src_dtype, so + p + half);
@@ -96,7 +98,7 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft)
 // The same rotation, four pairs per thread with 8-byte loads and stores (bf16
 // input, 8-byte aligned rows): pairs p0 .. p0 + 3 of one token.
 template <int kTag>
-__global__ void __launch_bounds__(256) rotate4_kernel(RotateArgs a, FreqTable ft) {
+__global__ void __launch_bounds__(256) rotate4_kernel(RotateArgs a, FreqTable ft, int hpb) {
   const int64_t half = a.head_dim / 2;
   const int64_t groups = half / 4;  // pair groups per token
   const int64_t tok_per_block = 256 / groups;
@@ -123,7 +125,9 @@ __global__ void __launch_bounds__(256) rotate4_kernel(RotateArgs a, FreqTable ft
     }
   }
   const uint16_t* src = static_cast<const uint16_t*>(a.src);
-  for (int64_t h = 0; h < a.n_heads; ++h) {
+  const int64_t h0 = (int64_t)blockIdx.y * hpb;
+  const int64_t h1 = h0 + hpb < a.n_heads ? h0 + hpb : a.n_heads;
+  for (int64_t h = h0; h < h1; ++h) {
     const int64_t so = h * a.src_sh + t * a.src_st + p0;
     const uint2 u1 = *reinterpret_cast<const uint2*>(src + so);
     const uint2 u2 = *reinterpret_cast<const uint2*>(src + so + half);
@@ -185,15 +189,19 @@ int launch_rotate_tagged(const RotateArgs& a, const FreqTable& ft, hipStream_t s
                     ((uintptr_t)a.src & 7) == 0 && ((uintptr_t)a.dst & 7) == 0 &&
                     a.src_sh % 4 == 0 && a.src_st % 4 == 0 && a.dst_sh % 4 == 0 &&
                     a.dst_st % 4 == 0 && a.dst_vs % 4 == 0;
-  if (wide) {
-    const int64_t tok_per_block = 256 / (half / 4);
-    const int64_t blocks = (a.n_tok + tok_per_block - 1) / tok_per_block;
-    hipLaunchKernelGGL(rotate4_kernel<kTag>, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
-    return check_launch("rotate");
-  }
-  const int64_t tok_per_block = 256 / half;
+  const int64_t tok_per_block = wide ? 256 / (half / 4) : 256 / half;
   const int64_t blocks = (a.n_tok + tok_per_block - 1) / tok_per_block;
-  hipLaunchKernelGGL(rotate_kernel<kTag>, dim3((unsigned)blocks), dim3(256), 0, s, a, ft);
+  // heads spread over grid.y until about 2048 workgroups: a block shares its
+  // cos/sin over its heads, and few tokens (a decode step) still fill the chip
+  int64_t hy = (2048 + blocks - 1) / blocks;
+  if (hy > a.n_heads) hy = a.n_heads;
+  const int hpb = (int)((a.n_heads + hy - 1) / hy);
+  hy = (a.n_heads + hpb - 1) / hpb;
+  const dim3 grid((unsigned)blocks, (unsigned)hy);
+  if (wide)
+    hipLaunchKernelGGL(rotate4_kernel<kTag>, grid, dim3(256), 0, s, a, ft, hpb);
+  else
+    hipLaunchKernelGGL(rotate_kernel<kTag>, grid, dim3(256), 0, s, a, ft, hpb);
   return check_launch("rotate");
 }
 }  // namespace
@@ -214,7 +222,7 @@ int launch_dca_positions(int64_t tok_start, int64_t n_tok, const DcaParams& d,
 
 int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
                              const DcaParams& d, uint16_t* dst, int n_var,
-                             hipStream_t s) {
+                             hipStream_t s, bool decode) {
   const int64_t D = p.head_dim, L = p.chunk_len, H = p.n_heads;
   RotateArgs a{};
   a.src = p.q;
@@ -233,7 +241,8 @@ int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
   a.n_var = n_var;
   a.dca = d;
   a.scale = 1.0f;
-  return launch_rotate_tagged<1>(a, ft, s);
+  // a separate instantiation for the decode step keeps the two apart in traces
+  return decode ? launch_rotate_tagged<3>(a, ft, s) : launch_rotate_tagged<1>(a, ft, s);
 }
 
 int launch_rotate_q_estimate(const lcsr_problem_t& p, const FreqTable& ft,
