@@ -20,11 +20,12 @@ library primitives used).  Sources are cited by page and section:
   "YaRN実装" (parameter names beta_fast / beta_slow / original_max_pos).
 * [architecture overview] deepseekmodel.com long-context architecture page,
   §2.2 (PI / NTK / YaRN), §2.4 code (inv_freq, rotate_half convention),
-  §3.2 (blocked attention with online softmax), §4.2 (vertical-slash).
+  §3.2 (blocked attention with online softmax), §4.1 (attention sinks and
+  the sliding window), §4.2 (vertical-slash and the other head patterns).
 
 Pinned by the ``-m "not gpu"`` tests (brute force, closed forms, invariants).
-Readings taken where the pages are silent or garbled are listed in the design doc
-and repeated next to the code they affect.  One part is "parity unpinned":
+Readings taken where the pages are silent or garbled are stated next to the
+code they affect.  One part is "parity unpinned":
 the exact YaRN frequency ramp between beta_slow and beta_fast (the pages'
 snippet is garbled; only its end points and monotonicity are pinned).
 """
@@ -37,6 +38,7 @@ from .attention import (KeyContext, attention_logits, dense_causal_rows,
                         critical_set, sparse_rows, attention_recall)
 from .estimate import estimate_scores, select_top, select_pattern
 from .refine import refine_budgets
+from .patterns import a_shape_set, a_shape_lists, choose_candidates
 
 __all__ = [
     "bf16_round", "bf16_round64", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",

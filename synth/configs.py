@@ -2,7 +2,7 @@
 
 Shapes, budgets and RoPE/DCA/YaRN settings of the synthetic layers the path
 is measured and checked on.  Values the workload description leaves open are
-fixed here (and listed with their reasons in the design doc):
+fixed here:
 
 * tiny: DCA local window W = 64 (so the key period S = C - W = 192 is a
   multiple of the 64-key tile), one prefill chunk of 1024;
