@@ -134,6 +134,36 @@ def dense_baseline(cfg, layer, q, k, v, contexts):
     return out
 
 
+def a_shape_point(cfg, layer, q, n_sink=16, n_local=2048, reps=5):
+    """The last chunk's attention with every head on the A-shape pattern
+    (sink + recent window), in pattern buffers of its own: median call time
+    with HIP events, exact pair count, algorithmic TFLOP/s."""
+    c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
+    c1 = c0 + lc
+    pat = L.Pattern(cfg.n_heads, n_sink, n_local, q.device)
+    L.pattern_fill_a_shape(pat, n_sink, n_local, c1)
+    o = torch.empty((cfg.n_heads, lc, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
+    stats = torch.zeros(2, dtype=torch.int64, device=q.device)
+    call = lambda st=None: L.vs_sparse_attn_prefill(  # noqa: E731
+        q[:, c0:c1], layer.k_cache[:, :c1], layer.v_cache[:, :c1], c0, layer.rope, layer.dca,
+        layer.sm_scale, pat, out=o, stats=st)
+    call(stats)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    pairs = stats.cpu().tolist()[1]
+    return {"n_sink": n_sink, "n_local": n_local, "chunk": [c0, c1], "ms": round(ms, 3),
+            "pairs": pairs,
+            "tflops": round(4.0 * cfg.head_dim * pairs / (ms * 1e-3) / 1e12, 2)}
+
+
 def decode_points(cfg, layer, q, row_counts, reps=20):
     """Decode step over the full KV cache (left by the timed steps): the last
     n rows of the prompt against every key up to each, one lcsr_attn_decode
@@ -219,6 +249,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--dense-ctx", default="196608,589824,1048576",
                     help="context lengths of the dense one-chunk points ('' for none)")
+    ap.add_argument("--no-a-shape", action="store_true",
+                    help="skip the last-chunk A-shape (sink 16 + window 2048) point")
     ap.add_argument("--decode-rows", default="1,4",
                     help="rows per decode-step point over the full cache ('' for none)")
     args = ap.parse_args()
@@ -290,6 +322,9 @@ def main():
         print("[bench] dense one-chunk points", file=sys.stderr, flush=True)
         rec["dense_chunk"] = dense_baseline(cfg, layer, q, k, v,
                                             [int(x) for x in args.dense_ctx.split(",")])
+    if not args.no_a_shape:
+        print("[bench] a-shape chunk point", file=sys.stderr, flush=True)
+        rec["a_shape_chunk"] = a_shape_point(cfg, layer, q)
     if args.decode_rows:
         print("[bench] decode-step points", file=sys.stderr, flush=True)
         rec["decode"] = decode_points(cfg, layer, q,

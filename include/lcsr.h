@@ -166,6 +166,27 @@ int lcsr_rope_yarn_apply(const void* x, int32_t x_dtype, int64_t x_stride_h,
                          const lcsr_rope_t* rope, float scale, uint32_t flags,
                          void* stream);
 
+/* lcsr_pattern_fill_a_shape — the A-shape head pattern (attention sinks plus
+ * a sliding window, [architecture overview] §4.1; one pattern per head,
+ * §4.2) written into the rows of `pat` whose head_mask entry is non-zero
+ * (every row if head_mask is NULL): verticals 0 .. min(n_sink, n_ctx) - 1,
+ * slash offsets 0 .. min(n_local, n_ctx) - 1, ascending, the rest of each
+ * row -1, and the counts.  Under the vertical-slash rule row i then attends
+ * to every j <= i with j < n_sink or i - j < n_local.  Other rows are left
+ * as they are, so one pattern can hold A-shape heads beside heads filled by
+ * lcsr_vs_pattern_estimate (with the complementary head_mask).
+ *   pat        (host struct, device arrays) as for lcsr_vs_pattern_estimate
+ *   n_heads    rows of the pattern arrays, 1 .. 64
+ *   head_mask  (host) int32 [n_heads] or NULL
+ *   n_sink     0 .. pat->max_vert;  n_local 0 .. pat->max_slash
+ *   n_ctx      keys visible to the chunk (chunk_start + chunk_len)
+ * Asynchronous on `stream`.  Errors: LCSR_EINVAL for a NULL or inconsistent
+ * pattern, n_heads out of range, negative sizes or sizes beyond the pattern's
+ * row lengths (nothing written); LCSR_EHIP if the launch fails. */
+int lcsr_pattern_fill_a_shape(const lcsr_pattern_t* pat, int32_t n_heads,
+                              const int32_t* head_mask, int32_t n_sink, int32_t n_local,
+                              int64_t n_ctx, void* stream);
+
 /* lcsr_dca_positions — DCA position maps of tokens [tok_start, tok_start +
  * n_tok) ([Qwen2.5-1M explainer] Length Extrapolation, see lcsr_dca_t).
  * Each output is int32 [n_tok] or NULL (not written).  With DCA off every

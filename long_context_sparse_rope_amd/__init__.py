@@ -9,12 +9,13 @@ fails loudly if it has not been built.
 from . import _capi
 from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, yarn_softmax_scale,
                   rope_yarn_apply, dca_positions, vs_pattern_estimate,
-                  vs_sparse_attn_prefill, attn_decode, attn_recall_check, workspace_bytes)
-from .driver import ChunkedSparsePrefill
+                  vs_sparse_attn_prefill, attn_decode, attn_recall_check, workspace_bytes,
+                  pattern_fill_a_shape)
+from .driver import ChunkedSparsePrefill, search_head_patterns
 
 _capi.load()
 
 __all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "yarn_softmax_scale",
            "rope_yarn_apply", "dca_positions", "vs_pattern_estimate",
            "vs_sparse_attn_prefill", "attn_decode", "attn_recall_check", "workspace_bytes",
-           "ChunkedSparsePrefill"]
+           "pattern_fill_a_shape", "ChunkedSparsePrefill", "search_head_patterns"]

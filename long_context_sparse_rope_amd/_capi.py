@@ -26,7 +26,8 @@ LCSR_WS_DECODE = 3
 
 EXPORTED = ("lcsr_workspace_bytes", "lcsr_last_error", "lcsr_rope_yarn_apply",
             "lcsr_dca_positions", "lcsr_vs_pattern_estimate",
-            "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_recall_check")
+            "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_recall_check",
+            "lcsr_pattern_fill_a_shape")
 
 
 class lcsr_rope_t(ctypes.Structure):
@@ -85,6 +86,8 @@ def load():
                                          P(lcsr_rope_t), f32, u32, vp]
     lib.lcsr_dca_positions.restype = ctypes.c_int
     lib.lcsr_dca_positions.argtypes = [i64, i64, P(lcsr_dca_t), vp, vp, vp, vp, vp]
+    lib.lcsr_pattern_fill_a_shape.restype = ctypes.c_int
+    lib.lcsr_pattern_fill_a_shape.argtypes = [P(lcsr_pattern_t), i32, vp, i32, i32, i64, vp]
     lib.lcsr_vs_pattern_estimate.restype = ctypes.c_int
     lib.lcsr_vs_pattern_estimate.argtypes = [P(lcsr_problem_t), i32, vp, vp, vp,
                                              P(lcsr_pattern_t), vp, vp, u32, vp,

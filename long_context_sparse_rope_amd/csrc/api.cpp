@@ -266,6 +266,26 @@ int lcsr_dca_positions(int64_t tok_start, int64_t n_tok, const lcsr_dca_t* dca,
                               pq_inter, static_cast<hipStream_t>(stream));
 }
 
+int lcsr_pattern_fill_a_shape(const lcsr_pattern_t* pat, int32_t n_heads,
+                              const int32_t* head_mask, int32_t n_sink, int32_t n_local,
+                              int64_t n_ctx, void* stream) {
+  int rc = validate_pattern(nullptr, pat, true);
+  if (rc) return rc;
+  if (n_heads < 1 || n_heads > kMaxHeads)
+    return fail(LCSR_EINVAL, "n_heads must be in [1, %d]", kMaxHeads);
+  if (n_sink < 0 || n_local < 0 || n_ctx < 0)
+    return fail(LCSR_EINVAL, "n_sink, n_local and n_ctx must be >= 0");
+  if (n_sink > pat->max_vert || n_local > pat->max_slash)
+    return fail(LCSR_EINVAL, "n_sink %d / n_local %d exceed max_vert %d / max_slash %d", n_sink,
+                n_local, pat->max_vert, pat->max_slash);
+  uint64_t mask = 0;
+  for (int h = 0; h < n_heads; ++h)
+    if (!head_mask || head_mask[h]) mask |= (uint64_t)1 << h;
+  const int32_t nv = (int32_t)std::min<int64_t>(n_sink, n_ctx);
+  const int32_t ns = (int32_t)std::min<int64_t>(n_local, n_ctx);
+  return launch_fill_a_shape(*pat, n_heads, mask, nv, ns, static_cast<hipStream_t>(stream));
+}
+
 int lcsr_vs_pattern_estimate(const lcsr_problem_t* p, int32_t last_q,
                              const int32_t* n_vert, const int32_t* n_slash,
                              const int32_t* head_mask, const lcsr_pattern_t* pat,

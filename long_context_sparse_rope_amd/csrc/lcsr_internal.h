@@ -198,6 +198,11 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat,
 int run_decode(const lcsr_problem_t& p, void* out, int32_t out_dtype, int64_t o_sh,
                int64_t o_st, float* lse, char* ws, hipStream_t s);
 
+// A-shape rows (verticals 0 .. nv - 1, slashes 0 .. ns - 1) for the heads
+// of `mask`.
+int launch_fill_a_shape(const lcsr_pattern_t& pat, int32_t n_heads, uint64_t mask,
+                        int32_t nv, int32_t ns, hipStream_t s);
+
 int run_recall(const lcsr_problem_t& p, const lcsr_pattern_t& pat,
                uint64_t head_mask, const int32_t* rows, int32_t n_rows,
                float* lse_full, float* lse_sparse, float* recall, char* ws,

@@ -7,6 +7,13 @@ queries with continuous positions, then the chunk's attention is computed
 over them with DCA positions.  Chunked Prefill gives the 32,768-token chunk
 and the attention-recall check used by the refinement.
 
+Heads may also carry a fixed A-shape pattern (attention sinks plus a recent
+window, the page deepseekmodel.com long-context architecture overview, §4.1)
+instead of an estimated vertical-slash one; §4.2 there gives each head one
+pattern.  `search_head_patterns` is the offline per-head search of the
+0h-n0.github.io page, section 疎アテンション, scored by attention recall
+(section Chunked Prefill).
+
 Every numeric step runs in liblcsr.so; this module only sequences the calls
 on one stream and owns the KV cache buffers.
 """
@@ -21,7 +28,9 @@ class ChunkedSparsePrefill:
 
     K and V caches are bf16 [H_kv, max_ctx, D]; keys are stored rotated at
     their DCA key position.  Budgets are per query head and may be raised by
-    `refine_chunk`.
+    `refine_chunk`.  A head is either a vertical-slash head (budgets n_vert,
+    n_slash, pattern from the estimate) or an A-shape head (n_sink, n_local,
+    no estimate); see `set_head_patterns`.
     """
 
     def __init__(self, n_heads, n_kv_heads, head_dim, max_ctx, rope, dca, sm_scale,
@@ -33,6 +42,7 @@ class ChunkedSparsePrefill:
         self.device = torch.device(device)
         self.n_vert = [int(n_vert)] * n_heads if isinstance(n_vert, int) else list(n_vert)
         self.n_slash = [int(n_slash)] * n_heads if isinstance(n_slash, int) else list(n_slash)
+        self.a_shape = [None] * n_heads      # (n_sink, n_local) of A-shape heads
         self.k_cache = torch.empty((n_kv_heads, self.max_ctx, head_dim), dtype=torch.bfloat16,
                                    device=self.device)
         self.v_cache = torch.empty_like(self.k_cache)
@@ -49,11 +59,43 @@ class ChunkedSparsePrefill:
         ops.rope_yarn_apply(v_chunk, None, self.rope, rotate=False,
                             out=self.v_cache[:, chunk_start:chunk_start + n])
 
+    def set_head_patterns(self, configs):
+        """One configuration per query head: {"kind": "vs", "n_vert": a,
+        "n_slash": b} or {"kind": "a_shape", "n_sink": s, "n_local": w}.
+        The pattern buffers grow to fit."""
+        if len(configs) != self.H:
+            raise ValueError("one configuration per query head")
+        for h, c in enumerate(configs):
+            if c["kind"] == "vs":
+                self.n_vert[h], self.n_slash[h] = int(c["n_vert"]), int(c["n_slash"])
+                self.a_shape[h] = None
+            elif c["kind"] == "a_shape":
+                self.a_shape[h] = (int(c["n_sink"]), int(c["n_local"]))
+            else:
+                raise ValueError(f"unknown pattern kind {c['kind']!r}")
+        mv = max(self.n_vert + [a[0] for a in self.a_shape if a])
+        ms = max(self.n_slash + [a[1] for a in self.a_shape if a])
+        if mv > self.pattern.max_vert or ms > self.pattern.max_slash:
+            self.pattern = ops.Pattern(self.H, max(mv, self.pattern.max_vert),
+                                       max(ms, self.pattern.max_slash), self.device)
+
     def estimate(self, q_chunk, chunk_start, head_mask=None):
+        """The chunk's pattern: the estimate for vertical-slash heads, the
+        A-shape rows for the others (only heads in head_mask, if given)."""
         c1 = chunk_start + q_chunk.shape[1]
-        return ops.vs_pattern_estimate(
-            q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
-            self.n_vert, self.n_slash, self.pattern, last_q=self.last_q, head_mask=head_mask)
+        sel = [head_mask is None or bool(head_mask[h]) for h in range(self.H)]
+        vs = [sel[h] and self.a_shape[h] is None for h in range(self.H)]
+        if any(vs):
+            ops.vs_pattern_estimate(
+                q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
+                self.n_vert, self.n_slash, self.pattern, last_q=self.last_q,
+                head_mask=None if all(vs) else vs)
+        sizes = sorted({self.a_shape[h] for h in range(self.H) if sel[h] and self.a_shape[h]})
+        for size in sizes:
+            ops.pattern_fill_a_shape(self.pattern, size[0], size[1], c1,
+                                     head_mask=[sel[h] and self.a_shape[h] == size
+                                                for h in range(self.H)])
+        return self.pattern
 
     def attend(self, q_chunk, chunk_start, out=None, lse=None, stats=None, head_mask=None,
                dense=False):
@@ -82,14 +124,15 @@ class ChunkedSparsePrefill:
         `rows` is under the threshold get doubled budgets (capped at the
         number of keys), are re-estimated and re-attended; at most
         `max_rounds` rounds.  Raised budgets carry over to later chunks.
-        Returns the per-round head recalls (host tensors)."""
+        A-shape heads keep their fixed pattern.  Returns the per-round head
+        recalls (host tensors)."""
         c1 = chunk_start + q_chunk.shape[1]
         history = []
         for _ in range(max_rounds + 1):
             _, _, rec = self.recall(q_chunk, chunk_start, rows)
             mean = rec.mean(dim=1).cpu()
             history.append(mean)
-            low = [bool(mean[h] < threshold) and
+            low = [bool(mean[h] < threshold) and self.a_shape[h] is None and
                    (self.n_vert[h] < c1 or self.n_slash[h] < c1) for h in range(self.H)]
             if len(history) > max_rounds or not any(low):
                 break
@@ -118,9 +161,56 @@ class ChunkedSparsePrefill:
         N = q.shape[1]
         if out is None:
             out = torch.empty((self.H, N, self.D), dtype=torch.float32, device=self.device)
+        # the library writes lse as a dense [H, rows] block per call
+        part = None if lse is None else torch.empty((self.H, min(chunk_size, N)),
+                                                    dtype=torch.float32, device=self.device)
         for c0 in range(0, N, chunk_size):
             c1 = min(N, c0 + chunk_size)
+            lc = None if part is None else part[:, :c1 - c0]
+            if lc is not None and c1 - c0 < part.shape[1]:
+                lc = lc.contiguous()
             self.prefill_chunk(q[:, c0:c1], k[:, c0:c1], v[:, c0:c1], c0,
-                               out=out[:, c0:c1], lse=None if lse is None else lse[:, c0:c1],
-                               stats=stats)
+                               out=out[:, c0:c1], lse=lc, stats=stats)
+            if lse is not None:
+                lse[:, c0:c1].copy_(lc)
         return out
+
+
+def search_head_patterns(layer, q, chunks, candidates, rows):
+    """Offline per-head pattern search over a calibration prompt.
+
+    The layer's KV cache must already hold the prompt (append_kv for every
+    chunk).  For each candidate (a configuration as in set_head_patterns)
+    every head takes that candidate, each calibration chunk (c0, length) of
+    `chunks` gets its pattern (estimate or A-shape fill) and the attention
+    recall of its `rows` (row offsets within the chunk: one int32 device
+    tensor, or one per chunk); a head's score is its recall averaged over the
+    rows of a chunk, then over the chunks.  Each head takes the candidate
+    with the highest score, the earlier one on an exact tie.  The layer's own
+    configuration is restored afterwards.
+
+    Returns (choice: list of H candidate indices, scores: fp64 host tensor
+    [n_candidates, H]).
+    """
+    saved = (list(layer.n_vert), list(layer.n_slash), list(layer.a_shape))
+    H = layer.H
+    scores = torch.zeros(len(candidates), H, dtype=torch.float64)
+    try:
+        for ci, cand in enumerate(candidates):
+            layer.set_head_patterns([cand] * H)
+            for k, (c0, n) in enumerate(chunks):
+                r = rows[k] if isinstance(rows, (list, tuple)) else rows
+                layer.estimate(q[:, c0:c0 + n], c0)
+                _, _, rec = layer.recall(q[:, c0:c0 + n], c0, r)
+                scores[ci] += rec.double().mean(dim=1).cpu()
+            scores[ci] /= len(chunks)
+    finally:
+        layer.n_vert, layer.n_slash, layer.a_shape = saved
+    choice = []
+    for h in range(H):
+        best = 0
+        for c in range(1, len(candidates)):
+            if scores[c, h] > scores[best, h]:
+                best = c
+        choice.append(best)
+    return choice, scores

@@ -129,6 +129,16 @@ def _head_mask(mask, H):
     return _host_i32([bool(x) for x in mask])
 
 
+def _dense_rows(t, H, n, what):
+    """A per-(head, row) fp32 output must be one dense [H, n] block: the C
+    ABI takes it without strides."""
+    if t is None:
+        return None
+    if (t.dtype != torch.float32 or tuple(t.shape) != (H, n) or not t.is_contiguous()):
+        raise ValueError(f"{what} must be a contiguous float32 tensor of shape [{H}, {n}]")
+    return t.data_ptr()
+
+
 def _problem(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale):
     if q.dim() != 3 or k_cache.dim() != 3:
         raise ValueError("q is [H, L, D], caches are [H_kv, N, D]")
@@ -199,6 +209,18 @@ def dca_positions(tok_start, n_tok, dca, device, stream=None):
     return outs
 
 
+def pattern_fill_a_shape(pattern, n_sink, n_local, n_ctx, head_mask=None, stream=None):
+    """Write the A-shape (verticals 0 .. n_sink - 1, slashes 0 .. n_local - 1,
+    cut at n_ctx) into the rows of `pattern` selected by head_mask
+    (lcsr_pattern_fill_a_shape); other rows are left as they are."""
+    H = pattern.vert_cnt.shape[0]
+    hm = _head_mask(head_mask, H)
+    pat = pattern.c()
+    _check(C.load().lcsr_pattern_fill_a_shape(ctypes.byref(pat), H, _ptr(hm), int(n_sink),
+                                               int(n_local), int(n_ctx), _stream(stream)))
+    return pattern
+
+
 def vs_pattern_estimate(q, k_cache, chunk_start, rope, dca, sm_scale, n_vert, n_slash,
                         pattern, last_q=64, head_mask=None, vert_score=None,
                         slash_score=None, select_only=False, workspace=None, stream=None):
@@ -240,7 +262,7 @@ def vs_sparse_attn_prefill(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale
     hm = _head_mask(head_mask, H)
     _check(C.load().lcsr_vs_sparse_attn_prefill(
         ctypes.byref(prob), pat, _ptr(hm), out.data_ptr(), _dtype_code(out),
-        out.stride(0), out.stride(1), None if lse is None else lse.data_ptr(),
+        out.stride(0), out.stride(1), _dense_rows(lse, q.shape[0], q.shape[1], "lse"),
         None if stats is None else stats.data_ptr(), C.LCSR_ATTN_DENSE if dense else 0,
         ws.data_ptr(), ws.numel(), _stream(stream)))
     return out, lse
@@ -258,7 +280,7 @@ def attn_decode(q, k_cache, v_cache, row_start, rope, dca, sm_scale, out=None,
     ws = _workspace(C.LCSR_WS_DECODE, prob, 0, 0, q.device, workspace)
     _check(C.load().lcsr_attn_decode(
         ctypes.byref(prob), out.data_ptr(), _dtype_code(out), out.stride(0), out.stride(1),
-        None if lse is None else lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+        _dense_rows(lse, H, n, "lse"), ws.data_ptr(), ws.numel(), _stream(stream)))
     return out, lse
 
 
@@ -273,8 +295,8 @@ def attn_recall_check(q, k_cache, chunk_start, rope, dca, sm_scale, pattern, row
                     workspace)
     pat = pattern.c()
     hm = _head_mask(head_mask, H)
-    if rows.dtype != torch.int32:
-        raise TypeError("rows must be int32")
+    if rows.dtype != torch.int32 or not rows.is_contiguous():
+        raise TypeError("rows must be a contiguous int32 tensor")
     _check(C.load().lcsr_attn_recall_check(
         ctypes.byref(prob), ctypes.byref(pat), _ptr(hm), rows.data_ptr(), n,
         outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), ws.data_ptr(), ws.numel(),

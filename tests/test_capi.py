@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert set(names) == set(C.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -172,6 +172,28 @@ def test_decode_workspace_and_rejects(lib):
     assert attn(lib, q, pattern()) == C.LCSR_ENOTSUP
 
 
+def test_fill_a_shape_rejects(lib):
+    """Every rejection happens before a launch (nothing is written)."""
+    def fill(pat, n_heads=28, mask=None, n_sink=16, n_local=2048, n_ctx=65536):
+        return lib.lcsr_pattern_fill_a_shape(
+            None if pat is None else ctypes.byref(pat), n_heads, mask, n_sink, n_local, n_ctx,
+            None)
+
+    assert fill(None) == C.LCSR_EINVAL
+    assert fill(pattern(), n_heads=0) == C.LCSR_EINVAL
+    assert fill(pattern(), n_heads=65) == C.LCSR_EINVAL
+    assert fill(pattern(), n_sink=-1) == C.LCSR_EINVAL
+    assert fill(pattern(), n_ctx=-5) == C.LCSR_EINVAL
+    assert fill(pattern(max_vert=8), n_sink=9) == C.LCSR_EINVAL and "max_vert" in err(lib)
+    assert fill(pattern(max_slash=100), n_local=101) == C.LCSR_EINVAL
+    bad = pattern()
+    bad.slash_cnt = None
+    assert fill(bad) == C.LCSR_EINVAL
+    # a mask that selects no head launches nothing and succeeds
+    none = (ctypes.c_int32 * 28)()
+    assert fill(pattern(), mask=none) == C.LCSR_OK
+
+
 def test_rope_and_dca_reject(lib):
     rope = C.lcsr_rope_t(1e4, 1.0, 262144, 32.0, 1.0, 0)
     call = lib.lcsr_rope_yarn_apply
@@ -195,3 +217,16 @@ def test_rope_and_dca_reject(lib):
     dca = C.lcsr_dca_t(256, 64)
     assert lib.lcsr_dca_positions(0, -1, ctypes.byref(dca), FAKE, None, None, None,
                                   None) == C.LCSR_EINVAL
+
+
+def test_binding_checks_lse_layout():
+    """lse crosses the ABI without strides: the binding takes only a dense
+    float32 [H, rows] block (a column slice of a wider buffer is refused)."""
+    import torch
+    from long_context_sparse_rope_amd.ops import _dense_rows
+    whole = torch.zeros(4, 10)
+    assert _dense_rows(None, 4, 5, "lse") is None
+    assert _dense_rows(whole[:, :5].contiguous(), 4, 5, "lse") is not None
+    for bad in (whole[:, :5], whole, torch.zeros(4, 5, dtype=torch.float64)):
+        with pytest.raises(ValueError):
+            _dense_rows(bad, 4, 5, "lse")
