@@ -21,7 +21,8 @@ library primitives used).  Sources are cited by page and section:
 * [architecture overview] deepseekmodel.com long-context architecture page,
   §2.2 (PI / NTK / YaRN), §2.4 code (inv_freq, rotate_half convention),
   §3.2 (blocked attention with online softmax), §4.1 (attention sinks and
-  the sliding window), §4.2 (vertical-slash and the other head patterns).
+  the sliding window), §4.2 (vertical-slash and the other head patterns),
+  §4.3 (selection of whole key blocks).
 
 Pinned by the ``-m "not gpu"`` tests (brute force, closed forms, invariants).
 Readings taken where the pages are silent or garbled are stated next to the
@@ -39,6 +40,8 @@ from .attention import (KeyContext, attention_logits, dense_causal_rows,
 from .estimate import estimate_scores, select_top, select_pattern
 from .refine import refine_budgets
 from .patterns import a_shape_set, a_shape_lists, choose_candidates
+from .blocksparse import (BLOCK, block_scores, select_blocks, block_key_set,
+                          block_sparse_rows)
 
 __all__ = [
     "bf16_round", "bf16_round64", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",
