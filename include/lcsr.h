@@ -62,12 +62,15 @@ extern "C" {
 #define LCSR_ROPE_NO_ROTATE 0x2u  /* rope_yarn_apply: convert/scale only      */
 #define LCSR_EST_SELECT_ONLY 0x1u /* estimate: scores are inputs, select only */
 #define LCSR_ATTN_DENSE 0x1u      /* attention: every causal key (no pattern) */
+#define LCSR_BS_SELECT_ONLY 0x1u  /* block estimate: scores are inputs        */
 
 /* ---- workspace kinds --------------------------------------------------- */
 #define LCSR_WS_ESTIMATE 0
 #define LCSR_WS_ATTN 1
 #define LCSR_WS_RECALL 2
 #define LCSR_WS_DECODE 3
+#define LCSR_WS_BLOCK_EST 4
+#define LCSR_WS_BLOCK_ATTN 5
 
 /* Rotary embedding setup ([architecture overview] §2.4 code; YaRN from
  * [Qwen2.5-1M explainer] Length Extrapolation and [long-context blog]
@@ -187,6 +190,61 @@ int lcsr_pattern_fill_a_shape(const lcsr_pattern_t* pat, int32_t n_heads,
                               const int32_t* head_mask, int32_t n_sink, int32_t n_local,
                               int64_t n_ctx, void* stream);
 
+/* lcsr_block_sparse_estimate — the block-sparse head pattern of one prefill
+ * chunk.  [architecture overview] §4.2 lists a block pattern among the
+ * stable head patterns and §4.3 selectors that score whole key blocks per
+ * query; [Qwen2.5-1M explainer] アルゴリズム: selection at continuous
+ * positions.  Blocks are 64 tokens aligned to the token index; query block
+ * qb holds chunk rows [64 qb, 64 qb + 64) and its diagonal key block is
+ * diag = chunk_start / 64 + qb.
+ *   score[h][qb][kb] = sm_scale <mean_i R(i) q_i, mean_j R(j) k_j>   (kb <= diag)
+ * over the block's queries i and keys j (partial last blocks: the mean of
+ * the tokens present; keys are read from the K cache at P_k and turned to
+ * continuous positions).  Each query block keeps its diagonal and the
+ * k - 1 best key blocks kb < diag by (score desc, index asc), with
+ * k = min(n_blocks[h], diag + 1).
+ *   p            as for the other calls; chunk_start % 64 == 0; at most
+ *                32768 key blocks (2M keys); p->v_cache unused
+ *   n_blocks     (host) int32 [H], 1 .. max_blocks, kept blocks per query block
+ *   head_mask    (host) int32 [H] or NULL; other heads are not touched
+ *   blk_idx      int32 [H][n_qb][max_blocks], n_qb = ceil(chunk_len / 64):
+ *                kept key blocks ascending, -1 after the count
+ *   blk_cnt      int32 [H][n_qb]
+ *   scores       fp32 [H][n_qb][n_kb] (n_kb = ceil((chunk_start + chunk_len)
+ *                / 64)) or NULL: written with the scores at or below each
+ *                diagonal; with LCSR_BS_SELECT_ONLY an input (only the
+ *                selection runs)
+ *   ws           lcsr_workspace_bytes(LCSR_WS_BLOCK_EST, ...) bytes (not
+ *                needed with LCSR_BS_SELECT_ONLY)
+ * Asynchronous on `stream`.  Errors: LCSR_EINVAL (shapes, NULL arrays,
+ * budgets, chunk_start alignment), LCSR_ENOTSUP (head_dim, context beyond
+ * the block limit), LCSR_EWORKSPACE, LCSR_EHIP. */
+int lcsr_block_sparse_estimate(const lcsr_problem_t* p, const int32_t* n_blocks,
+                               const int32_t* head_mask, int32_t max_blocks, int32_t* blk_idx,
+                               int32_t* blk_cnt, float* scores, uint32_t flags, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* lcsr_block_sparse_attn_prefill — attention of the chunk's rows over their
+ * query block's kept key blocks: row i attends to every key j <= i inside a
+ * listed block, with the DCA logits and temperature of
+ * lcsr_vs_sparse_attn_prefill ([Qwen2.5-1M explainer] Length
+ * Extrapolation).  out_i = softmax over that set times V; lse_i natural
+ * log.  blk_idx / blk_cnt as written by lcsr_block_sparse_estimate (any
+ * ascending lists of distinct blocks <= each diagonal are accepted).
+ *   out      [H, chunk_len, D] with strides (o_stride_h, o_stride_t),
+ *            out_dtype LCSR_FP32 or LCSR_BF16
+ *   lse      fp32 [H, chunk_len] (dense) or NULL
+ *   stats    int64 [2] or NULL: adds (pairs multiplied on whole 64 x 32
+ *            tiles, pairs in the sets)
+ *   ws       lcsr_workspace_bytes(LCSR_WS_BLOCK_ATTN, ...) bytes
+ * Errors as for lcsr_block_sparse_estimate; LCSR_EINVAL also for a NULL or
+ * mistyped output. */
+int lcsr_block_sparse_attn_prefill(const lcsr_problem_t* p, const int32_t* blk_idx,
+                                   const int32_t* blk_cnt, int32_t max_blocks,
+                                   const int32_t* head_mask, void* out, int32_t out_dtype,
+                                   int64_t o_stride_h, int64_t o_stride_t, float* lse,
+                                   int64_t* stats, void* ws, size_t ws_bytes, void* stream);
+
 /* lcsr_dca_positions — DCA position maps of tokens [tok_start, tok_start +
  * n_tok) ([Qwen2.5-1M explainer] Length Extrapolation, see lcsr_dca_t).
  * Each output is int32 [n_tok] or NULL (not written).  With DCA off every
@@ -264,6 +322,21 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
 int lcsr_attn_decode(const lcsr_problem_t* p, void* out, int32_t out_dtype,
                      int64_t o_stride_h, int64_t o_stride_t, float* lse, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* lcsr_block_sparse_recall_check — attention recall of sampled rows for a
+ * block-sparse pattern ([Qwen2.5-1M explainer] Chunked Prefill), C_i being
+ * every key j <= i inside the kept blocks of i's query block (the set of
+ * lcsr_block_sparse_attn_prefill), same logits.  The blocks come from
+ * blk_idx / blk_cnt as written by lcsr_block_sparse_estimate; entries
+ * outside [0, the row's block] are ignored.
+ *   rows       int32 [n_rows], offsets within the chunk
+ *   lse_full, lse_sparse, recall   fp32 [H, n_rows]
+ * No workspace.  Errors: LCSR_EINVAL, LCSR_ENOTSUP, LCSR_EHIP. */
+int lcsr_block_sparse_recall_check(const lcsr_problem_t* p, const int32_t* blk_idx,
+                                   const int32_t* blk_cnt, int32_t max_blocks,
+                                   const int32_t* head_mask, const int32_t* rows,
+                                   int32_t n_rows, float* lse_full, float* lse_sparse,
+                                   float* recall, void* stream);
 
 /* lcsr_attn_recall_check — attention recall of sampled rows
  * ([Qwen2.5-1M explainer] Chunked Prefill: lse_full over every j <= i,

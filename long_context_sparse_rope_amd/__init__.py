@@ -10,7 +10,8 @@ from . import _capi
 from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, yarn_softmax_scale,
                   rope_yarn_apply, dca_positions, vs_pattern_estimate,
                   vs_sparse_attn_prefill, attn_decode, attn_recall_check, workspace_bytes,
-                  pattern_fill_a_shape)
+                  pattern_fill_a_shape, BlockPattern, block_sparse_estimate,
+                  block_sparse_attn_prefill, block_sparse_recall_check)
 from .driver import ChunkedSparsePrefill, search_head_patterns
 
 _capi.load()
@@ -18,4 +19,6 @@ _capi.load()
 __all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "yarn_softmax_scale",
            "rope_yarn_apply", "dca_positions", "vs_pattern_estimate",
            "vs_sparse_attn_prefill", "attn_decode", "attn_recall_check", "workspace_bytes",
-           "pattern_fill_a_shape", "ChunkedSparsePrefill", "search_head_patterns"]
+           "pattern_fill_a_shape", "BlockPattern", "block_sparse_estimate",
+           "block_sparse_attn_prefill", "block_sparse_recall_check", "ChunkedSparsePrefill",
+           "search_head_patterns"]

@@ -18,16 +18,20 @@ LCSR_ROPE_YARN_FREQ = 0x1
 LCSR_ROPE_NO_ROTATE = 0x2
 LCSR_EST_SELECT_ONLY = 0x1
 LCSR_ATTN_DENSE = 0x1
+LCSR_BS_SELECT_ONLY = 0x1
 
 LCSR_WS_ESTIMATE = 0
 LCSR_WS_ATTN = 1
 LCSR_WS_RECALL = 2
 LCSR_WS_DECODE = 3
+LCSR_WS_BLOCK_EST = 4
+LCSR_WS_BLOCK_ATTN = 5
 
 EXPORTED = ("lcsr_workspace_bytes", "lcsr_last_error", "lcsr_rope_yarn_apply",
             "lcsr_dca_positions", "lcsr_vs_pattern_estimate",
             "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_recall_check",
-            "lcsr_pattern_fill_a_shape")
+            "lcsr_pattern_fill_a_shape", "lcsr_block_sparse_estimate",
+            "lcsr_block_sparse_attn_prefill", "lcsr_block_sparse_recall_check")
 
 
 class lcsr_rope_t(ctypes.Structure):
@@ -86,6 +90,15 @@ def load():
                                          P(lcsr_rope_t), f32, u32, vp]
     lib.lcsr_dca_positions.restype = ctypes.c_int
     lib.lcsr_dca_positions.argtypes = [i64, i64, P(lcsr_dca_t), vp, vp, vp, vp, vp]
+    lib.lcsr_block_sparse_estimate.restype = ctypes.c_int
+    lib.lcsr_block_sparse_estimate.argtypes = [P(lcsr_problem_t), vp, vp, i32, vp, vp, vp, u32,
+                                               vp, ctypes.c_size_t, vp]
+    lib.lcsr_block_sparse_attn_prefill.restype = ctypes.c_int
+    lib.lcsr_block_sparse_attn_prefill.argtypes = [P(lcsr_problem_t), vp, vp, i32, vp, vp, i32,
+                                                   i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.lcsr_block_sparse_recall_check.restype = ctypes.c_int
+    lib.lcsr_block_sparse_recall_check.argtypes = [P(lcsr_problem_t), vp, vp, i32, vp, vp, i32,
+                                                   vp, vp, vp, vp]
     lib.lcsr_pattern_fill_a_shape.restype = ctypes.c_int
     lib.lcsr_pattern_fill_a_shape.argtypes = [P(lcsr_pattern_t), i32, vp, i32, i32, i64, vp]
     lib.lcsr_vs_pattern_estimate.restype = ctypes.c_int

@@ -209,6 +209,8 @@ size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert
     case LCSR_WS_ATTN: return attn_layout(*p, max_vert, max_slash, true).total;
     case LCSR_WS_RECALL: return attn_layout(*p, max_vert, max_slash, false).total;
     case LCSR_WS_DECODE: return decode_layout(*p).total;
+    case LCSR_WS_BLOCK_EST: return block_layout(*p).est_total;
+    case LCSR_WS_BLOCK_ATTN: return block_layout(*p).attn_total;
     default: set_error("unknown workspace kind %d", which); return 0;
   }
 }
@@ -352,6 +354,72 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
                        static_cast<char*>(ws), static_cast<hipStream_t>(stream));
 }
 
+static int validate_blocks(const lcsr_problem_t* p, int32_t max_blocks) {
+  if (p->chunk_start % 64)
+    return fail(LCSR_EINVAL, "block-sparse calls need chunk_start %% 64 == 0");
+  if (max_blocks < 1) return fail(LCSR_EINVAL, "max_blocks must be >= 1");
+  const int64_t n_kb = (p->chunk_start + p->chunk_len + 63) / 64;
+  if (n_kb > kMaxKeyBlocks)
+    return fail(LCSR_ENOTSUP, "block-sparse context limited to %d key blocks of 64",
+                kMaxKeyBlocks);
+  return LCSR_OK;
+}
+
+int lcsr_block_sparse_estimate(const lcsr_problem_t* p, const int32_t* n_blocks,
+                               const int32_t* head_mask, int32_t max_blocks, int32_t* blk_idx,
+                               int32_t* blk_cnt, float* scores, uint32_t flags, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc = validate_problem(p, false);
+  if (rc) return rc;
+  rc = validate_blocks(p, max_blocks);
+  if (rc) return rc;
+  if (!blk_idx || !blk_cnt) return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
+  if (!n_blocks) return fail(LCSR_EINVAL, "n_blocks is NULL");
+  const bool select_only = flags & LCSR_BS_SELECT_ONLY;
+  if (select_only && !scores) return fail(LCSR_EINVAL, "LCSR_BS_SELECT_ONLY needs the scores");
+  uint64_t hm;
+  head_mask_bits(p, head_mask, &hm);
+  for (int h = 0; h < p->n_heads; ++h)
+    if (((hm >> h) & 1ull) && (n_blocks[h] < 1 || n_blocks[h] > max_blocks))
+      return fail(LCSR_EINVAL, "n_blocks[%d] = %d outside [1, max_blocks %d]", h, n_blocks[h],
+                  max_blocks);
+  const BlockLayout L = block_layout(*p);
+  const size_t need = select_only ? 0 : (scores ? L.o_scores : L.est_total);
+  if (need && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(LCSR_EWORKSPACE, "block estimate needs %zu workspace bytes (16-byte aligned), "
+                "got %zu", need, ws_bytes);
+  if (p->chunk_len == 0) return LCSR_OK;
+  return run_block_estimate(*p, n_blocks, hm, max_blocks, blk_idx, blk_cnt, scores, select_only,
+                            static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int lcsr_block_sparse_attn_prefill(const lcsr_problem_t* p, const int32_t* blk_idx,
+                                   const int32_t* blk_cnt, int32_t max_blocks,
+                                   const int32_t* head_mask, void* out, int32_t out_dtype,
+                                   int64_t o_stride_h, int64_t o_stride_t, float* lse,
+                                   int64_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_problem(p, true);
+  if (rc) return rc;
+  rc = validate_blocks(p, max_blocks);
+  if (rc) return rc;
+  if (!blk_idx || !blk_cnt) return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
+  if (!out) return fail(LCSR_EINVAL, "out must not be NULL");
+  if (out_dtype != LCSR_FP32 && out_dtype != LCSR_BF16)
+    return fail(LCSR_EINVAL, "out_dtype must be LCSR_FP32 or LCSR_BF16");
+  if (o_stride_t < p->head_dim || o_stride_h < p->head_dim)
+    return fail(LCSR_EINVAL, "output strides must be >= head_dim");
+  uint64_t hm;
+  head_mask_bits(p, head_mask, &hm);
+  const BlockLayout L = block_layout(*p);
+  if (!ws || ws_bytes < L.attn_total || !aligned16(ws))
+    return fail(LCSR_EWORKSPACE, "block attention needs %zu workspace bytes (16-byte aligned), "
+                "got %zu", L.attn_total, ws_bytes);
+  if (p->chunk_len == 0) return LCSR_OK;
+  return run_block_attention(*p, blk_idx, blk_cnt, max_blocks, hm, out, out_dtype, o_stride_h,
+                             o_stride_t, lse, stats, static_cast<char*>(ws),
+                             static_cast<hipStream_t>(stream));
+}
+
 int lcsr_attn_decode(const lcsr_problem_t* p, void* out, int32_t out_dtype,
                      int64_t o_stride_h, int64_t o_stride_t, float* lse, void* ws,
                      size_t ws_bytes, void* stream) {
@@ -395,6 +463,26 @@ int lcsr_attn_recall_check(const lcsr_problem_t* p, const lcsr_pattern_t* pat,
   if (n_rows == 0 || p->chunk_len == 0) return LCSR_OK;
   return run_recall(*p, *pat, hm, rows, n_rows, lse_full, lse_sparse, recall,
                     static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int lcsr_block_sparse_recall_check(const lcsr_problem_t* p, const int32_t* blk_idx,
+                                   const int32_t* blk_cnt, int32_t max_blocks,
+                                   const int32_t* head_mask, const int32_t* rows,
+                                   int32_t n_rows, float* lse_full, float* lse_sparse,
+                                   float* recall, void* stream) {
+  int rc = validate_problem(p, false);
+  if (rc) return rc;
+  rc = validate_blocks(p, max_blocks);
+  if (rc) return rc;
+  if (!blk_idx || !blk_cnt) return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
+  if (n_rows < 0) return fail(LCSR_EINVAL, "n_rows must be >= 0");
+  if (n_rows > 0 && (!rows || !lse_full || !lse_sparse || !recall))
+    return fail(LCSR_EINVAL, "rows and the three outputs must be non-NULL");
+  uint64_t hm;
+  head_mask_bits(p, head_mask, &hm);
+  if (n_rows == 0 || p->chunk_len == 0) return LCSR_OK;
+  return run_block_recall(*p, blk_idx, blk_cnt, max_blocks, hm, rows, n_rows, lse_full,
+                          lse_sparse, recall, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1419,6 +1419,184 @@ __global__ void __launch_bounds__(256) decode_combine(DecArgs a, void* out, int3
   if (lse && tid == 0) lse[(int64_t)h * a.n_q + r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// ------------------------------------------------------------ block sparse
+// Attention over whole 64-key blocks: row block rb (32 rows) of head h
+// attends to the key blocks listed for its 64-row query block, causally
+// inside the diagonal block.  The same three-wave scheme as the decode step:
+// wave 1 streams the K tiles and wave 2 the V tiles of the list into a ring
+// of kStages stages, wave 0 multiplies.  A 32-row block lies inside one DCA
+// chunk (the period and the chunk start are multiples of 64), so the query
+// variant changes only with the tile's key chunk.
+struct BsArgs {
+  const uint16_t* __restrict__ q_rot;  // [n_var][H][L][D]
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  int64_t kv_sh, kv_st;
+  int32_t H, G, n_var, max_blocks;
+  int64_t c0, L, n_ctx, period, n_qb;
+  const int32_t* blk_idx;  // [H][n_qb][max_blocks]
+  const int32_t* blk_cnt;  // [H][n_qb]
+  uint64_t head_mask;
+  float scale_log2;
+  void* out;
+  int32_t out_dtype;
+  int64_t o_sh, o_st;
+  float* lse;
+  unsigned long long* stats;  // [2]: (executed, selected) pairs
+};
+
+template <int M, int S>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  // `ahead` tiles after the one that must have landed are still allowed in
+  // flight (at most S - 2)
+  if (S >= 5 && ahead >= 3) wait_vm<3 * M>();
+  else if (S >= 4 && ahead >= 2) wait_vm<2 * M>();
+  else if (S >= 3 && ahead >= 1) wait_vm<M>();
+  else wait_vm<0>();
+}
+
+template <int D, int kStages>
+__global__ void __launch_bounds__(192) bs_attn_kernel(BsArgs a) {
+  using B = Buf<D>;
+  constexpr int M = B::kInstrPerMat;
+  constexpr int R = B::kRowsPerInstr;
+  constexpr int kStageBytes = 2 * B::kKBytes;
+  __shared__ __attribute__((aligned(16))) char stage[kStages][kStageBytes];
+  const int rb = blockIdx.x, h = blockIdx.y;
+  if (!((a.head_mask >> h) & 1ull)) return;
+  const int g = h / a.G;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int64_t qb = rb >> 1;
+  const int32_t* list = a.blk_idx + ((int64_t)h * a.n_qb + qb) * a.max_blocks;
+  const int cnt_in = __builtin_amdgcn_readfirstlane(a.blk_cnt[(int64_t)h * a.n_qb + qb]);
+  const int n_local = cnt_in < a.max_blocks ? cnt_in : a.max_blocks;
+  // a listed block outside [0, diagonal] is taken as the diagonal: no load
+  // leaves the keys the chunk can see, whatever the lists hold
+  const int32_t diag = (int32_t)(a.c0 / kTileK + qb);
+  auto tile_of = [&](int i) {
+    int32_t kb = __builtin_amdgcn_readfirstlane(list[i]);
+    kb = kb < 0 || kb > diag ? diag : kb;
+    Tile x;
+    x.ks = kb * kTileK;
+    x.n = (int32_t)(a.n_ctx - x.ks < kTileK ? a.n_ctx - x.ks : kTileK);
+    x.wave = -1;
+    x.kchunk = a.period ? (int32_t)(x.ks / a.period) : 0;
+    x.kmax = x.ks + x.n - 1;
+    x.gran = 15;
+    return x;
+  };
+  if (w > 0) {
+    const bool isv = w == 2;
+    const char* src = reinterpret_cast<const char*>((isv ? a.v : a.k) + (int64_t)g * a.kv_sh);
+    const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+    const uint32_t base = lds_addr(&stage[0][0]) + (isv ? B::kKBytes : 0);
+    const int sub = lane / B::kChunks, cl = lane % B::kChunks;
+    auto issue = [&](int i) {
+      const Tile x = tile_of(i);
+      const char* sb = src + (int64_t)x.ks * kvst_b;
+      const uint32_t dst = base + (uint32_t)((i % kStages) * kStageBytes);
+#pragma unroll
+      for (int gm = 0; gm < M; ++gm) {
+        const int row = gm * R + sub;
+        const uint32_t rr = (uint32_t)(row < x.n ? row : x.n - 1);
+        const int chunk = isv ? swz_v<D>(cl, row) : swz_k<D>(cl, row);
+        dma16_s(sb, rr * kvst_b + (uint32_t)chunk * 16u, dst + gm * 1024);
+      }
+    };
+    for (int i = 0; i < kStages - 1 && i < n_local; ++i) issue(i);
+    for (int i = 0; i < n_local; ++i) {
+      const int ahead = n_local - 1 - i;
+      wait_tiles_ahead<M, kStages>(ahead);
+      step_barrier();
+      if (i + kStages - 1 < n_local) issue(i + kStages - 1);
+    }
+    return;
+  }
+  // ---------------- wave 0: the products; lane rows rho = lane & 31
+  const int rho = lane & 31;
+  const int64_t row = a.c0 + (int64_t)rb * kRowBlock + rho;
+  const bool live = row < a.c0 + a.L;
+  const int64_t my_row = live ? row : a.c0 + a.L - 1;
+  const int64_t qchunk = a.period ? my_row / a.period : 0;
+  LaneConst<D> lc;
+  lane_consts<D>(lc, lane);
+  WaveState<D> st;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.o[db] = (f32x16){};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  int cur_var = -1;
+  unsigned long long sel = 0;
+  for (int i = 0; i < n_local; ++i) {
+    step_barrier();
+    const Tile tt = tile_of(i);
+    const int64_t rel = qchunk - tt.kchunk;
+    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (int)rel);
+    if (__ballot(var != cur_var) != 0ull) {
+      const uint16_t* qp =
+          a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const bf16x8*>(qp + s2 * 16);
+      wait_vm<0>();
+      cur_var = var;
+    }
+    const int64_t lim = my_row - tt.ks + 1;
+    const uint64_t mword = low_bits(lim < tt.n ? lim : tt.n);
+    if (live && half == 0) sel += __popcll(mword);
+    const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+    const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+    const bool masked = __ballot(mword == ~0ull) != ~0ull;
+    const char* bc = stage[i % kStages];
+    bf16x8 pf[4];
+    wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
+    wave_pv<D>(bc, lc, st, pf, act0, act1);
+  }
+  const float l_tot = sum_halves(st.l);
+  if (live) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t tr = row - a.c0;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * half;
+        const float v0 = st.o[db][4 * i4 + 0] * inv, v1 = st.o[db][4 * i4 + 1] * inv;
+        const float v2 = st.o[db][4 * i4 + 2] * inv, v3 = st.o[db][4 * i4 + 3] * inv;
+        if (a.out_dtype == LCSR_FP32) {
+          float* o = static_cast<float*>(a.out) + h * a.o_sh + tr * a.o_st + d;
+          o[0] = v0;
+          o[1] = v1;
+          o[2] = v2;
+          o[3] = v3;
+        } else {
+          uint16_t* o = static_cast<uint16_t*>(a.out) + h * a.o_sh + tr * a.o_st + d;
+          o[0] = f32_to_bf16(v0);
+          o[1] = f32_to_bf16(v1);
+          o[2] = f32_to_bf16(v2);
+          o[3] = f32_to_bf16(v3);
+        }
+      }
+    if (a.lse && half == 0)
+      a.lse[(int64_t)h * a.L + tr] = l_tot > 0.f ? (st.m + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  if (a.stats) {
+    unsigned long long se = sel;
+    for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
+    if (lane == 0) {
+      atomicAdd(&a.stats[0], (unsigned long long)n_local * 32ull * kTileK);
+      atomicAdd(&a.stats[1], se);
+    }
+  }
+}
+
+template <int D>
+int launch_block_attn(const BsArgs& a, int64_t n_rb, hipStream_t s) {
+  hipLaunchKernelGGL((bs_attn_kernel<D, 4>), dim3((unsigned)n_rb, (unsigned)a.H), dim3(192), 0,
+                     s, a);
+  return check_launch("block-sparse attention");
+}
+
 template <int D>
 int launch_decode(const DecArgs& a, void* out, int32_t out_dtype, int64_t o_sh, int64_t o_st,
                   float* lse, int n_kv, hipStream_t s) {
@@ -1581,6 +1759,48 @@ int run_decode(const lcsr_problem_t& p, void* out, int32_t out_dtype, int64_t o_
   a.part_ml = reinterpret_cast<float*>(ws + L.o_part_ml);
   if (p.head_dim == 128) return launch_decode<128>(a, out, out_dtype, o_sh, o_st, lse, p.n_kv_heads, s);
   return launch_decode<64>(a, out, out_dtype, o_sh, o_st, lse, p.n_kv_heads, s);
+}
+
+int run_block_attention(const lcsr_problem_t& p, const int32_t* idx, const int32_t* cnt,
+                        int32_t max_blocks, uint64_t head_mask, void* out, int32_t out_dtype,
+                        int64_t o_sh, int64_t o_st, float* lse, int64_t* stats, char* ws,
+                        hipStream_t s) {
+  const BlockLayout L = block_layout(p);
+  if (p.chunk_len == 0 || !head_mask) return LCSR_OK;
+  FreqTable ft;
+  int rc = build_freq_table(&p.rope, p.head_dim, &ft);
+  if (rc) return rc;
+  const DcaParams d = make_dca(&p.dca);
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(ws + L.o_q_rot);
+  rc = launch_rotate_q_variants(p, ft, d, q_rot, (int)L.n_var, s);
+  if (rc) return rc;
+  BsArgs a{};
+  a.q_rot = q_rot;
+  a.k = static_cast<const uint16_t*>(p.k_cache);
+  a.v = static_cast<const uint16_t*>(p.v_cache);
+  a.kv_sh = p.kv_stride_h;
+  a.kv_st = p.kv_stride_t;
+  a.H = p.n_heads;
+  a.G = p.n_heads / p.n_kv_heads;
+  a.n_var = (int32_t)L.n_var;
+  a.max_blocks = max_blocks;
+  a.c0 = p.chunk_start;
+  a.L = p.chunk_len;
+  a.n_ctx = L.n_ctx;
+  a.period = d.period;
+  a.n_qb = L.n_qb;
+  a.blk_idx = idx;
+  a.blk_cnt = cnt;
+  a.head_mask = head_mask;
+  a.scale_log2 = p.sm_scale * kLog2e;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.o_sh = o_sh;
+  a.o_st = o_st;
+  a.lse = lse;
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  const int64_t n_rb = (p.chunk_len + kRowBlock - 1) / kRowBlock;
+  return p.head_dim == 128 ? launch_block_attn<128>(a, n_rb, s) : launch_block_attn<64>(a, n_rb, s);
 }
 
 }  // namespace lcsr

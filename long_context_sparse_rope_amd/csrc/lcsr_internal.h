@@ -34,6 +34,7 @@ constexpr int kMaxAttnWaves = 7;         // query heads per attention workgroup 
 constexpr int kEstRows = 64;             // largest last_q
 constexpr int kBitPad = 8;               // zero words before and after each head's bitmap
 constexpr int kMaxDecSplit = 256;        // key splits of the decode step per KV head
+constexpr int kMaxKeyBlocks = 32768;     // 64-key blocks of a block-sparse context (2M keys)
 
 // fp64 inverse frequencies, built on the host from lcsr_rope_t.
 struct FreqTable {
@@ -159,6 +160,14 @@ struct DecodeLayout {
   int64_t n_ctx, n_tiles, n_var, n_split;
   size_t o_q_rot, o_part_o, o_part_ml, total;
 };
+// Block-sparse pattern: 64-token blocks; estimate workspace (pooled keys,
+// pooled query variants, scores) and attention workspace (rotated queries).
+struct BlockLayout {
+  int64_t n_ctx, n_qb, n_kb, n_kc, n_var;
+  size_t o_pk, o_pq, o_scores, est_total;
+  size_t o_q_rot, attn_total;
+};
+BlockLayout block_layout(const lcsr_problem_t& p);
 EstimateLayout estimate_layout(const lcsr_problem_t& p);
 DecodeLayout decode_layout(const lcsr_problem_t& p);
 AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_slash,
@@ -194,6 +203,20 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat,
                   uint64_t head_mask, void* out, int32_t out_dtype,
                   int64_t o_sh, int64_t o_st, float* lse, int64_t* stats,
                   bool dense, char* ws, hipStream_t s);
+
+int run_block_estimate(const lcsr_problem_t& p, const int32_t* budgets_host, uint64_t head_mask,
+                       int32_t max_blocks, int32_t* idx, int32_t* cnt, float* scores,
+                       bool select_only, char* ws, hipStream_t s);
+
+int run_block_attention(const lcsr_problem_t& p, const int32_t* idx, const int32_t* cnt,
+                        int32_t max_blocks, uint64_t head_mask, void* out, int32_t out_dtype,
+                        int64_t o_sh, int64_t o_st, float* lse, int64_t* stats, char* ws,
+                        hipStream_t s);
+
+int run_block_recall(const lcsr_problem_t& p, const int32_t* idx, const int32_t* cnt,
+                     int32_t max_blocks, uint64_t head_mask, const int32_t* rows,
+                     int32_t n_rows, float* lse_full, float* lse_sparse, float* recall,
+                     hipStream_t s);
 
 int run_decode(const lcsr_problem_t& p, void* out, int32_t out_dtype, int64_t o_sh,
                int64_t o_st, float* lse, char* ws, hipStream_t s);

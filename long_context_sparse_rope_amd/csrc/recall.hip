@@ -34,6 +34,12 @@ struct RecallArgs {
   uint64_t head_mask;
   const int32_t* rows;
   int32_t n_rows;
+  // block-sparse sets instead of the bitmaps (blk_idx != nullptr): the kept
+  // 64-key blocks of each (head, 64-row query block)
+  const int32_t* blk_idx;
+  const int32_t* blk_cnt;
+  int32_t max_blocks;
+  int64_t n_qb;
   float* lse_full;
   float* lse_sparse;
   float* recall;
@@ -55,6 +61,7 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
   if (!((a.head_mask >> h) & 1)) return;
   __shared__ float qv[3][128];
   __shared__ float red[4][kRecallThreads / 64];
+  __shared__ uint32_t kept[kMaxKeyBlocks / 32];
   const int64_t out_i = (int64_t)h * a.n_rows + k;
   const int32_t t = a.rows[k];
   if (t < 0 || t >= a.L) {  // row outside the chunk: NaN results
@@ -88,6 +95,23 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
     qv[v][p] = bf16_to_f32(f32_to_bf16(x1 * c - x2 * s));
     qv[v][p + half] = bf16_to_f32(f32_to_bf16(x2 * c + x1 * s));
   }
+  const bool blocks = a.blk_idx != nullptr;
+  if (blocks) {
+    // this row's kept key blocks as a bitmap (blocks past the diagonal or
+    // negative are ignored, like the attention kernel's guard keeps loads in
+    // bounds; they hold no key j <= i)
+    const int64_t nw = (i / 64) / 32 + 1;
+    for (int64_t x = threadIdx.x; x < nw; x += kRecallThreads) kept[x] = 0u;
+    __syncthreads();
+    const int64_t qb = t / 64;
+    const int32_t* list = a.blk_idx + ((int64_t)h * a.n_qb + qb) * a.max_blocks;
+    int n = a.blk_cnt[(int64_t)h * a.n_qb + qb];
+    n = n < a.max_blocks ? n : a.max_blocks;
+    for (int x = threadIdx.x; x < n; x += kRecallThreads) {
+      const int32_t b = list[x];
+      if (b >= 0 && b <= i / 64) atomicOr(&kept[b >> 5], 1u << (b & 31));
+    }
+  }
   __syncthreads();
   const int g = h / a.G;
   const uint16_t* kb = a.k + (int64_t)g * a.kv_sh;
@@ -111,7 +135,9 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
     }
     const float x = dot * a.scale_log2;
     lse_merge(mf, lf, x, 1.f);
-    if (bit_at(cb, j) || bit_at(ob, i - j)) lse_merge(ms, ls, x, 1.f);
+    const bool in_set = blocks ? ((kept[j >> 11] >> ((j >> 6) & 31)) & 1u)
+                               : (bit_at(cb, j) || bit_at(ob, i - j));
+    if (in_set) lse_merge(ms, ls, x, 1.f);
   }
   // block reduction in a fixed order
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -178,6 +204,43 @@ int run_recall(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head
   hipLaunchKernelGGL(recall_kernel, dim3((unsigned)n_rows, (unsigned)p.n_heads),
                      dim3(kRecallThreads), 0, s, a);
   return check_launch("recall");
+}
+
+int run_block_recall(const lcsr_problem_t& p, const int32_t* idx, const int32_t* cnt,
+                     int32_t max_blocks, uint64_t head_mask, const int32_t* rows,
+                     int32_t n_rows, float* lse_full, float* lse_sparse, float* recall,
+                     hipStream_t s) {
+  RecallArgs a{};
+  int rc = build_freq_table(&p.rope, p.head_dim, &a.ft);
+  if (rc) return rc;
+  a.q = p.q;
+  a.q_dtype = p.q_dtype;
+  a.q_sh = p.q_stride_h;
+  a.q_st = p.q_stride_t;
+  a.k = static_cast<const uint16_t*>(p.k_cache);
+  a.kv_sh = p.kv_stride_h;
+  a.kv_st = p.kv_stride_t;
+  a.H = p.n_heads;
+  a.G = p.n_heads / p.n_kv_heads;
+  a.D = p.head_dim;
+  a.c0 = p.chunk_start;
+  a.L = p.chunk_len;
+  a.n_ctx = p.chunk_start + p.chunk_len;
+  a.dca = make_dca(&p.dca);
+  a.scale_log2 = p.sm_scale * kLog2e;
+  a.head_mask = head_mask;
+  a.rows = rows;
+  a.n_rows = n_rows;
+  a.lse_full = lse_full;
+  a.lse_sparse = lse_sparse;
+  a.recall = recall;
+  a.blk_idx = idx;
+  a.blk_cnt = cnt;
+  a.max_blocks = max_blocks;
+  a.n_qb = (p.chunk_len + 63) / 64;
+  hipLaunchKernelGGL(recall_kernel, dim3((unsigned)n_rows, (unsigned)p.n_heads),
+                     dim3(kRecallThreads), 0, s, a);
+  return check_launch("block recall");
 }
 
 }  // namespace lcsr

@@ -9,8 +9,9 @@ and the attention-recall check used by the refinement.
 
 Heads may also carry a fixed A-shape pattern (attention sinks plus a recent
 window, the page deepseekmodel.com long-context architecture overview, §4.1)
-instead of an estimated vertical-slash one; §4.2 there gives each head one
-pattern.  `search_head_patterns` is the offline per-head search of the
+or a block-sparse one (whole 64-key blocks chosen per 64-query block, §4.2 and
+§4.3 there) instead of an estimated vertical-slash one; §4.2 gives each head
+one pattern.  `search_head_patterns` is the offline per-head search of the
 0h-n0.github.io page, section 疎アテンション, scored by attention recall
 (section Chunked Prefill).
 
@@ -28,9 +29,10 @@ class ChunkedSparsePrefill:
 
     K and V caches are bf16 [H_kv, max_ctx, D]; keys are stored rotated at
     their DCA key position.  Budgets are per query head and may be raised by
-    `refine_chunk`.  A head is either a vertical-slash head (budgets n_vert,
-    n_slash, pattern from the estimate) or an A-shape head (n_sink, n_local,
-    no estimate); see `set_head_patterns`.
+    `refine_chunk`.  A head is a vertical-slash head (budgets n_vert,
+    n_slash, pattern from the estimate), an A-shape head (n_sink, n_local, no
+    estimate) or a block-sparse head (n_blocks key blocks per query block);
+    see `set_head_patterns`.
     """
 
     def __init__(self, n_heads, n_kv_heads, head_dim, max_ctx, rope, dca, sm_scale,
@@ -43,6 +45,8 @@ class ChunkedSparsePrefill:
         self.n_vert = [int(n_vert)] * n_heads if isinstance(n_vert, int) else list(n_vert)
         self.n_slash = [int(n_slash)] * n_heads if isinstance(n_slash, int) else list(n_slash)
         self.a_shape = [None] * n_heads      # (n_sink, n_local) of A-shape heads
+        self.blocks = [None] * n_heads       # n_blocks of block-sparse heads
+        self.block_pattern = None
         self.k_cache = torch.empty((n_kv_heads, self.max_ctx, head_dim), dtype=torch.bfloat16,
                                    device=self.device)
         self.v_cache = torch.empty_like(self.k_cache)
@@ -61,16 +65,18 @@ class ChunkedSparsePrefill:
 
     def set_head_patterns(self, configs):
         """One configuration per query head: {"kind": "vs", "n_vert": a,
-        "n_slash": b} or {"kind": "a_shape", "n_sink": s, "n_local": w}.
-        The pattern buffers grow to fit."""
+        "n_slash": b}, {"kind": "a_shape", "n_sink": s, "n_local": w} or
+        {"kind": "block", "n_blocks": k}.  The pattern buffers grow to fit."""
         if len(configs) != self.H:
             raise ValueError("one configuration per query head")
         for h, c in enumerate(configs):
             if c["kind"] == "vs":
                 self.n_vert[h], self.n_slash[h] = int(c["n_vert"]), int(c["n_slash"])
-                self.a_shape[h] = None
+                self.a_shape[h], self.blocks[h] = None, None
             elif c["kind"] == "a_shape":
-                self.a_shape[h] = (int(c["n_sink"]), int(c["n_local"]))
+                self.a_shape[h], self.blocks[h] = (int(c["n_sink"]), int(c["n_local"])), None
+            elif c["kind"] == "block":
+                self.a_shape[h], self.blocks[h] = None, int(c["n_blocks"])
             else:
                 raise ValueError(f"unknown pattern kind {c['kind']!r}")
         mv = max(self.n_vert + [a[0] for a in self.a_shape if a])
@@ -84,7 +90,8 @@ class ChunkedSparsePrefill:
         A-shape rows for the others (only heads in head_mask, if given)."""
         c1 = chunk_start + q_chunk.shape[1]
         sel = [head_mask is None or bool(head_mask[h]) for h in range(self.H)]
-        vs = [sel[h] and self.a_shape[h] is None for h in range(self.H)]
+        blk = [sel[h] and self.blocks[h] is not None for h in range(self.H)]
+        vs = [sel[h] and self.a_shape[h] is None and not blk[h] for h in range(self.H)]
         if any(vs):
             ops.vs_pattern_estimate(
                 q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
@@ -95,21 +102,66 @@ class ChunkedSparsePrefill:
             ops.pattern_fill_a_shape(self.pattern, size[0], size[1], c1,
                                      head_mask=[sel[h] and self.a_shape[h] == size
                                                 for h in range(self.H)])
+        if any(blk):
+            n_qb = -(-q_chunk.shape[1] // 64)
+            mb = max(b for b in self.blocks if b is not None)
+            bp = self.block_pattern
+            if bp is None or bp.idx.shape[1] != n_qb or bp.max_blocks < mb:
+                self.block_pattern = ops.BlockPattern(self.H, n_qb, mb, self.device)
+            ops.block_sparse_estimate(
+                q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
+                [b or 1 for b in self.blocks], self.block_pattern, head_mask=blk)
         return self.pattern
 
     def attend(self, q_chunk, chunk_start, out=None, lse=None, stats=None, head_mask=None,
                dense=False):
+        """The chunk's attention: one call for the vertical-slash and A-shape
+        heads, one for the block-sparse heads, each on its own heads."""
         c1 = chunk_start + q_chunk.shape[1]
-        return ops.vs_sparse_attn_prefill(
+        sel = [head_mask is None or bool(head_mask[h]) for h in range(self.H)]
+        blk = [sel[h] and self.blocks[h] is not None and not dense for h in range(self.H)]
+        rest = [sel[h] and not blk[h] for h in range(self.H)]
+        if not any(blk):
+            return ops.vs_sparse_attn_prefill(
+                q_chunk, self.k_cache[:, :c1], self.v_cache[:, :c1], chunk_start, self.rope,
+                self.dca, self.sm_scale, None if dense else self.pattern, out=out, lse=lse,
+                stats=stats, head_mask=head_mask, dense=dense)
+        if out is None:
+            out = torch.empty((self.H, q_chunk.shape[1], self.D), dtype=torch.float32,
+                              device=self.device)
+        if any(rest):
+            ops.vs_sparse_attn_prefill(
+                q_chunk, self.k_cache[:, :c1], self.v_cache[:, :c1], chunk_start, self.rope,
+                self.dca, self.sm_scale, self.pattern, out=out, lse=lse, stats=stats,
+                head_mask=rest)
+        ops.block_sparse_attn_prefill(
             q_chunk, self.k_cache[:, :c1], self.v_cache[:, :c1], chunk_start, self.rope,
-            self.dca, self.sm_scale, None if dense else self.pattern, out=out, lse=lse,
-            stats=stats, head_mask=head_mask, dense=dense)
+            self.dca, self.sm_scale, self.block_pattern, out=out, lse=lse, stats=stats,
+            head_mask=blk)
+        return out, lse
 
     def recall(self, q_chunk, chunk_start, rows, head_mask=None):
+        """(lse_full, lse_sparse, recall) [H, n_rows] of the sampled rows,
+        each head on its own pattern kind."""
         c1 = chunk_start + q_chunk.shape[1]
-        return ops.attn_recall_check(q_chunk, self.k_cache[:, :c1], chunk_start, self.rope,
-                                     self.dca, self.sm_scale, self.pattern, rows,
-                                     head_mask=head_mask)
+        sel = [head_mask is None or bool(head_mask[h]) for h in range(self.H)]
+        blk = [sel[h] and self.blocks[h] is not None for h in range(self.H)]
+        rest = [sel[h] and not blk[h] for h in range(self.H)]
+        if not any(blk):
+            return ops.attn_recall_check(q_chunk, self.k_cache[:, :c1], chunk_start, self.rope,
+                                         self.dca, self.sm_scale, self.pattern, rows,
+                                         head_mask=head_mask)
+        bf, bs, br = ops.block_sparse_recall_check(
+            q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
+            self.block_pattern, rows, head_mask=blk)
+        if not any(rest):
+            return bf, bs, br
+        lf, ls, rc = ops.attn_recall_check(q_chunk, self.k_cache[:, :c1], chunk_start,
+                                           self.rope, self.dca, self.sm_scale, self.pattern,
+                                           rows, head_mask=rest)
+        hb = torch.tensor([h for h in range(self.H) if blk[h]], device=self.device)
+        lf[hb], ls[hb], rc[hb] = bf[hb], bs[hb], br[hb]
+        return lf, ls, rc
 
     def prefill_chunk(self, q_chunk, k_chunk, v_chunk, chunk_start, out=None, lse=None,
                       stats=None):
@@ -124,8 +176,8 @@ class ChunkedSparsePrefill:
         `rows` is under the threshold get doubled budgets (capped at the
         number of keys), are re-estimated and re-attended; at most
         `max_rounds` rounds.  Raised budgets carry over to later chunks.
-        A-shape heads keep their fixed pattern.  Returns the per-round head
-        recalls (host tensors)."""
+        A-shape and block-sparse heads keep their pattern.  Returns the
+        per-round head recalls (host tensors)."""
         c1 = chunk_start + q_chunk.shape[1]
         history = []
         for _ in range(max_rounds + 1):
@@ -133,6 +185,7 @@ class ChunkedSparsePrefill:
             mean = rec.mean(dim=1).cpu()
             history.append(mean)
             low = [bool(mean[h] < threshold) and self.a_shape[h] is None and
+                   self.blocks[h] is None and
                    (self.n_vert[h] < c1 or self.n_slash[h] < c1) for h in range(self.H)]
             if len(history) > max_rounds or not any(low):
                 break
@@ -192,7 +245,7 @@ def search_head_patterns(layer, q, chunks, candidates, rows):
     Returns (choice: list of H candidate indices, scores: fp64 host tensor
     [n_candidates, H]).
     """
-    saved = (list(layer.n_vert), list(layer.n_slash), list(layer.a_shape))
+    saved = (list(layer.n_vert), list(layer.n_slash), list(layer.a_shape), list(layer.blocks))
     H = layer.H
     scores = torch.zeros(len(candidates), H, dtype=torch.float64)
     try:
@@ -205,7 +258,7 @@ def search_head_patterns(layer, q, chunks, candidates, rows):
                 scores[ci] += rec.double().mean(dim=1).cpu()
             scores[ci] /= len(chunks)
     finally:
-        layer.n_vert, layer.n_slash, layer.a_shape = saved
+        layer.n_vert, layer.n_slash, layer.a_shape, layer.blocks = saved
     choice = []
     for h in range(H):
         best = 0

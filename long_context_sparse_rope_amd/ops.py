@@ -93,6 +93,18 @@ class Pattern:
                 [si[h, :sc[h]].long() for h in range(si.shape[0])])
 
 
+class BlockPattern:
+    """Device buffers of a block-sparse pattern for one chunk: kept key
+    blocks idx [H, n_qb, max_blocks] (ascending, -1 padded) and counts
+    cnt [H, n_qb]; n_qb = ceil(chunk_len / 64)."""
+
+    def __init__(self, n_heads, n_qb, max_blocks, device):
+        self.max_blocks = int(max_blocks)
+        self.idx = torch.full((n_heads, max(1, n_qb), self.max_blocks), -1, dtype=torch.int32,
+                              device=device)
+        self.cnt = torch.zeros((n_heads, max(1, n_qb)), dtype=torch.int32, device=device)
+
+
 def _check(rc):
     if rc != 0:
         raise LcsrError(rc, C.load().lcsr_last_error().decode())
@@ -219,6 +231,84 @@ def pattern_fill_a_shape(pattern, n_sink, n_local, n_ctx, head_mask=None, stream
     _check(C.load().lcsr_pattern_fill_a_shape(ctypes.byref(pat), H, _ptr(hm), int(n_sink),
                                                int(n_local), int(n_ctx), _stream(stream)))
     return pattern
+
+
+def block_sparse_estimate(q, k_cache, chunk_start, rope, dca, sm_scale, n_blocks, pattern,
+                          head_mask=None, scores=None, select_only=False, workspace=None,
+                          stream=None):
+    """Fill the BlockPattern `pattern` with each query block's kept key
+    blocks (lcsr_block_sparse_estimate); `scores` fp32 [H, n_qb, n_kb] is
+    written if given (an input with select_only)."""
+    prob = _problem(q, k_cache, None, chunk_start, rope, dca, sm_scale)
+    H, n = q.shape[0], q.shape[1]
+    if len(n_blocks) != H:
+        raise ValueError("one budget per query head")
+    n_qb = -(-n // 64)
+    if pattern.idx.shape[0] != H or pattern.idx.shape[1] < n_qb:
+        raise ValueError("pattern buffers too small for this chunk")
+    if scores is not None:
+        n_kb = -(-(chunk_start + n) // 64)
+        if (scores.dtype != torch.float32 or tuple(scores.shape) != (H, n_qb, n_kb)
+                or not scores.is_contiguous()):
+            raise ValueError(f"scores must be contiguous float32 [{H}, {n_qb}, {n_kb}]")
+    nb = _host_i32(n_blocks)
+    hm = _head_mask(head_mask, H)
+    if select_only:
+        ws = torch.empty(16, dtype=torch.uint8, device=q.device)
+    else:
+        ws = _workspace(C.LCSR_WS_BLOCK_EST, prob, 0, 0, q.device, workspace)
+    idx, cnt = pattern.idx[:, :n_qb], pattern.cnt[:, :n_qb]
+    if not (idx.is_contiguous() and cnt.is_contiguous()):
+        raise ValueError("pattern buffers must hold exactly this chunk's query blocks")
+    _check(C.load().lcsr_block_sparse_estimate(
+        ctypes.byref(prob), _ptr(nb), _ptr(hm), pattern.max_blocks, idx.data_ptr(),
+        cnt.data_ptr(), None if scores is None else scores.data_ptr(),
+        C.LCSR_BS_SELECT_ONLY if select_only else 0, ws.data_ptr(), ws.numel(), _stream(stream)))
+    return pattern
+
+
+def block_sparse_attn_prefill(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale, pattern,
+                              out=None, out_dtype=torch.float32, lse=None, stats=None,
+                              head_mask=None, workspace=None, stream=None):
+    """Attention of the chunk's rows over their kept key blocks
+    (lcsr_block_sparse_attn_prefill).  Returns (out [H, L, D], lse or None)."""
+    prob = _problem(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale)
+    H, n, D = q.shape
+    n_qb = -(-n // 64)
+    if out is None:
+        out = torch.empty((H, n, D), dtype=out_dtype, device=q.device)
+    idx, cnt = pattern.idx[:, :n_qb], pattern.cnt[:, :n_qb]
+    if not (idx.is_contiguous() and cnt.is_contiguous()):
+        raise ValueError("pattern buffers must hold exactly this chunk's query blocks")
+    hm = _head_mask(head_mask, H)
+    ws = _workspace(C.LCSR_WS_BLOCK_ATTN, prob, 0, 0, q.device, workspace)
+    _check(C.load().lcsr_block_sparse_attn_prefill(
+        ctypes.byref(prob), idx.data_ptr(), cnt.data_ptr(), pattern.max_blocks, _ptr(hm),
+        out.data_ptr(), _dtype_code(out), out.stride(0), out.stride(1),
+        _dense_rows(lse, H, n, "lse"), None if stats is None else stats.data_ptr(), ws.data_ptr(),
+        ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def block_sparse_recall_check(q, k_cache, chunk_start, rope, dca, sm_scale, pattern, rows,
+                              head_mask=None, stream=None):
+    """(lse_full, lse_sparse, recall), each [H, n_rows], of a block-sparse
+    pattern (lcsr_block_sparse_recall_check)."""
+    prob = _problem(q, k_cache, None, chunk_start, rope, dca, sm_scale)
+    H, n = q.shape[0], rows.numel()
+    n_qb = -(-q.shape[1] // 64)
+    if rows.dtype != torch.int32 or not rows.is_contiguous():
+        raise TypeError("rows must be a contiguous int32 tensor")
+    idx, cnt = pattern.idx[:, :n_qb], pattern.cnt[:, :n_qb]
+    if not (idx.is_contiguous() and cnt.is_contiguous()):
+        raise ValueError("pattern buffers must hold exactly this chunk's query blocks")
+    outs = [torch.empty((H, n), dtype=torch.float32, device=q.device) for _ in range(3)]
+    hm = _head_mask(head_mask, H)
+    _check(C.load().lcsr_block_sparse_recall_check(
+        ctypes.byref(prob), idx.data_ptr(), cnt.data_ptr(), pattern.max_blocks, _ptr(hm),
+        rows.data_ptr(), n, outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+        _stream(stream)))
+    return tuple(outs)
 
 
 def vs_pattern_estimate(q, k_cache, chunk_start, rope, dca, sm_scale, n_vert, n_slash,

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     assert set(names) == set(C.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -192,6 +192,46 @@ def test_fill_a_shape_rejects(lib):
     # a mask that selects no head launches nothing and succeeds
     none = (ctypes.c_int32 * 28)()
     assert fill(pattern(), mask=none) == C.LCSR_OK
+
+
+def test_block_sparse_rejects(lib):
+    """Rejections before any launch (nothing written): alignment, budgets,
+    NULL arrays, workspace, context limit."""
+    p = problem()
+    need_e = lib.lcsr_workspace_bytes(C.LCSR_WS_BLOCK_EST, ctypes.byref(p), 0, 0)
+    need_a = lib.lcsr_workspace_bytes(C.LCSR_WS_BLOCK_ATTN, ctypes.byref(p), 0, 0)
+    # pooled keys + pooled queries + scores (28 x 512 x 1024 fp32 alone);
+    # the attention holds at least one rotated copy of the chunk's queries
+    assert need_e > 28 * 512 * 1024 * 4
+    assert need_a >= 28 * 32768 * 128 * 2
+    budgets = (ctypes.c_int32 * 28)(*([8] * 28))
+
+    def est(pp, nb=budgets, max_blocks=16, idx=FAKE, cnt=FAKE, scores=None, flags=0,
+            ws=FAKE, ws_bytes=1 << 40):
+        return lib.lcsr_block_sparse_estimate(ctypes.byref(pp), nb, None, max_blocks, idx, cnt,
+                                              scores, flags, ws, ws_bytes, None)
+
+    def att(pp, max_blocks=16, idx=FAKE, cnt=FAKE, out=FAKE, out_dtype=C.LCSR_FP32,
+            ws=FAKE, ws_bytes=1 << 40):
+        return lib.lcsr_block_sparse_attn_prefill(ctypes.byref(pp), idx, cnt, max_blocks, None,
+                                                  out, out_dtype, 128, 128 * 32768, None, None,
+                                                  ws, ws_bytes, None)
+
+    assert est(problem(chunk_start=32768 + 32)) == C.LCSR_EINVAL and "% 64" in err(lib)
+    assert est(p, max_blocks=0) == C.LCSR_EINVAL
+    assert est(p, max_blocks=4) == C.LCSR_EINVAL and "n_blocks[0]" in err(lib)
+    assert est(p, nb=None) == C.LCSR_EINVAL
+    assert est(p, idx=None) == C.LCSR_EINVAL
+    assert est(p, flags=C.LCSR_BS_SELECT_ONLY) == C.LCSR_EINVAL
+    assert est(p, ws_bytes=need_e - 1) == C.LCSR_EWORKSPACE
+    far = problem(chunk_start=1 << 21, chunk_len=64)
+    assert est(far) == C.LCSR_ENOTSUP and "key blocks" in err(lib)
+    assert att(problem(chunk_start=32768 + 32)) == C.LCSR_EINVAL
+    assert att(p, cnt=None) == C.LCSR_EINVAL
+    assert att(p, out=None) == C.LCSR_EINVAL
+    assert att(p, out_dtype=7) == C.LCSR_EINVAL
+    assert att(p, ws_bytes=need_a - 1) == C.LCSR_EWORKSPACE
+    assert att(problem(head_dim=96)) == C.LCSR_ENOTSUP
 
 
 def test_rope_and_dca_reject(lib):

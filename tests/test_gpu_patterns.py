@@ -32,6 +32,7 @@ CFG_STRIPES = scaled(FOURTEEN_B_512K_REFINE, n_heads=10, n_kv_heads=2, seq_len=4
 
 VS = lambda nv, ns: {"kind": "vs", "n_vert": nv, "n_slash": ns}          # noqa: E731
 AS = lambda s, w: {"kind": "a_shape", "n_sink": s, "n_local": w}          # noqa: E731
+BS = lambda k: {"kind": "block", "n_blocks": k}                           # noqa: E731
 
 
 def _layer(cfg):
@@ -80,13 +81,15 @@ def test_fill_a_shape_bit_exact(n_sink, n_local, n_ctx):
 
 def test_mixed_head_patterns_layer():
     """Heads cycle through a vertical-slash estimate, two A-shapes, a pure
-    sliding window and sinks only; the whole chunk loop runs, then every row
-    of the last chunk is checked against the oracle (A-shape heads on the
-    oracle's own lists, vertical-slash heads on the GPU's selection)."""
+    sliding window, sinks only and two block-sparse budgets; the whole chunk
+    loop runs, then every row of the last chunk is checked against the oracle
+    (A-shape heads on the oracle's own lists, vertical-slash and block heads
+    on the GPU's selection)."""
     cfg = CFG
     q, k, v = synth.generate(cfg, DEV)
     layer = _layer(cfg)
-    kinds = [VS(64, 128), AS(16, 256), AS(0, 100), AS(64, 0), AS(4, 700), VS(32, 200)]
+    kinds = [VS(64, 128), AS(16, 256), BS(4), AS(0, 100), AS(64, 0), BS(11), AS(4, 700),
+             VS(32, 200)]
     configs = [kinds[h % len(kinds)] for h in range(cfg.n_heads)]
     layer.set_head_patterns(configs)
     N, C = cfg.seq_len, cfg.prefill_chunk
@@ -98,21 +101,28 @@ def test_mixed_head_patterns_layer():
     layer.attend(q[:, c0:], c0, stats=stats)
     torch.cuda.synchronize()
     verts, slashes = layer.pattern.lists()
+    bidx, bcnt = layer.block_pattern.idx.cpu().numpy(), layer.block_pattern.cnt.cpu().numpy()
     qo, _, _ = oracle_inputs(q, k[:1], v[:1])
     ctxs = _contexts(cfg, k, v, N)
     rows = np.arange(c0, N)
     G = cfg.n_heads // cfg.n_kv_heads
     pairs = 0
     for h, c in enumerate(configs):
-        if c["kind"] == "a_shape":
-            ov, os_ = oracle.a_shape_lists(c["n_sink"], c["n_local"], N)
-            np.testing.assert_array_equal(verts[h].numpy(), ov)
-            np.testing.assert_array_equal(slashes[h].numpy(), os_)
+        if c["kind"] == "block":
+            assert np.all(bcnt[h] == np.minimum(c["n_blocks"], c0 // 64 + np.arange(16) + 1))
+            kept = lambda i, h=h: bidx[h, (i - c0) // 64, :bcnt[h, (i - c0) // 64]]  # noqa
+            ro, rl, sizes = oracle.block_sparse_rows(qo[h, rows], rows, ctxs[h // G], kept,
+                                                     layer.sm_scale)
         else:
-            ov, os_ = verts[h].numpy(), slashes[h].numpy()
-            assert ov.size == min(c["n_vert"], N) and os_.size == min(c["n_slash"], N)
-        ro, rl, sizes = oracle.sparse_rows(qo[h, rows], rows, ctxs[h // G], ov, os_,
-                                           layer.sm_scale)
+            if c["kind"] == "a_shape":
+                ov, os_ = oracle.a_shape_lists(c["n_sink"], c["n_local"], N)
+                np.testing.assert_array_equal(verts[h].numpy(), ov)
+                np.testing.assert_array_equal(slashes[h].numpy(), os_)
+            else:
+                ov, os_ = verts[h].numpy(), slashes[h].numpy()
+                assert ov.size == min(c["n_vert"], N) and os_.size == min(c["n_slash"], N)
+            ro, rl, sizes = oracle.sparse_rows(qo[h, rows], rows, ctxs[h // G], ov, os_,
+                                               layer.sm_scale)
         print(f"[mixed] head {h} {c}", flush=True)
         compare(host64(out[h, c0:]), ro)
         lse_compare(host64(lse[h, c0:]), rl)
@@ -128,7 +138,7 @@ def test_search_head_patterns(cfg):
     q, k, v = synth.generate(cfg, DEV)
     layer = _layer(cfg)
     build_cache(layer, k, v, cfg.seq_len)
-    cands = [AS(16, 128), VS(32, 96), AS(64, 512), VS(128, 384)]
+    cands = [AS(16, 128), VS(32, 96), BS(4), AS(64, 512), VS(128, 384), BS(8)]
     chunks = [(2048, 1024), (3072, 1024)]
     rng = np.random.default_rng(7)
     off = np.unique(np.concatenate([np.arange(1024 - 64, 1024), rng.integers(0, 1024, 32)]))
@@ -140,7 +150,7 @@ def test_search_head_patterns(cfg):
     print(f"[search] {len(cands)} candidates x {len(chunks)} chunks: "
           f"{(time.perf_counter() - t0) * 1e3:.1f} ms", flush=True)
     # the layer's own configuration is restored
-    assert layer.a_shape == [None] * cfg.n_heads
+    assert layer.a_shape == [None] * cfg.n_heads and layer.blocks == [None] * cfg.n_heads
     assert layer.n_vert == [cfg.n_vert] * cfg.n_heads
     qo, _, _ = oracle_inputs(q, k[:1], v[:1])
     ctxs = _contexts(cfg, k, v, cfg.seq_len)
@@ -153,12 +163,21 @@ def test_search_head_patterns(cfg):
             verts, slashes = layer.pattern.lists()
             r = c0 + off
             for h in range(cfg.n_heads):
-                if c["kind"] == "a_shape":
-                    ov, os_ = oracle.a_shape_lists(c["n_sink"], c["n_local"], c0 + n)
+                if c["kind"] == "block":
+                    bidx = layer.block_pattern.idx[h].cpu().numpy()
+                    bcnt = layer.block_pattern.cnt[h].cpu().numpy()
+                    kept = lambda i, c0=c0: bidx[(i - c0) // 64, :bcnt[(i - c0) // 64]]  # noqa
+                    _, sl, _ = oracle.block_sparse_rows(qo[h, r], r, ctxs[h // G], kept,
+                                                        layer.sm_scale)
+                    _, fl = oracle.dense_causal_rows(qo[h, r], r, ctxs[h // G], layer.sm_scale)
+                    rec = np.exp(sl - fl)
                 else:
-                    ov, os_ = verts[h].numpy(), slashes[h].numpy()
-                rec = oracle.attention_recall(qo[h, r], r, ctxs[h // G], ov, os_,
-                                              layer.sm_scale)[2]
+                    if c["kind"] == "a_shape":
+                        ov, os_ = oracle.a_shape_lists(c["n_sink"], c["n_local"], c0 + n)
+                    else:
+                        ov, os_ = verts[h].numpy(), slashes[h].numpy()
+                    rec = oracle.attention_recall(qo[h, r], r, ctxs[h // G], ov, os_,
+                                                  layer.sm_scale)[2]
                 ref[ci, h] += rec.mean() / len(chunks)
     got = scores.numpy()
     d = np.abs(got - ref)
