@@ -164,6 +164,46 @@ def a_shape_point(cfg, layer, q, n_sink=16, n_local=2048, reps=5):
             "tflops": round(4.0 * cfg.head_dim * pairs / (ms * 1e-3) / 1e12, 2)}
 
 
+def block_sparse_point(cfg, layer, q, n_blocks=100, reps=5):
+    """The last chunk with every head block-sparse (n_blocks kept 64-key
+    blocks per 64-query block, 6,400 keys: about the vertical-slash
+    budget): median times of the estimate (pooling, scores, selection) and
+    of the attention, exact pair count, algorithmic TFLOP/s of the
+    attention."""
+    c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
+    c1 = c0 + lc
+    H = cfg.n_heads
+    pat = L.BlockPattern(H, -(-lc // 64), n_blocks, q.device)
+    o = torch.empty((H, lc, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
+    stats = torch.zeros(2, dtype=torch.int64, device=q.device)
+    est = lambda: L.block_sparse_estimate(  # noqa: E731
+        q[:, c0:c1], layer.k_cache[:, :c1], c0, layer.rope, layer.dca, layer.sm_scale,
+        [n_blocks] * H, pat)
+    att = lambda st=None: L.block_sparse_attn_prefill(  # noqa: E731
+        q[:, c0:c1], layer.k_cache[:, :c1], layer.v_cache[:, :c1], c0, layer.rope, layer.dca,
+        layer.sm_scale, pat, out=o, stats=st)
+    est()
+    att(stats)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    ms_e, ms_a = timed(est), timed(att)
+    pairs = stats.cpu().tolist()[1]
+    return {"n_blocks": n_blocks, "chunk": [c0, c1], "estimate_ms": round(ms_e, 3),
+            "attention_ms": round(ms_a, 3), "pairs": pairs,
+            "tflops": round(4.0 * cfg.head_dim * pairs / (ms_a * 1e-3) / 1e12, 2)}
+
+
 def decode_points(cfg, layer, q, row_counts, reps=20):
     """Decode step over the full KV cache (left by the timed steps): the last
     n rows of the prompt against every key up to each, one lcsr_attn_decode
@@ -251,6 +291,8 @@ def main():
                     help="context lengths of the dense one-chunk points ('' for none)")
     ap.add_argument("--no-a-shape", action="store_true",
                     help="skip the last-chunk A-shape (sink 16 + window 2048) point")
+    ap.add_argument("--no-block-sparse", action="store_true",
+                    help="skip the last-chunk block-sparse (100 blocks) point")
     ap.add_argument("--decode-rows", default="1,4",
                     help="rows per decode-step point over the full cache ('' for none)")
     args = ap.parse_args()
@@ -325,6 +367,9 @@ def main():
     if not args.no_a_shape:
         print("[bench] a-shape chunk point", file=sys.stderr, flush=True)
         rec["a_shape_chunk"] = a_shape_point(cfg, layer, q)
+    if not args.no_block_sparse:
+        print("[bench] block-sparse chunk point", file=sys.stderr, flush=True)
+        rec["block_sparse_chunk"] = block_sparse_point(cfg, layer, q)
     if args.decode_rows:
         print("[bench] decode-step points", file=sys.stderr, flush=True)
         rec["decode"] = decode_points(cfg, layer, q,

@@ -1420,11 +1420,11 @@ __global__ void __launch_bounds__(256) decode_combine(DecArgs a, void* out, int3
 }
 
 // ------------------------------------------------------------ block sparse
-// Attention over whole 64-key blocks: row block rb (32 rows) of head h
-// attends to the key blocks listed for its 64-row query block, causally
-// inside the diagonal block.  The same three-wave scheme as the decode step:
-// wave 1 streams the K tiles and wave 2 the V tiles of the list into a ring
-// of kStages stages, wave 0 multiplies.  A 32-row block lies inside one DCA
+// Attention over whole 64-key blocks: the 64 rows of query block qb of head h
+// attend to the key blocks listed for it, causally inside the diagonal
+// block.  The decode step's scheme with two consumers: waves 0 and 1 multiply
+// (rows 0-31 and 32-63 of the block, sharing every tile), wave 2 streams the
+// K tiles and wave 3 the V tiles of the list into a ring of kStages stages.  A 32-row block lies inside one DCA
 // chunk (the period and the chunk start are multiples of 64), so the query
 // variant changes only with the tile's key chunk.
 struct BsArgs {
@@ -1445,6 +1445,8 @@ struct BsArgs {
   unsigned long long* stats;  // [2]: (executed, selected) pairs
 };
 
+constexpr int kBsStages = 2;  // ring stages (two workgroups per CU at D 128)
+
 template <int M, int S>
 __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   // `ahead` tiles after the one that must have landed are still allowed in
@@ -1456,18 +1458,18 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
 }
 
 template <int D, int kStages>
-__global__ void __launch_bounds__(192) bs_attn_kernel(BsArgs a) {
+__global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
   using B = Buf<D>;
   constexpr int M = B::kInstrPerMat;
   constexpr int R = B::kRowsPerInstr;
   constexpr int kStageBytes = 2 * B::kKBytes;
   __shared__ __attribute__((aligned(16))) char stage[kStages][kStageBytes];
-  const int rb = blockIdx.x, h = blockIdx.y;
+  const int64_t qb = blockIdx.x;
+  const int h = blockIdx.y;
   if (!((a.head_mask >> h) & 1ull)) return;
   const int g = h / a.G;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, half = lane >> 5;
-  const int64_t qb = rb >> 1;
   const int32_t* list = a.blk_idx + ((int64_t)h * a.n_qb + qb) * a.max_blocks;
   const int cnt_in = __builtin_amdgcn_readfirstlane(a.blk_cnt[(int64_t)h * a.n_qb + qb]);
   const int n_local = cnt_in < a.max_blocks ? cnt_in : a.max_blocks;
@@ -1486,8 +1488,8 @@ __global__ void __launch_bounds__(192) bs_attn_kernel(BsArgs a) {
     x.gran = 15;
     return x;
   };
-  if (w > 0) {
-    const bool isv = w == 2;
+  if (w >= 2) {
+    const bool isv = w == 3;
     const char* src = reinterpret_cast<const char*>((isv ? a.v : a.k) + (int64_t)g * a.kv_sh);
     const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
     const uint32_t base = lds_addr(&stage[0][0]) + (isv ? B::kKBytes : 0);
@@ -1513,9 +1515,9 @@ __global__ void __launch_bounds__(192) bs_attn_kernel(BsArgs a) {
     }
     return;
   }
-  // ---------------- wave 0: the products; lane rows rho = lane & 31
+  // ---------------- waves 0 and 1: the products; lane rows rho = lane & 31
   const int rho = lane & 31;
-  const int64_t row = a.c0 + (int64_t)rb * kRowBlock + rho;
+  const int64_t row = a.c0 + (qb * 2 + w) * kRowBlock + rho;
   const bool live = row < a.c0 + a.L;
   const int64_t my_row = live ? row : a.c0 + a.L - 1;
   const int64_t qchunk = a.period ? my_row / a.period : 0;
@@ -1591,9 +1593,9 @@ __global__ void __launch_bounds__(192) bs_attn_kernel(BsArgs a) {
 }
 
 template <int D>
-int launch_block_attn(const BsArgs& a, int64_t n_rb, hipStream_t s) {
-  hipLaunchKernelGGL((bs_attn_kernel<D, 4>), dim3((unsigned)n_rb, (unsigned)a.H), dim3(192), 0,
-                     s, a);
+int launch_block_attn(const BsArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((bs_attn_kernel<D, kBsStages>), dim3((unsigned)a.n_qb, (unsigned)a.H),
+                     dim3(256), 0, s, a);
   return check_launch("block-sparse attention");
 }
 
@@ -1799,8 +1801,7 @@ int run_block_attention(const lcsr_problem_t& p, const int32_t* idx, const int32
   a.o_st = o_st;
   a.lse = lse;
   a.stats = reinterpret_cast<unsigned long long*>(stats);
-  const int64_t n_rb = (p.chunk_len + kRowBlock - 1) / kRowBlock;
-  return p.head_dim == 128 ? launch_block_attn<128>(a, n_rb, s) : launch_block_attn<64>(a, n_rb, s);
+  return p.head_dim == 128 ? launch_block_attn<128>(a, s) : launch_block_attn<64>(a, s);
 }
 
 }  // namespace lcsr

@@ -20,7 +20,8 @@ namespace lcsr {
 namespace {
 
 constexpr int kBlk = 64;
-constexpr int kScoreQb = 4;  // query blocks per score workgroup
+constexpr int kScoreQb = 4;      // query blocks per score workgroup
+constexpr int kScoreSpan = 1024;  // key blocks per score workgroup (grid.z splits the rest)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -32,7 +33,9 @@ __device__ __forceinline__ float load_q(const void* q, int32_t dtype, int64_t id
   return bf16_to_f32(static_cast<const uint16_t*>(q)[idx]);
 }
 
-// grid (n_kb, H_kv), 64 threads: mean of each 64-key block of the cache.
+// grid (n_kb, H_kv), 64 threads: mean of each 64-key block of the cache,
+// stored as float4 [H_kv][D / 4][n_kb] so that lanes of the score kernel
+// (one key block each) read consecutive addresses.
 __global__ void __launch_bounds__(64) bs_pool_keys(const uint16_t* __restrict__ k, int64_t kv_sh,
                                                    int64_t kv_st, int64_t n_ctx, int D,
                                                    int64_t n_kb, float* __restrict__ pk) {
@@ -46,7 +49,7 @@ __global__ void __launch_bounds__(64) bs_pool_keys(const uint16_t* __restrict__ 
     float s = 0.f;
 #pragma unroll 8
     for (int64_t j = j0; j < j1; ++j) s += bf16_to_f32(src[j * kv_st]);
-    pk[((int64_t)g * n_kb + kb) * D + d] = s * inv;
+    pk[(((int64_t)g * (D / 4) + d / 4) * n_kb + kb) * 4 + d % 4] = s * inv;
   }
 }
 
@@ -93,13 +96,13 @@ __global__ void __launch_bounds__(64) bs_pool_queries(PoolQArgs a, FreqTable ft)
   }
 }
 
-// grid (ceil(n_qb / kScoreQb), H_kv), 256 threads, one key block per thread
-// and pass: the scores of the G query heads x kScoreQb query blocks against
-// every key block up to the workgroup's last diagonal, key chunk by key
-// chunk (the matching query means sit in LDS).  Blocks above a query
-// block's diagonal are not written.
+// grid (ceil(n_qb / kScoreQb), H_kv, key-block spans), 256 threads, one key
+// block per thread and pass: the scores of the G query heads x kScoreQb query
+// blocks against the key blocks of span z (kScoreSpan blocks) up to the
+// workgroup's last diagonal, key chunk by key chunk (the matching query means
+// sit in LDS).  Blocks above a query block's diagonal are not written.
 struct ScoreArgs {
-  const float* pk;  // [H_kv][n_kb][D]
+  const float* pk;  // float4 [H_kv][D / 4][n_kb]
   const float* pq;  // [n_kc][H][n_qb][D]
   float* scores;    // [H][n_qb][n_kb]
   int64_t c0, period, n_qb, n_kb;
@@ -108,9 +111,8 @@ struct ScoreArgs {
   float sm_scale;
 };
 
-template <int D>
+template <int D, int NV>
 __global__ void __launch_bounds__(256) bs_score(ScoreArgs a) {
-  constexpr int NV = kMaxGroup * kScoreQb;
   __shared__ float4 qv[NV][D / 4];
   const int g = blockIdx.y;
   const int64_t qb0 = (int64_t)blockIdx.x * kScoreQb;
@@ -119,10 +121,16 @@ __global__ void __launch_bounds__(256) bs_score(ScoreArgs a) {
   const int64_t diag0 = a.c0 / kBlk + qb0;        // diagonal of the first block
   const int64_t kb_end = diag0 + nq;              // one past the last diagonal
   const int64_t kpc = a.period ? a.period / kBlk : kb_end;  // key blocks per key chunk
+  const int64_t z0 = (int64_t)blockIdx.z * kScoreSpan;
+  const int64_t z1 = z0 + kScoreSpan < kb_end ? z0 + kScoreSpan : kb_end;
+  if (z0 >= z1) return;
   for (int kc = 0; kc < a.n_kc; ++kc) {
-    const int64_t kb_lo = kc * kpc;
-    const int64_t kb_hi = kb_lo + kpc < kb_end ? kb_lo + kpc : kb_end;
+    int64_t kb_lo = kc * kpc;
+    int64_t kb_hi = kb_lo + kpc < kb_end ? kb_lo + kpc : kb_end;
     if (kb_lo >= kb_hi) break;
+    kb_lo = kb_lo > z0 ? kb_lo : z0;
+    kb_hi = kb_hi < z1 ? kb_hi : z1;
+    if (kb_lo >= kb_hi) continue;
     __syncthreads();
     for (int e = threadIdx.x; e < nv * (D / 4); e += 256) {
       const int vv = e / (D / 4), d4 = e % (D / 4);
@@ -133,13 +141,13 @@ __global__ void __launch_bounds__(256) bs_score(ScoreArgs a) {
     }
     __syncthreads();
     for (int64_t kb = kb_lo + threadIdx.x; kb < kb_hi; kb += 256) {
-      const float4* kp = reinterpret_cast<const float4*>(a.pk + ((int64_t)g * a.n_kb + kb) * D);
+      const float4* kp = reinterpret_cast<const float4*>(a.pk) + (int64_t)g * (D / 4) * a.n_kb + kb;
       float acc[NV];
 #pragma unroll
       for (int vv = 0; vv < NV; ++vv) acc[vv] = 0.f;
 #pragma unroll 2
       for (int d4 = 0; d4 < D / 4; ++d4) {
-        const float4 k4 = kp[d4];
+        const float4 k4 = kp[(int64_t)d4 * a.n_kb];
 #pragma unroll
         for (int vv = 0; vv < NV; ++vv) {
           if (vv < nv) {
@@ -168,10 +176,37 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exclusive prefix sum over the 256 threads of a workgroup (wave scans with
+// lane shuffles, then the four wave totals); also returns the total.
+__device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* wave_tot,
+                                                    uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[w] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t t = wave_tot[u];
+    before += u < w ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
 // grid (n_qb, H), 256 threads: per query block, the k - 1 best of the key
 // blocks 0 .. diag - 1 (order: score desc, index asc) and the diagonal, in
 // ascending order; -1 after the count.  Keys sit in LDS (dynamic, n_kb
-// words); a four-round 8-bit radix select finds the k-1-th key, then an
+// words); a radix select over 11, 11 and 10 key bits (2048-bin histograms,
+// so that keys of one magnitude spread over many bins, with prefix sums
+// across the workgroup to find the bin) gives the k-1-th key, then an
 // ordered compaction writes the indices.
 struct SelectArgs {
   const float* scores;  // [H][n_qb][n_kb]
@@ -183,11 +218,12 @@ struct SelectArgs {
   uint64_t head_mask;
 };
 
+constexpr int kSelBins = 2048;
+
 __global__ void __launch_bounds__(256) bs_select(SelectArgs a) {
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t part[256];
-  __shared__ uint32_t part2[256];
+  __shared__ uint32_t hist[kSelBins];
+  __shared__ uint32_t wave_tot[4];
   __shared__ uint32_t sh_prefix, sh_need;
   const int64_t qb = blockIdx.x;
   const int h = blockIdx.y;
@@ -203,19 +239,33 @@ __global__ void __launch_bounds__(256) bs_select(SelectArgs a) {
   for (int i = tid; i < n; i += 256) keys[i] = order_key(sc[i]);
   __syncthreads();
   uint32_t prefix = 0, mask = 0, need = (uint32_t)kk;
-  if (kk > 0 && kk < n) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+  const bool partial = kk > 0 && kk < n;  // uniform
+  if (partial) {
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int r = 0; r < 3; ++r) {
+      const int shift = shifts[r];
+      const uint32_t dmask = (1u << widths[r]) - 1u;
+      const int nb = 1 << widths[r];
+      for (int b = tid; b < nb; b += 256) hist[b] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += 256) {
         const uint32_t u = keys[i];
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int b = 255;
-        for (; b > 0; --b) {
+      // thread t owns bins [t * per, (t + 1) * per), counted from the top
+      // bin down: thread 0 the highest bins
+      const int per = nb / 256;
+      const int top = nb - 1 - tid * per;
+      uint32_t own = 0;
+      for (int b = 0; b < per; ++b) own += hist[top - b];
+      uint32_t total;
+      const uint32_t above = block_scan_excl(own, wave_tot, &total);
+      if (above < need && above + own >= need) {
+        uint32_t cum = above;
+        int b = top;
+        for (; b > top - per + 1; --b) {
           if (cum + hist[b] >= need) break;
           cum += hist[b];
         }
@@ -225,7 +275,7 @@ __global__ void __launch_bounds__(256) bs_select(SelectArgs a) {
       __syncthreads();
       prefix = sh_prefix;
       need = sh_need;
-      mask |= 255u << shift;
+      mask |= dmask << shift;
     }
   }
   // keep: key > T, or key == T among the first `need` ties by index; with
@@ -234,45 +284,24 @@ __global__ void __launch_bounds__(256) bs_select(SelectArgs a) {
   const int seg = (n + 255) / 256;
   const int b0 = tid * seg < n ? tid * seg : n;
   const int b1 = b0 + seg < n ? b0 + seg : n;
-  uint32_t eq = 0;
-  if (kk > 0 && kk < n)
-    for (int i = b0; i < b1; ++i) eq += keys[i] == T;
-  part[tid] = eq;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t s = 0;
-    for (int t = 0; t < 256; ++t) {
-      const uint32_t x = part[t];
-      part[t] = s;
-      s += x;
+  uint32_t eq = 0, gt = 0;
+  if (partial)
+    for (int i = b0; i < b1; ++i) {
+      eq += keys[i] == T;
+      gt += keys[i] > T;
     }
+  uint32_t tot;
+  const uint32_t eq_before0 = block_scan_excl(eq, wave_tot, &tot);
+  uint32_t sel;
+  if (kk >= n) sel = (uint32_t)(b1 - b0);
+  else if (kk == 0) sel = 0;
+  else {
+    // ties of this segment that are kept: those ranked below `need`
+    const uint32_t lo = eq_before0 < need ? need - eq_before0 : 0u;
+    sel = gt + (eq < lo ? eq : lo);
   }
-  __syncthreads();
-  uint32_t eq_before = part[tid], sel = 0;
-  for (int i = b0; i < b1; ++i) {
-    bool keep;
-    if (kk >= n) keep = true;
-    else if (kk == 0) keep = false;
-    else {
-      const uint32_t u = keys[i];
-      keep = u > T || (u == T && eq_before < need);
-      eq_before += u == T;
-    }
-    sel += keep;
-  }
-  part2[tid] = sel;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t s = 0;
-    for (int t = 0; t < 256; ++t) {
-      const uint32_t x = part2[t];
-      part2[t] = s;
-      s += x;
-    }
-  }
-  __syncthreads();
-  uint32_t pos = part2[tid];
-  eq_before = part[tid];
+  uint32_t pos = block_scan_excl(sel, wave_tot, &tot);
+  uint32_t eq_before = eq_before0;
   for (int i = b0; i < b1; ++i) {
     bool keep;
     if (kk >= n) keep = true;
@@ -367,11 +396,25 @@ int run_block_estimate(const lcsr_problem_t& p, const int32_t* budgets_host, uin
     sa.n_kc = (int)L.n_kc;
     sa.head_mask = head_mask;
     sa.sm_scale = p.sm_scale;
-    const dim3 grid((unsigned)((L.n_qb + kScoreQb - 1) / kScoreQb), (unsigned)p.n_kv_heads);
-    if (p.head_dim == 128)
-      hipLaunchKernelGGL(bs_score<128>, grid, dim3(256), 0, s, sa);
-    else
-      hipLaunchKernelGGL(bs_score<64>, grid, dim3(256), 0, s, sa);
+    const dim3 grid((unsigned)((L.n_qb + kScoreQb - 1) / kScoreQb), (unsigned)p.n_kv_heads,
+                    (unsigned)((L.n_kb + kScoreSpan - 1) / kScoreSpan));
+    // accumulators for G x kScoreQb query means, rounded up to a power of two
+    const int nv = sa.G * kScoreQb;
+#define LCSR_BS_SCORE(DD, NV) hipLaunchKernelGGL((bs_score<DD, NV>), grid, dim3(256), 0, s, sa)
+    if (p.head_dim == 128) {
+      if (nv <= 4) LCSR_BS_SCORE(128, 4);
+      else if (nv <= 8) LCSR_BS_SCORE(128, 8);
+      else if (nv <= 16) LCSR_BS_SCORE(128, 16);
+      else if (nv <= 32) LCSR_BS_SCORE(128, 32);
+      else LCSR_BS_SCORE(128, 64);
+    } else {
+      if (nv <= 4) LCSR_BS_SCORE(64, 4);
+      else if (nv <= 8) LCSR_BS_SCORE(64, 8);
+      else if (nv <= 16) LCSR_BS_SCORE(64, 16);
+      else if (nv <= 32) LCSR_BS_SCORE(64, 32);
+      else LCSR_BS_SCORE(64, 64);
+    }
+#undef LCSR_BS_SCORE
     rc = check_launch("block scores");
     if (rc) return rc;
   }
