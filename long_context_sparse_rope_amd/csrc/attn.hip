@@ -1304,9 +1304,13 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
     step_barrier();  // tile i in its stage; the stage of tile i - 1 is released
     const Tile tt = tile_of(t_begin + i);
     // the query variant of this lane's row against the tile's DCA chunk (a
-    // tile never crosses a chunk edge: the period is a multiple of 64)
+    // tile never crosses a chunk edge: the period is a multiple of 64).  Rows
+    // of one call may straddle a chunk edge: an earlier row then meets tiles
+    // of the next chunk (rel < 0), whose keys all lie after it and are
+    // masked; it takes variant 0 there, so the query load stays inside the
+    // variants
     const int64_t rel = qchunk - tt.kchunk;
-    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (int)rel);
+    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
     if (__ballot(var != cur_var) != 0ull) {
       const uint16_t* qb = a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
 #pragma unroll
@@ -1533,8 +1537,10 @@ __global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
   for (int i = 0; i < n_local; ++i) {
     step_barrier();
     const Tile tt = tile_of(i);
+    // rel >= 0 here (kept blocks lie at or before the diagonal); clamped all
+    // the same, so that the query load can never leave the variants
     const int64_t rel = qchunk - tt.kchunk;
-    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (int)rel);
+    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
     if (__ballot(var != cur_var) != 0ull) {
       const uint16_t* qp =
           a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;

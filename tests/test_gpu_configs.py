@@ -132,6 +132,39 @@ def run_layer(name):
         res["dense"] = {"rows": rows, "out": out[:, ri].cpu().numpy(),
                         "lse": lse[:, ri].cpu().numpy(),
                         "q": q[:, torch.as_tensor(rows, device=DEV)].float().cpu().numpy()}
+        # the other head patterns on the last chunk, in buffers of their own:
+        # block-sparse with 100 kept blocks and A-shape with sink 16 + window
+        # 2048 (the measured configurations)
+        c1 = c0 + lc
+        oh = oracle_heads(cfg)
+        rows = sample_rows(cfg, c0, lc)
+        ri = torch.as_tensor(rows - c0, device=DEV)
+        qr = q[:, torch.as_tensor(rows, device=DEV)].float().cpu().numpy()
+        n_qb, n_kb = lc // 64, c1 // 64
+        bp = L.BlockPattern(H, n_qb, 100, DEV)
+        sc = torch.empty(H, n_qb, n_kb, device=DEV)
+        L.block_sparse_estimate(q[:, c0:c1], layer.k_cache[:, :c1], c0, layer.rope, layer.dca,
+                                sm, [100] * H, bp, scores=sc)
+        st_b = torch.zeros(2, dtype=torch.int64, device=DEV)
+        L.block_sparse_attn_prefill(q[:, c0:c1], layer.k_cache[:, :c1], layer.v_cache[:, :c1],
+                                    c0, layer.rope, layer.dca, sm, bp, out=out[:, :lc],
+                                    lse=lse[:, :lc], stats=st_b)
+        res["block"] = {"c0": c0, "rows": rows, "q": qr, "out": out[:, ri].cpu().numpy(),
+                        "lse": lse[:, ri].cpu().numpy(),
+                        "idx": {h: bp.idx[h].cpu().numpy() for h in oh},
+                        "cnt": {h: bp.cnt[h].cpu().numpy() for h in oh},
+                        "scores": {h: sc[h].cpu().numpy() for h in oh},
+                        "q_chunk": {h: q[h, c0:c1].float().cpu().numpy() for h in oh},
+                        "stats": st_b.cpu().tolist()}
+        del sc
+        ap = L.Pattern(H, 16, 2048, DEV)
+        L.pattern_fill_a_shape(ap, 16, 2048, c1)
+        L.vs_sparse_attn_prefill(q[:, c0:c1], layer.k_cache[:, :c1], layer.v_cache[:, :c1], c0,
+                                 layer.rope, layer.dca, sm, ap, out=out[:, :lc], lse=lse[:, :lc])
+        av, asl = ap.lists()
+        res["a_shape"] = {"rows": rows, "q": qr, "out": out[:, ri].cpu().numpy(),
+                          "lse": lse[:, ri].cpu().numpy(),
+                          "verts": [x.numpy() for x in av], "slashes": [x.numpy() for x in asl]}
     if name in ("7b_1m_dca", "14b_256k"):
         # decode steps on the full cache: the newest rows (as many as fill the
         # 32 matrix rows, then one) and, with DCA, rows across a period edge
@@ -295,6 +328,56 @@ def test_dense_mode_1m_sampled_rows():
                                           res["sm"])
         compare(dn["out"][h].astype(np.float64), ro)
         lse_compare(dn["lse"][h].astype(np.float64), rl)
+
+
+def test_block_sparse_1m_sampled_rows():
+    """Block-sparse heads at the 1M context (last chunk, 100 blocks): block
+    scores of the oracle heads against fp64, the selection bit-exact on the
+    GPU's scores, and sampled rows against the oracle on the GPU's lists."""
+    name = "7b_1m_dca"
+    cfg = CONFIGS[name]
+    res = run_layer(name)
+    b = res["block"]
+    c0 = b["c0"]
+    for h in oracle_heads(cfg):
+        ctx = key_context(name, h // cfg.group)
+        ref = oracle.block_scores(b["q_chunk"][h].astype(np.float64), c0, ctx, res["sm"])
+        got = b["scores"][h].astype(np.float64)
+        fin = np.isfinite(ref)
+        d = np.abs(got[fin] - ref[fin])
+        print(f"[block] {name} head {h}: score max |d| {d.max():.2e} (max |s| "
+              f"{np.abs(ref[fin]).max():.2e})", flush=True)
+        assert np.all(d <= 1e-4 + 1e-4 * np.abs(ref[fin]))
+        idx, cnt = b["idx"][h], b["cnt"][h]
+        for qb in range(cnt.size):
+            diag = c0 // 64 + qb
+            sel = oracle.select_blocks(got[qb, :diag + 1], diag, 100)
+            assert cnt[qb] == sel.size and idx[qb, :sel.size].tolist() == sel.tolist(), qb
+        kept = lambda i: idx[(i - c0) // 64, :cnt[(i - c0) // 64]]  # noqa: E731
+        ro, rl, sizes = oracle.block_sparse_rows(b["q"][h].astype(np.float64), b["rows"], ctx,
+                                                 kept, res["sm"])
+        compare(b["out"][h].astype(np.float64), ro)
+        lse_compare(b["lse"][h].astype(np.float64), rl)
+    st = b["stats"]
+    assert st[0] >= st[1] > 0
+
+
+def test_a_shape_1m_sampled_rows():
+    """A-shape heads (sink 16, window 2048) at the 1M context: the filled
+    lists are the oracle's, and sampled rows match its attention."""
+    name = "7b_1m_dca"
+    cfg = CONFIGS[name]
+    res = run_layer(name)
+    a = res["a_shape"]
+    ov, os_ = oracle.a_shape_lists(16, 2048, cfg.seq_len)
+    for h in range(cfg.n_heads):
+        assert a["verts"][h].tolist() == ov.tolist() and a["slashes"][h].tolist() == os_.tolist()
+    for h in oracle_heads(cfg):
+        ctx = key_context(name, h // cfg.group)
+        ro, rl, _ = oracle.sparse_rows(a["q"][h].astype(np.float64), a["rows"], ctx, ov, os_,
+                                       res["sm"])
+        compare(a["out"][h].astype(np.float64), ro)
+        lse_compare(a["lse"][h].astype(np.float64), rl)
 
 
 @pytest.mark.parametrize("name", ["7b_1m_dca", "14b_256k"])
