@@ -259,7 +259,7 @@ def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
     ctx.k_dca()
     setup_s = time.perf_counter() - t_setup
     rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(np.arange(c0, c1), size=16384, replace=False))
+    rows = np.sort(rng.choice(np.arange(c0, c1), size=min(16384, c1 - c0), replace=False))
     qh = q[h, rows].float().cpu().numpy().astype(np.float64)
     sm = layer.sm_scale
     done, pairs = 0, 0
