@@ -1598,6 +1598,244 @@ __global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
   }
 }
 
+// Block-sparse attention with the tiles shared by the heads of a KV group:
+// one workgroup per (KV head g, 32-row block rb) holds one wave per query
+// head of the group (NW <= 7) and one loader wave.  The heads' lists for the
+// row block's query block are turned into per-head block bitmaps in LDS,
+// their union is compacted into an ascending tile list with a per-tile head
+// mask, and every union tile is streamed once (K then V, 32 loads) into a
+// three-stage ring; a head wave multiplies only the tiles its own list holds.
+// With the 7B grouping and 100 blocks per head, about 120 union tiles replace
+// 700 per-head ones per query block.
+constexpr int kBsgStages = 3;
+constexpr int kBsgMaxList = 2048;  // union tiles per workgroup (NW x max_blocks bound)
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * (NW + 1)) bs_attn_gqa_kernel(BsArgs a) {
+  using B = Buf<D>;
+  constexpr int M = B::kInstrPerMat;
+  constexpr int R = B::kRowsPerInstr;
+  constexpr int kStageBytes = 2 * B::kKBytes;
+  __shared__ __attribute__((aligned(16))) char stage[kBsgStages][kStageBytes];
+  __shared__ uint16_t tile_kb[kBsgMaxList];
+  __shared__ uint8_t tile_heads[kBsgMaxList];
+  __shared__ uint32_t n_tiles_sh;
+  extern __shared__ uint32_t bits[];  // [NW + 1][nw]: head bitmaps, then the union
+  const int rb = blockIdx.x, g = blockIdx.y;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int64_t qb = rb >> 1;
+  const int32_t diag = (int32_t)(a.c0 / kTileK + qb);
+  const int nw = diag / 32 + 1;
+  uint32_t* ubits = bits + NW * nw;
+  // ---------------- the union tile list
+  for (int x = threadIdx.x; x < (NW + 1) * nw; x += 64 * (NW + 1)) bits[x] = 0u;
+  __syncthreads();
+  if (w < NW) {
+    const int h = g * a.G + w;
+    if ((a.head_mask >> h) & 1ull) {
+      const int32_t* list = a.blk_idx + ((int64_t)h * a.n_qb + qb) * a.max_blocks;
+      int n = a.blk_cnt[(int64_t)h * a.n_qb + qb];
+      n = n < a.max_blocks ? n : a.max_blocks;
+      for (int x = lane; x < n; x += 64) {
+        int32_t kb = list[x];
+        kb = kb < 0 || kb > diag ? diag : kb;  // out-of-range entries: the diagonal
+        atomicOr(&bits[w * nw + (kb >> 5)], 1u << (kb & 31));
+      }
+    }
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < nw; x += 64 * (NW + 1)) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int hh = 0; hh < NW; ++hh) u |= bits[hh * nw + x];
+    ubits[x] = u;
+  }
+  __syncthreads();
+  if (w == NW) {
+    // ordered compaction of the union bitmap, 64 words per pass
+    uint32_t base = 0;
+    for (int x0 = 0; x0 < nw; x0 += 64) {
+      const int x = x0 + lane;
+      const uint32_t u = x < nw ? ubits[x] : 0u;
+      const uint32_t cnt = __popc(u);
+      uint32_t incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      uint32_t pos = base + incl - cnt;
+      uint32_t rest = u;
+      while (rest) {
+        const int b = __ffs(rest) - 1;
+        rest &= rest - 1;
+        if (pos < (uint32_t)kBsgMaxList) {
+          const int kb = x * 32 + b;
+          uint32_t hm = 0;
+#pragma unroll
+          for (int hh = 0; hh < NW; ++hh) hm |= ((bits[hh * nw + x] >> b) & 1u) << hh;
+          tile_kb[pos] = (uint16_t)kb;
+          tile_heads[pos] = (uint8_t)hm;
+        }
+        ++pos;
+      }
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) n_tiles_sh = base < (uint32_t)kBsgMaxList ? base : (uint32_t)kBsgMaxList;
+  }
+  __syncthreads();
+  const int n_local = (int)__builtin_amdgcn_readfirstlane(n_tiles_sh);
+  auto tile_of = [&](int i) {
+    const int32_t kb = (int32_t)__builtin_amdgcn_readfirstlane(tile_kb[i]);
+    Tile x;
+    x.ks = kb * kTileK;
+    x.n = (int32_t)(a.n_ctx - x.ks < kTileK ? a.n_ctx - x.ks : kTileK);
+    x.wave = -1;
+    x.kchunk = a.period ? (int32_t)(x.ks / a.period) : 0;
+    x.kmax = x.ks + x.n - 1;
+    x.gran = 15;
+    return x;
+  };
+  if (w == NW) {
+    // ---------------- loader: K then V of each union tile
+    const char* kbase = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
+    const char* vbase = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
+    const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
+    const uint32_t base = lds_addr(&stage[0][0]);
+    const int sub = lane / B::kChunks, cl = lane % B::kChunks;
+    auto issue = [&](int i) {
+      const Tile x = tile_of(i);
+      const int64_t off = (int64_t)x.ks * kvst_b;
+      const uint32_t dst = base + (uint32_t)((i % kBsgStages) * kStageBytes);
+#pragma unroll
+      for (int gm = 0; gm < M; ++gm) {
+        const int row = gm * R + sub;
+        const uint32_t rr = (uint32_t)(row < x.n ? row : x.n - 1);
+        dma16_s(kbase + off, rr * kvst_b + (uint32_t)swz_k<D>(cl, row) * 16u, dst + gm * 1024);
+      }
+#pragma unroll
+      for (int gm = 0; gm < M; ++gm) {
+        const int row = gm * R + sub;
+        const uint32_t rr = (uint32_t)(row < x.n ? row : x.n - 1);
+        dma16_s(vbase + off, rr * kvst_b + (uint32_t)swz_v<D>(cl, row) * 16u,
+                dst + B::kKBytes + gm * 1024);
+      }
+    };
+    for (int i = 0; i < kBsgStages - 1 && i < n_local; ++i) issue(i);
+    for (int i = 0; i < n_local; ++i) {
+      // tile i has landed; tile i + 1 may still be in flight
+      if (n_local - 1 - i >= 1) wait_vm<2 * M>();
+      else wait_vm<0>();
+      step_barrier();
+      if (i + kBsgStages - 1 < n_local) issue(i + kBsgStages - 1);
+    }
+    return;
+  }
+  // ---------------- head waves
+  const int hh = w;
+  const int h = g * a.G + hh;
+  const bool head_on = (a.head_mask >> h) & 1ull;
+  const int rho = lane & 31;
+  const int64_t row = a.c0 + (int64_t)rb * kRowBlock + rho;
+  const bool live = row < a.c0 + a.L;
+  const int64_t my_row = live ? row : a.c0 + a.L - 1;
+  const int64_t qchunk = a.period ? my_row / a.period : 0;
+  LaneConst<D> lc;
+  lane_consts<D>(lc, lane);
+  WaveState<D> st;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.o[db] = (f32x16){};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  int cur_var = -1;
+  unsigned long long sel = 0, exe = 0;
+  for (int i = 0; i < n_local; ++i) {
+    step_barrier();
+    const uint32_t heads = __builtin_amdgcn_readfirstlane(tile_heads[i]);
+    if (!head_on || !((heads >> hh) & 1u)) continue;
+    const Tile tt = tile_of(i);
+    const int64_t rel = qchunk - tt.kchunk;
+    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
+    if (__ballot(var != cur_var) != 0ull) {
+      const uint16_t* qp =
+          a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const bf16x8*>(qp + s2 * 16);
+      wait_vm<0>();
+      cur_var = var;
+    }
+    const int64_t lim = my_row - tt.ks + 1;
+    const uint64_t mword = low_bits(lim < tt.n ? lim : tt.n);
+    if (live && half == 0) sel += __popcll(mword);
+    ++exe;
+    const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+    const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+    const bool masked = __ballot(mword == ~0ull) != ~0ull;
+    const char* bc = stage[i % kBsgStages];
+    bf16x8 pf[4];
+    wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
+    wave_pv<D>(bc, lc, st, pf, act0, act1);
+  }
+  if (!head_on) return;
+  const float l_tot = sum_halves(st.l);
+  if (live) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t tr = row - a.c0;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * half;
+        const float v0 = st.o[db][4 * i4 + 0] * inv, v1 = st.o[db][4 * i4 + 1] * inv;
+        const float v2 = st.o[db][4 * i4 + 2] * inv, v3 = st.o[db][4 * i4 + 3] * inv;
+        if (a.out_dtype == LCSR_FP32) {
+          float* o = static_cast<float*>(a.out) + h * a.o_sh + tr * a.o_st + d;
+          o[0] = v0;
+          o[1] = v1;
+          o[2] = v2;
+          o[3] = v3;
+        } else {
+          uint16_t* o = static_cast<uint16_t*>(a.out) + h * a.o_sh + tr * a.o_st + d;
+          o[0] = f32_to_bf16(v0);
+          o[1] = f32_to_bf16(v1);
+          o[2] = f32_to_bf16(v2);
+          o[3] = f32_to_bf16(v3);
+        }
+      }
+    if (a.lse && half == 0)
+      a.lse[(int64_t)h * a.L + tr] = l_tot > 0.f ? (st.m + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  if (a.stats) {
+    unsigned long long se = sel;
+    for (int off = 32; off > 0; off >>= 1) se += __shfl_xor(se, off);
+    if (lane == 0) {
+      atomicAdd(&a.stats[0], exe * 32ull * kTileK);
+      atomicAdd(&a.stats[1], se);
+    }
+  }
+}
+
+template <int D>
+int launch_block_attn_gqa(const BsArgs& a, int nw, int64_t n_rb, int n_kv, hipStream_t s) {
+  const int64_t words = (a.c0 / kTileK + (n_rb - 1) / 2) / 32 + 1;  // of the last row block
+  const dim3 grid((unsigned)n_rb, (unsigned)n_kv);
+#define LCSR_BSG(NW)                                                                      \
+  hipLaunchKernelGGL((bs_attn_gqa_kernel<D, NW>), grid, dim3(64 * ((NW) + 1)),             \
+                     (size_t)((NW) + 1) * words * 4, s, a)
+  switch (nw) {
+    case 1: LCSR_BSG(1); break;
+    case 2: LCSR_BSG(2); break;
+    case 3: LCSR_BSG(3); break;
+    case 4: LCSR_BSG(4); break;
+    case 5: LCSR_BSG(5); break;
+    case 6: LCSR_BSG(6); break;
+    default: LCSR_BSG(7); break;
+  }
+#undef LCSR_BSG
+  return check_launch("block-sparse attention (shared tiles)");
+}
+
 template <int D>
 int launch_block_attn(const BsArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bs_attn_kernel<D, kBsStages>), dim3((unsigned)a.n_qb, (unsigned)a.H),
@@ -1807,6 +2045,13 @@ int run_block_attention(const lcsr_problem_t& p, const int32_t* idx, const int32
   a.o_st = o_st;
   a.lse = lse;
   a.stats = reinterpret_cast<unsigned long long*>(stats);
+  // tiles shared across the heads of a group when the union list fits in
+  // LDS; else one workgroup per (head, query block)
+  const int G = a.G;
+  const int64_t n_rb = (p.chunk_len + kRowBlock - 1) / kRowBlock;
+  if (G <= 7 && (int64_t)G * max_blocks <= kBsgMaxList)
+    return p.head_dim == 128 ? launch_block_attn_gqa<128>(a, G, n_rb, p.n_kv_heads, s)
+                             : launch_block_attn_gqa<64>(a, G, n_rb, p.n_kv_heads, s);
   return p.head_dim == 128 ? launch_block_attn<128>(a, s) : launch_block_attn<64>(a, s);
 }
 

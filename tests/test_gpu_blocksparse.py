@@ -143,6 +143,30 @@ def test_block_sparse_attention_rows():
     assert int(stats[1].item()) == pairs
 
 
+def test_shared_tiles_equal_per_head_kernel():
+    """Lists that fit the shared-tile kernel (G x max_blocks <= 2048) and the
+    same lists in wider buffers (per-head kernel) give bitwise the same rows:
+    each head multiplies its own blocks in the same ascending order."""
+    cfg = CFG
+    q, k, v = synth.generate(cfg, DEV)
+    layer = _layer(cfg)
+    build_cache(layer, k, v, cfg.seq_len)
+    c0, c1 = 3072, 4096
+    budgets = [4, 8, 1, 12, 6, 3, 20] * 2
+    pat, _ = _estimate(layer, q, c0, c1, budgets, 20)
+    wide = L.BlockPattern(cfg.n_heads, pat.idx.shape[1], 300, DEV)
+    wide.idx[:, :, :20] = pat.idx
+    wide.cnt.copy_(pat.cnt)
+    outs = []
+    for pt in (pat, wide):
+        o, lse = L.block_sparse_attn_prefill(
+            q[:, c0:c1], layer.k_cache[:, :c1], layer.v_cache[:, :c1], c0, layer.rope,
+            layer.dca, layer.sm_scale, pt, lse=torch.empty(cfg.n_heads, c1 - c0, device=DEV))
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_block_recall_rows():
     """lcsr_block_sparse_recall_check against the oracle: lse over the kept
     blocks, lse over every causal key, recall = exp of the difference."""
