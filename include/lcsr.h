@@ -53,6 +53,10 @@ extern "C" {
 #define LCSR_EWORKSPACE (-3) /* workspace smaller than lcsr_workspace_bytes()   */
 #define LCSR_EHIP (-4)       /* a HIP launch failed                             */
 
+/* Zero-length calls.  chunk_len 0 (or n_rows 0 for the recall checks) is a
+ * valid call that launches nothing and writes nothing; output pointers may
+ * then be NULL. */
+
 /* ---- element types ----------------------------------------------------- */
 #define LCSR_BF16 0
 #define LCSR_FP32 1

@@ -132,7 +132,8 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // chunk must start on a 64-token tile
 int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = false) {
   if (!p) return fail(LCSR_EINVAL, "problem is NULL");
-  if (!p->q || !p->k_cache || (need_v && !p->v_cache))
+  // an empty chunk reads no query (its pointer may be NULL)
+  if ((!p->q && p->chunk_len > 0) || !p->k_cache || (need_v && !p->v_cache))
     return fail(LCSR_EINVAL, "q/k_cache/v_cache pointer is NULL");
   if (!aligned16(p->q) || !aligned16(p->k_cache) || (need_v && !aligned16(p->v_cache)))
     return fail(LCSR_EINVAL, "q/k_cache/v_cache must be 16-byte aligned");
@@ -336,7 +337,8 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
     rc = validate_pattern(p, pat, false);
     if (rc) return rc;
   }
-  if (!out || !aligned16(out)) return fail(LCSR_EINVAL, "out must be non-NULL and 16-byte aligned");
+  if (p->chunk_len > 0 && (!out || !aligned16(out)))
+    return fail(LCSR_EINVAL, "out must be non-NULL and 16-byte aligned");
   if (out_dtype != LCSR_FP32 && out_dtype != LCSR_BF16)
     return fail(LCSR_EINVAL, "out_dtype must be LCSR_FP32 or LCSR_BF16");
   if (o_stride_t < p->head_dim || o_stride_h < p->head_dim || o_stride_t % 8 || o_stride_h % 8)
@@ -373,7 +375,8 @@ int lcsr_block_sparse_estimate(const lcsr_problem_t* p, const int32_t* n_blocks,
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
-  if (!blk_idx || !blk_cnt) return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
+  if ((!blk_idx || !blk_cnt) && p->chunk_len > 0)
+    return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
   if (!n_blocks) return fail(LCSR_EINVAL, "n_blocks is NULL");
   const bool select_only = flags & LCSR_BS_SELECT_ONLY;
   if (select_only && !scores) return fail(LCSR_EINVAL, "LCSR_BS_SELECT_ONLY needs the scores");
@@ -402,8 +405,9 @@ int lcsr_block_sparse_attn_prefill(const lcsr_problem_t* p, const int32_t* blk_i
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
-  if (!blk_idx || !blk_cnt) return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
-  if (!out) return fail(LCSR_EINVAL, "out must not be NULL");
+  if ((!blk_idx || !blk_cnt) && p->chunk_len > 0)
+    return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
+  if (!out && p->chunk_len > 0) return fail(LCSR_EINVAL, "out must not be NULL");
   if (out_dtype != LCSR_FP32 && out_dtype != LCSR_BF16)
     return fail(LCSR_EINVAL, "out_dtype must be LCSR_FP32 or LCSR_BF16");
   if (o_stride_t < p->head_dim || o_stride_h < p->head_dim)
@@ -429,7 +433,8 @@ int lcsr_attn_decode(const lcsr_problem_t* p, void* out, int32_t out_dtype,
   if ((int64_t)G * p->chunk_len > 32)
     return fail(LCSR_ENOTSUP, "decode takes (n_heads / n_kv_heads) x chunk_len <= 32 rows, got "
                 "%d x %lld", G, (long long)p->chunk_len);
-  if (!out || !aligned16(out)) return fail(LCSR_EINVAL, "out must be non-NULL and 16-byte aligned");
+  if (p->chunk_len > 0 && (!out || !aligned16(out)))
+    return fail(LCSR_EINVAL, "out must be non-NULL and 16-byte aligned");
   if (out_dtype != LCSR_FP32 && out_dtype != LCSR_BF16)
     return fail(LCSR_EINVAL, "out_dtype must be LCSR_FP32 or LCSR_BF16");
   if (o_stride_t < p->head_dim || o_stride_h < p->head_dim)
@@ -474,7 +479,8 @@ int lcsr_block_sparse_recall_check(const lcsr_problem_t* p, const int32_t* blk_i
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
-  if (!blk_idx || !blk_cnt) return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
+  if ((!blk_idx || !blk_cnt) && p->chunk_len > 0)
+    return fail(LCSR_EINVAL, "blk_idx / blk_cnt must not be NULL");
   if (n_rows < 0) return fail(LCSR_EINVAL, "n_rows must be >= 0");
   if (n_rows > 0 && (!rows || !lse_full || !lse_sparse || !recall))
     return fail(LCSR_EINVAL, "rows and the three outputs must be non-NULL");

@@ -246,3 +246,30 @@ def test_tiny_ragged_chunk_bf16_out():
                                         layer.sm_scale)
     d = np.abs(host64(out[0]) - ro)
     assert np.all(d <= 1e-2 + 2.0 ** -9 * np.abs(ro)), d.max()
+
+
+def test_empty_chunk_is_a_no_op():
+    """chunk_len 0: the block estimate, attention and recall succeed and write
+    nothing; a decode call with no rows too."""
+    cfg = CFG
+    q, k, v = synth.generate(cfg, DEV)
+    layer = _layer(cfg)
+    build_cache(layer, k, v, 1024)
+    H = cfg.n_heads
+    pat = L.BlockPattern(H, 1, 4, DEV)
+    pat.idx.fill_(7)
+    pat.cnt.fill_(3)
+    q0 = q[:, 1024:1024]
+    L.block_sparse_estimate(q0, layer.k_cache[:, :1024], 1024, layer.rope, layer.dca,
+                            layer.sm_scale, [4] * H, pat)
+    out = torch.full((H, 0, cfg.head_dim), 5.0, device=DEV)
+    L.block_sparse_attn_prefill(q0, layer.k_cache[:, :1024], layer.v_cache[:, :1024], 1024,
+                                layer.rope, layer.dca, layer.sm_scale, pat, out=out)
+    rows = torch.zeros(0, dtype=torch.int32, device=DEV)
+    lf, _, _ = L.block_sparse_recall_check(q0, layer.k_cache[:, :1024], 1024, layer.rope,
+                                           layer.dca, layer.sm_scale, pat, rows)
+    od, _ = L.attn_decode(q0, layer.k_cache[:, :1024], layer.v_cache[:, :1024], 1024,
+                          layer.rope, layer.dca, layer.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.all(pat.idx == 7) and torch.all(pat.cnt == 3)
+    assert lf.numel() == 0 and od.numel() == 0
