@@ -238,10 +238,13 @@ def decode_points(cfg, layer, q, row_counts, reps=20):
     return res
 
 
-def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
+def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0, step_pairs=None):
     """Time the fp64 oracle on a bounded sample of the same workload: sparse
     attention rows of the last chunk (first query head, the GPU's own
-    pattern), as many as fit in about `budget_s` seconds."""
+    pattern), as many as fit in about `budget_s` seconds.  With the step's
+    selected pair count, the time of the whole layer's sparse attention on
+    the oracle is extrapolated from the measured seconds per pair (labelled
+    as extrapolated; it is not run)."""
     import oracle
     from threadpoolctl import threadpool_info
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
@@ -271,7 +274,11 @@ def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0):
         done = blk.stop
     el = time.perf_counter() - t0
     flops = 4.0 * cfg.head_dim * pairs
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    extra = {}
+    if step_pairs:
+        extra["extrapolated_layer_s"] = round(el / max(pairs, 1) * step_pairs, 1)
+    return {**extra, "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
             "sample": (f"fp64 sparse attention of {done} sampled rows of the last 32K chunk "
                        f"(query head 0, GPU pattern), {el:.1f} s after {setup_s:.1f} s of "
@@ -376,7 +383,7 @@ def main():
                                       [int(x) for x in args.decode_rows.split(",")])
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, layer, q, k, v, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(cfg, layer, q, k, v, args.cpu_seconds, sel_pairs)
     print(json.dumps(rec), flush=True)
 
 
