@@ -236,7 +236,24 @@ __global__ void __launch_bounds__(256) bs_select(SelectArgs a) {
   kk -= 1;  // earlier blocks to keep
   int32_t* out = a.idx + ((int64_t)h * a.n_qb + qb) * a.max_blocks;
   const float* sc = a.scores + ((int64_t)h * a.n_qb + qb) * a.n_kb;
-  for (int i = tid; i < n; i += 256) keys[i] = order_key(sc[i]);
+  // the row's scores as order keys: 16-byte loads, several in flight per
+  // thread, when the row start is 16-byte aligned
+  if ((((uintptr_t)sc) & 15u) == 0) {
+    const int n4 = n / 4;
+    const float4* sc4 = reinterpret_cast<const float4*>(sc);
+#pragma unroll 4
+    for (int i = tid; i < n4; i += 256) {
+      const float4 x = sc4[i];
+      keys[4 * i] = order_key(x.x);
+      keys[4 * i + 1] = order_key(x.y);
+      keys[4 * i + 2] = order_key(x.z);
+      keys[4 * i + 3] = order_key(x.w);
+    }
+    for (int i = 4 * n4 + tid; i < n; i += 256) keys[i] = order_key(sc[i]);
+  } else {
+#pragma unroll 8
+    for (int i = tid; i < n; i += 256) keys[i] = order_key(sc[i]);
+  }
   __syncthreads();
   uint32_t prefix = 0, mask = 0, need = (uint32_t)kk;
   const bool partial = kk > 0 && kk < n;  // uniform
