@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from synth.configs import SEVEN_B_128K, TINY, scaled
+from synth.configs import FOURTEEN_B_256K, SEVEN_B_128K, TINY, scaled
 from tests.gpu_util import (DEV, build_cache, compare, dca_of, host64, lse_compare,
                             oracle_freqs, oracle_inputs, rope_of)
 
@@ -22,6 +22,11 @@ L = pytest.importorskip("long_context_sparse_rope_amd")
 # sees keys in DCA chunks 0 .. 5
 CFG = scaled(SEVEN_B_128K, n_heads=14, n_kv_heads=2, seq_len=4096, prefill_chunk=1024,
              dca_chunk=1024, dca_local=256, n_vert=64, n_slash=128)
+
+
+# the 14B grouping (5 query heads per KV head) at the same small shape
+CFG14 = scaled(FOURTEEN_B_256K, n_heads=10, n_kv_heads=2, seq_len=4096, prefill_chunk=1024,
+               dca_chunk=1024, dca_local=256, n_vert=64, n_slash=128)
 
 
 def _layer(cfg):
@@ -110,13 +115,13 @@ def test_selection_ties_and_signed_zeros():
     _check_selection(pat, sc, c0, budgets)
 
 
-def test_block_sparse_attention_rows():
-    cfg = CFG
+@pytest.mark.parametrize("cfg", [CFG, CFG14], ids=["group7", "group5"])
+def test_block_sparse_attention_rows(cfg):
     q, k, v = synth.generate(cfg, DEV)
     layer = _layer(cfg)
     build_cache(layer, k, v, cfg.seq_len)
     c0, c1 = 3072, 4096
-    budgets = [4, 8, 1, 12, 6, 3, 20] * 2
+    budgets = ([4, 8, 1, 12, 6, 3, 20] * 2)[:cfg.n_heads]
     pat, _ = _estimate(layer, q, c0, c1, budgets, 20)
     H, n, D = cfg.n_heads, c1 - c0, cfg.head_dim
     out = torch.empty(H, n, D, device=DEV)
