@@ -38,7 +38,7 @@ from .dca import (dca_position_maps, dca_chunk_of, query_positions,
 from .attention import (KeyContext, attention_logits, dense_causal_rows,
                         critical_set, sparse_rows, attention_recall)
 from .estimate import estimate_scores, select_top, select_pattern
-from .refine import refine_budgets
+from .refine import refine_budgets, refine_sizes
 from .patterns import a_shape_set, a_shape_lists, choose_candidates
 from .blocksparse import (BLOCK, block_scores, select_blocks, block_key_set,
                           block_sparse_rows)

@@ -115,3 +115,17 @@ def test_choose_candidates_nested_budgets():
     assert rec[-1] == pytest.approx(1.0, abs=1e-14)
     choice = oracle.choose_candidates(np.array(rec)[:, None])[0]
     assert rec[choice] == max(rec) and all(r < max(rec) for r in rec[:choice])
+
+
+def test_refine_sizes_hand_cases():
+    """One refinement round over mixed kinds (threshold 0.9, 1000 keys =
+    16 key blocks): low heads double their own size, capped; others stay."""
+    kinds = ["vs", "vs", "block", "block", "a_shape", "a_shape", "vs"]
+    sizes = [(10, 20), (10, 20), (3,), (10,), (4, 300), (4, 1000), (1000, 1000)]
+    rec = [0.5, 0.95, 0.2, 0.3, 0.1, 0.1, 0.1]
+    new, raised = oracle.refine_sizes(rec, kinds, sizes, 1000)
+    assert new == [(20, 40), (10, 20), (6,), (16,), (4, 600), (4, 1000), (1000, 1000)]
+    assert raised.tolist() == [True, False, True, True, True, False, False]
+    # the vertical-slash rule is the existing one
+    nv, ns, r2 = oracle.refine_budgets(rec[:2], [10, 10], [20, 20], 1000)
+    assert [tuple(x) for x in zip(nv, ns)] == new[:2] and r2.tolist() == raised[:2].tolist()
