@@ -108,6 +108,10 @@ class ChunkedSparsePrefill:
             bp = self.block_pattern
             if bp is None or bp.idx.shape[1] != n_qb or bp.max_blocks < mb:
                 self.block_pattern = ops.BlockPattern(self.H, n_qb, mb, self.device)
+                if bp is not None and bp.idx.shape[1] == n_qb:
+                    # rows of heads not estimated now keep their lists
+                    self.block_pattern.idx[:, :, :bp.max_blocks] = bp.idx
+                    self.block_pattern.cnt.copy_(bp.cnt)
             ops.block_sparse_estimate(
                 q_chunk, self.k_cache[:, :c1], chunk_start, self.rope, self.dca, self.sm_scale,
                 [b or 1 for b in self.blocks], self.block_pattern, head_mask=blk)
@@ -173,27 +177,46 @@ class ChunkedSparsePrefill:
     def refine_chunk(self, q_chunk, chunk_start, rows, out, lse=None, threshold=0.9,
                      max_rounds=3):
         """Sparsity refinement for one chunk: heads whose mean recall over
-        `rows` is under the threshold get doubled budgets (capped at the
-        number of keys), are re-estimated and re-attended; at most
-        `max_rounds` rounds.  Raised budgets carry over to later chunks.
-        A-shape and block-sparse heads keep their pattern.  Returns the
-        per-round head recalls (host tensors)."""
+        `rows` is under the threshold grow, are re-estimated (or re-filled)
+        and re-attended; at most `max_rounds` rounds.  A vertical-slash head
+        doubles both budgets (capped at the number of keys), a block-sparse
+        head its kept blocks (capped at the key blocks), an A-shape head its
+        window (capped at the number of keys; the sinks stay).  Raised sizes
+        carry over to later chunks.  Returns the per-round head recalls (host
+        tensors)."""
         c1 = chunk_start + q_chunk.shape[1]
         history = []
         for _ in range(max_rounds + 1):
             _, _, rec = self.recall(q_chunk, chunk_start, rows)
             mean = rec.mean(dim=1).cpu()
             history.append(mean)
-            low = [bool(mean[h] < threshold) and self.a_shape[h] is None and
-                   self.blocks[h] is None and
-                   (self.n_vert[h] < c1 or self.n_slash[h] < c1) for h in range(self.H)]
+            n_kb = -(-c1 // 64)
+
+            def can_grow(h):
+                if self.blocks[h] is not None:
+                    return self.blocks[h] < n_kb
+                if self.a_shape[h] is not None:
+                    return self.a_shape[h][1] < c1
+                return self.n_vert[h] < c1 or self.n_slash[h] < c1
+
+            low = [bool(mean[h] < threshold) and can_grow(h) for h in range(self.H)]
             if len(history) > max_rounds or not any(low):
                 break
             for h in range(self.H):
-                if low[h]:
+                if not low[h]:
+                    continue
+                if self.blocks[h] is not None:
+                    self.blocks[h] = min(2 * self.blocks[h], n_kb)
+                elif self.a_shape[h] is not None:
+                    s_, w_ = self.a_shape[h]
+                    self.a_shape[h] = (s_, min(2 * w_, c1))
+                else:
                     self.n_vert[h] = min(2 * self.n_vert[h], c1)
                     self.n_slash[h] = min(2 * self.n_slash[h], c1)
-            need_v, need_s = max(self.n_vert), max(self.n_slash)
+            need_v = max([self.n_vert[h] for h in range(self.H)] +
+                         [a[0] for a in self.a_shape if a])
+            need_s = max([self.n_slash[h] for h in range(self.H)] +
+                         [a[1] for a in self.a_shape if a])
             if need_v > self.pattern.max_vert or need_s > self.pattern.max_slash:
                 old = self.pattern
                 self.pattern = ops.Pattern(self.H, max(need_v, old.max_vert),

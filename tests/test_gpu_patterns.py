@@ -195,3 +195,71 @@ def test_search_head_patterns(cfg):
             assert choice[h] == best[h], h
         else:
             assert ref[choice[h], h] >= ref[best[h], h] - 1e-2, h
+
+
+def test_refinement_over_mixed_kinds():
+    """Refinement on the stripes layer with vertical-slash, block-sparse and
+    A-shape heads at small sizes: every round's decisions are the oracle's
+    rule applied to the GPU's recall, raised heads do not lose recall (their
+    sets are nested), and the final rows match the oracle on the final
+    patterns."""
+    cfg = CFG_STRIPES
+    q, k, v = synth.generate(cfg, DEV)
+    layer = _layer(cfg)
+    build_cache(layer, k, v, cfg.seq_len)
+    kinds = [VS(8, 16), BS(2), AS(4, 64), VS(32, 8), BS(1)]
+    configs = [kinds[h % len(kinds)] for h in range(cfg.n_heads)]
+    layer.set_head_patterns(configs)
+    c0, c1 = 3072, 4096
+    qc = q[:, c0:c1]
+    out = torch.empty(cfg.n_heads, c1 - c0, cfg.head_dim, device=DEV)
+    lse = torch.empty(cfg.n_heads, c1 - c0, device=DEV)
+    layer.estimate(qc, c0)
+    layer.attend(qc, c0, out=out, lse=lse)
+    rng = np.random.default_rng(11)
+    off = np.unique(np.concatenate([np.arange(1024 - 64, 1024), rng.integers(0, 1024, 32)]))
+    rows = torch.tensor(off, dtype=torch.int32, device=DEV)
+
+    def sizes():
+        res = []
+        for h in range(cfg.n_heads):
+            if layer.blocks[h] is not None:
+                res.append((layer.blocks[h],))
+            elif layer.a_shape[h] is not None:
+                res.append(tuple(layer.a_shape[h]))
+            else:
+                res.append((layer.n_vert[h], layer.n_slash[h]))
+        return res
+
+    kind_of = [c["kind"] for c in configs]
+    start = sizes()
+    hist = layer.refine_chunk(qc, c0, rows, out, lse=lse, threshold=0.9, max_rounds=3)
+    torch.cuda.synchronize()
+    cur = start
+    for r in range(len(hist) - 1):
+        nxt, raised = oracle.refine_sizes(hist[r].numpy(), kind_of, cur, c1)
+        assert raised.any()
+        assert np.all(hist[r + 1].numpy()[raised] >= hist[r].numpy()[raised] - 1e-5)
+        cur = nxt
+    final, _ = oracle.refine_sizes(hist[-1].numpy(), kind_of, cur, c1)
+    assert sizes() == cur, (sizes(), cur)
+    print(f"[refine] {len(hist) - 1} rounds; sizes {start} -> {cur}", flush=True)
+    # final rows against the oracle on the final patterns
+    verts, slashes = layer.pattern.lists()
+    bidx, bcnt = layer.block_pattern.idx.cpu().numpy(), layer.block_pattern.cnt.cpu().numpy()
+    qo, _, _ = oracle_inputs(q, k[:1], v[:1])
+    ctxs = _contexts(cfg, k, v, c1)
+    G = cfg.n_heads // cfg.n_kv_heads
+    r = c0 + off
+    for h in range(cfg.n_heads):
+        if layer.blocks[h] is not None:
+            kept = lambda i, h=h: bidx[h, (i - c0) // 64, :bcnt[h, (i - c0) // 64]]  # noqa
+            ro, rl, _ = oracle.block_sparse_rows(qo[h, r], r, ctxs[h // G], kept, layer.sm_scale)
+        else:
+            if layer.a_shape[h] is not None:
+                ov, os_ = oracle.a_shape_lists(*layer.a_shape[h], c1)
+            else:
+                ov, os_ = verts[h].numpy(), slashes[h].numpy()
+            ro, rl, _ = oracle.sparse_rows(qo[h, r], r, ctxs[h // G], ov, os_, layer.sm_scale)
+        compare(host64(out[h, off]), ro)
+        lse_compare(host64(lse[h, off]), rl)
