@@ -103,3 +103,33 @@ def test_decode_matches_dense_prefill_rows(tiny):
                              layer.sm_scale)
     d = (out_p - out_d).abs().max().item()
     assert d <= 1e-3, d
+
+
+def test_decode_graph_replay(tiny):
+    """The decode call with caller-owned output, lse and workspace launches
+    kernels only, so it can be captured in a HIP graph: every replay (with
+    eager work and synchronisations between them, and new query values
+    copied into the captured input) equals the eager call."""
+    cfg, q, k, v, layer = tiny
+    p0, n = 1000, 8
+    qs = q[:, p0:p0 + n].clone()
+    args = (layer.k_cache[:, :p0 + n], layer.v_cache[:, :p0 + n], p0, layer.rope, layer.dca,
+            layer.sm_scale)
+    ws = torch.empty(L.workspace_bytes(L._capi.LCSR_WS_DECODE, qs, args[0], p0, layer.rope,
+                                       layer.dca), dtype=torch.uint8, device=DEV)
+    out = torch.empty(cfg.n_heads, n, cfg.head_dim, device=DEV)
+    lse = torch.empty(cfg.n_heads, n, device=DEV)
+    L.attn_decode(qs, *args, out=out, lse=lse, workspace=ws)   # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.attn_decode(qs, *args, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src = q[:, p0 - 100 * rep:p0 - 100 * rep + n]
+        qs.copy_(src)
+        ref_o, _ = L.attn_decode(src.contiguous(), *args, lse=(ref_l := torch.empty_like(lse)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), rep
