@@ -1,8 +1,14 @@
-"""Thin Python binding of the five C-ABI calls (argument marshalling only).
+"""Thin Python binding of the C-ABI calls (argument marshalling only).
 
 Each function has the name of its C entry point without the ``lcsr_``
 prefix.  Tensors are torch device tensors (PyTorch supplies device memory
 and the stream); every computation runs in liblcsr.so.
+
+Workspaces: a call without a ``workspace`` argument uses one buffer per
+call kind and device, cached here and grown on demand.  Calls of the same
+kind that may overlap (on different streams) must each pass a workspace of
+their own (sized with ``workspace_bytes``); calls on one stream are ordered
+and can share the cached one.
 """
 
 import ctypes
