@@ -304,7 +304,7 @@ def main():
                     help="rows per decode-step point over the full cache ('' for none)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU (one KV-head shard per GPU is the multi-GPU layout); --gpus must be 1"}))
         sys.exit(2)
 
     cfg = CONFIGS[args.config]
