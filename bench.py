@@ -7,8 +7,8 @@ inputs resident in HBM.  Default workload: the 7B-shaped layer (28 query /
 4 KV heads, head_dim 128, bf16) at 1,048,576 tokens with DCA (C = 262,144,
 W = 32,768), YaRN s = 4, budgets 1000 verticals + 6096 slashes.
 
-Prints one JSON line (see the keys below).  --gpus above 1 is refused: this
-build runs on one GPU.
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: the
+benchmark runs on one GPU.
 """
 
 import argparse
