@@ -337,7 +337,13 @@ def main():
     exe_pairs = st[0] / args.steps
     alg_flops = 4.0 * cfg.head_dim * sel_pairs            # per step
     exe_flops = 4.0 * cfg.head_dim * exe_pairs
-    stages = {k_: sum(v_) / args.steps for k_, v_ in timer.totals().items()}
+    totals = timer.totals()
+    stages = {k_: sum(v_) / args.steps for k_, v_ in totals.items()}
+    # attention ms of each chunk (mean over the timed steps): the cost grows
+    # as the selected slashes spread over a longer context
+    att = totals.get("attention", [])
+    att_chunks = [round(sum(att[c::cfg.n_chunks]) / args.steps, 3) for c in range(cfg.n_chunks)] \
+        if len(att) == cfg.n_chunks * args.steps else []
     attn_calls = cfg.n_chunks
     attn_ms_call = stages["attention"] / attn_calls
     achieved = alg_flops / attn_calls / (attn_ms_call * 1e-3) / 1e12
@@ -361,6 +367,7 @@ def main():
                    "dca_local": cfg.dca_local, "yarn_factor": cfg.yarn_factor,
                    "n_vert": cfg.n_vert, "n_slash": cfg.n_slash, "out_dtype": "bf16"},
         "stage_ms": {k_: round(v_, 3) for k_, v_ in stages.items()},
+        "attention_ms_per_chunk": att_chunks,
         "algorithmic_tflop_per_step": round(alg_flops / 1e12, 3),
         "executed_tflop_per_step": round(exe_flops / 1e12, 3),
         "waste_ratio": round(exe_pairs / max(sel_pairs, 1), 3),
