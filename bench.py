@@ -65,7 +65,7 @@ def make_layer(cfg, dev):
     rope = L.RopeConfig(base=cfg.rope_base, yarn_factor=cfg.yarn_factor,
                         orig_max_pos=cfg.yarn_orig_max_pos)
     dca = L.DcaConfig(cfg.dca_chunk, cfg.dca_local)
-    sm = L.yarn_softmax_scale(cfg.head_dim, cfg.yarn_factor)
+    sm = L.softmax_scale(cfg.head_dim, rope)
     return L.ChunkedSparsePrefill(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, rope,
                                   dca, sm, cfg.n_vert, cfg.n_slash, cfg.last_q, dev)
 

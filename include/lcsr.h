@@ -82,8 +82,8 @@ extern "C" {
  * yarn_factor s > 1, theta_p is blended as YaRN's NTK-by-parts:
  * r_p = orig_max_pos * theta_p / (2 pi), g_p = clamp((r_p - beta_slow) /
  * (beta_fast - beta_slow), 0, 1), theta_p <- theta_p ((1 - g_p)/s + g_p).
- * The YaRN temperature is not applied here: callers pass it in sm_scale
- * (sm_scale = (0.1 ln s + 1)^2 / sqrt(D)). */
+ * The YaRN temperature is not applied here: the attention calls take it
+ * in sm_scale (lcsr_softmax_scale). */
 typedef struct lcsr_rope {
   double base;          /* RoPE base, e.g. 1e4 or 1e7                       */
   double yarn_factor;   /* s = inference length / training length; <=1 off */
@@ -127,7 +127,8 @@ typedef struct lcsr_problem {
   int64_t chunk_len;
   lcsr_rope_t rope;
   lcsr_dca_t dca;
-  float sm_scale;      /* 1 / (t sqrt(D)), the YaRN temperature folded in   */
+  float sm_scale;      /* 1 / (t sqrt(D)), the YaRN temperature folded in
+                          (lcsr_softmax_scale gives it from rope)          */
 } lcsr_problem_t;
 
 /* Vertical-slash pattern of every head.  vert_idx[h, :vert_cnt[h]] are key
@@ -151,6 +152,16 @@ size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p,
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* lcsr_last_error(void);
+
+/* lcsr_softmax_scale — the logit scale every attention call takes in
+ * lcsr_problem_t.sm_scale: 1 / (t sqrt(head_dim)) with the YaRN attention
+ * temperature sqrt(1/t) = 0.1 ln(s) + 1, s = rope->yarn_factor
+ * ([Qwen2.5-1M explainer] Length Extrapolation, YaRN Attention Scaling);
+ * s <= 1 means no temperature, 1 / sqrt(head_dim).  Formed in double and
+ * returned rounded to float.  Host only; launches nothing.
+ * Errors: returns 0 (message in lcsr_last_error) for a NULL rope,
+ * head_dim <= 0 or a yarn_factor that is NaN or infinite. */
+float lcsr_softmax_scale(const lcsr_rope_t* rope, int32_t head_dim);
 
 /* lcsr_rope_yarn_apply — y[h, t, :] = scale * R(pos[t]) x[h, t, :], stored
  * bf16.  Rotation pairs (x_p, x_{p+D/2}) turn by pos[t] * theta_p

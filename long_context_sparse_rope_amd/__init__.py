@@ -7,7 +7,7 @@ fails loudly if it has not been built.
 """
 
 from . import _capi
-from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, yarn_softmax_scale,
+from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, softmax_scale,
                   rope_yarn_apply, dca_positions, vs_pattern_estimate,
                   vs_sparse_attn_prefill, attn_decode, attn_recall_check, workspace_bytes,
                   pattern_fill_a_shape, BlockPattern, block_sparse_estimate,
@@ -16,7 +16,7 @@ from .driver import ChunkedSparsePrefill, search_head_patterns
 
 _capi.load()
 
-__all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "yarn_softmax_scale",
+__all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "softmax_scale",
            "rope_yarn_apply", "dca_positions", "vs_pattern_estimate",
            "vs_sparse_attn_prefill", "attn_decode", "attn_recall_check", "workspace_bytes",
            "pattern_fill_a_shape", "BlockPattern", "block_sparse_estimate",

@@ -27,7 +27,8 @@ LCSR_WS_DECODE = 3
 LCSR_WS_BLOCK_EST = 4
 LCSR_WS_BLOCK_ATTN = 5
 
-EXPORTED = ("lcsr_workspace_bytes", "lcsr_last_error", "lcsr_rope_yarn_apply",
+EXPORTED = ("lcsr_workspace_bytes", "lcsr_last_error", "lcsr_softmax_scale",
+            "lcsr_rope_yarn_apply",
             "lcsr_dca_positions", "lcsr_vs_pattern_estimate",
             "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_recall_check",
             "lcsr_pattern_fill_a_shape", "lcsr_block_sparse_estimate",
@@ -85,6 +86,8 @@ def load():
     lib.lcsr_workspace_bytes.argtypes = [ctypes.c_int, P(lcsr_problem_t), i32, i32]
     lib.lcsr_last_error.restype = ctypes.c_char_p
     lib.lcsr_last_error.argtypes = []
+    lib.lcsr_softmax_scale.restype = ctypes.c_float
+    lib.lcsr_softmax_scale.argtypes = [P(lcsr_rope_t), i32]
     lib.lcsr_rope_yarn_apply.restype = ctypes.c_int
     lib.lcsr_rope_yarn_apply.argtypes = [vp, i32, i64, i64, vp, i64, i64, i64, i64, i64, vp,
                                          P(lcsr_rope_t), f32, u32, vp]

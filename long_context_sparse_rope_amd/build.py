@@ -22,7 +22,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
-             "-packed-fp32-ops", "-munsafe-fp-atomics"]
+             "-packed-fp32-ops"]
 
 
 def sources():

@@ -202,6 +202,25 @@ extern "C" {
 
 const char* lcsr_last_error(void) { return g_err; }
 
+float lcsr_softmax_scale(const lcsr_rope_t* rope, int32_t head_dim) {
+  if (!rope) {
+    set_error("rope is NULL");
+    return 0.0f;
+  }
+  if (head_dim <= 0) {
+    set_error("head_dim must be > 0, got %d", head_dim);
+    return 0.0f;
+  }
+  const double s = rope->yarn_factor;
+  if (!std::isfinite(s)) {
+    set_error("yarn_factor must be finite");
+    return 0.0f;
+  }
+  // sqrt(1/t) = 0.1 ln s + 1 for s > 1; no temperature otherwise
+  const double m = s > 1.0 ? 0.1 * std::log(s) + 1.0 : 1.0;
+  return (float)(m * m / std::sqrt((double)head_dim));
+}
+
 size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert,
                             int32_t max_slash) {
   if (!p || validate_problem(p, false, which == LCSR_WS_DECODE) != LCSR_OK) return 0;

@@ -19,9 +19,20 @@ Every numeric step runs in liblcsr.so; this module only sequences the calls
 on one stream and owns the KV cache buffers.
 """
 
+import math
+
+import numpy as np
 import torch
 
 from . import ops
+
+
+def _head_means(recall):
+    """Mean recall of each head over its sampled rows, formed on the host
+    from the copied fp32 recalls (exactly rounded sums, so the order of the
+    rows does not matter)."""
+    r = recall.cpu().numpy().astype(np.float64)
+    return np.array([math.fsum(row) / row.size for row in r])
 
 
 class ChunkedSparsePrefill:
@@ -183,12 +194,12 @@ class ChunkedSparsePrefill:
         head its kept blocks (capped at the key blocks), an A-shape head its
         window (capped at the number of keys; the sinks stay).  Raised sizes
         carry over to later chunks.  Returns the per-round head recalls (host
-        tensors)."""
+        float64 arrays)."""
         c1 = chunk_start + q_chunk.shape[1]
         history = []
         for _ in range(max_rounds + 1):
             _, _, rec = self.recall(q_chunk, chunk_start, rows)
-            mean = rec.mean(dim=1).cpu()
+            mean = _head_means(rec)
             history.append(mean)
             n_kb = -(-c1 // 64)
 
@@ -265,12 +276,12 @@ def search_head_patterns(layer, q, chunks, candidates, rows):
     with the highest score, the earlier one on an exact tie.  The layer's own
     configuration is restored afterwards.
 
-    Returns (choice: list of H candidate indices, scores: fp64 host tensor
+    Returns (choice: list of H candidate indices, scores: float64 array
     [n_candidates, H]).
     """
     saved = (list(layer.n_vert), list(layer.n_slash), list(layer.a_shape), list(layer.blocks))
     H = layer.H
-    scores = torch.zeros(len(candidates), H, dtype=torch.float64)
+    scores = np.zeros((len(candidates), H))
     try:
         for ci, cand in enumerate(candidates):
             layer.set_head_patterns([cand] * H)
@@ -278,7 +289,7 @@ def search_head_patterns(layer, q, chunks, candidates, rows):
                 r = rows[k] if isinstance(rows, (list, tuple)) else rows
                 layer.estimate(q[:, c0:c0 + n], c0)
                 _, _, rec = layer.recall(q[:, c0:c0 + n], c0, r)
-                scores[ci] += rec.double().mean(dim=1).cpu()
+                scores[ci] += _head_means(rec)
             scores[ci] /= len(chunks)
     finally:
         layer.n_vert, layer.n_slash, layer.a_shape, layer.blocks = saved

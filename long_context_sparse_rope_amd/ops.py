@@ -12,7 +12,6 @@ and can share the cached one.
 """
 
 import ctypes
-import math
 from dataclasses import dataclass
 
 import torch
@@ -51,10 +50,14 @@ class DcaConfig:
         return C.lcsr_dca_t(self.chunk, self.local)
 
 
-def yarn_softmax_scale(head_dim, yarn_factor):
-    """1 / (t sqrt(D)) with sqrt(1/t) = 0.1 ln(s) + 1 (s <= 1: no scaling)."""
-    m = 1.0 if yarn_factor <= 1.0 else 0.1 * math.log(yarn_factor) + 1.0
-    return m * m / math.sqrt(head_dim)
+def softmax_scale(head_dim, rope):
+    """The attention calls' logit scale 1 / (t sqrt(D)), YaRN temperature
+    from rope.yarn_factor (lcsr_softmax_scale)."""
+    r = rope.c()
+    v = C.load().lcsr_softmax_scale(ctypes.byref(r), int(head_dim))
+    if not v > 0.0:
+        _check(C.LCSR_EINVAL)
+    return v
 
 
 class Pattern:

@@ -24,11 +24,11 @@ library primitives used).  Sources are cited by page and section:
   the sliding window), §4.2 (vertical-slash and the other head patterns),
   §4.3 (selection of whole key blocks).
 
-Pinned by the ``-m "not gpu"`` tests (brute force, closed forms, invariants).
-Readings taken where the pages are silent or garbled are stated next to the
-code they affect.  One part is "parity unpinned":
-the exact YaRN frequency ramp between beta_slow and beta_fast (the pages'
-snippet is garbled; only its end points and monotonicity are pinned).
+Pinned by the ``-m "not gpu"`` tests (brute force, closed forms, invariants,
+hand-worked values).  Readings taken where the pages are silent or garbled
+are stated next to the code they affect.  The YaRN frequency ramp between
+beta_slow and beta_fast (the pages' snippet is garbled) is pinned by its end
+points, its band sizes and three pairs worked by hand inside the ramp.
 """
 
 from .rope import (bf16_round, bf16_round64, rope_inv_freq, yarn_inv_freq, yarn_mscale,
@@ -51,5 +51,7 @@ __all__ = [
     "KeyContext", "attention_logits", "dense_causal_rows", "critical_set",
     "sparse_rows", "attention_recall",
     "estimate_scores", "select_top", "select_pattern",
-    "refine_budgets",
+    "refine_budgets", "refine_sizes",
+    "a_shape_set", "a_shape_lists", "choose_candidates",
+    "BLOCK", "block_scores", "select_blocks", "block_key_set", "block_sparse_rows",
 ]

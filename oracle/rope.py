@@ -11,11 +11,11 @@ import numpy as np
 def bf16_round(x):
     """Round float32 values to the nearest bfloat16 (ties to even), as fp32.
 
-    The library stores rotated keys, rotated queries and probabilities in
-    bfloat16 for the matrix cores and converts fp32 inputs to bf16 on entry;
-    the oracle applies this rounding to *inputs* (the tiny fp32 config) and,
-    through bf16_round64, to the K cache, whose bf16 type the interface fixes;
-    never to its other intermediates.
+    The library converts fp32 inputs to bf16 on entry; the oracle applies
+    the same rounding to those inputs (the tiny fp32 config).  Rounding of
+    rotated operands is a separate, optional mode of the oracle
+    (bf16_round64 through KeyContext(operands="bf16")) that models the
+    matrix cores' operand precision; parity is asserted without it.
     """
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     bits = a.view(np.uint32).astype(np.uint64)
@@ -62,6 +62,8 @@ def yarn_inv_freq(head_dim, base, factor, orig_max_pos, beta_fast=32.0,
     theta_p * ((1 - gamma_p) / factor + gamma_p).  Fast pairs are kept,
     slow pairs are interpolated by 1/factor ([architecture overview] §2.2:
     the longest wavelengths are interpolated).  factor <= 1 returns theta.
+    Pinned by three hand-worked pairs inside the ramp (tests/golden/
+    yarn_ramp.txt) besides its end points and band sizes.
     """
     theta = rope_inv_freq(head_dim, base)
     if factor <= 1.0:

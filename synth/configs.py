@@ -10,7 +10,13 @@ fixed here:
   within the 262,144-token training length, where DCA is the identity);
 * 1M and refinement-stress: DCA chunk C = 262,144, local window W = 32,768,
   YaRN factor s = N / 262,144 (4 and 2); no YaRN frequency blend on the
-  attention path (temperature only).
+  attention path (temperature only);
+* Q and K noise N(0, 1) under the planted parts, except in the refinement
+  stress layer, which draws it at 0.5 N(0, 1): with unit noise the softmax
+  mass of the 524,288 background keys is so large that no head reaches the
+  0.9 recall threshold unless its 64 far sinks carry logits near 12, and
+  logits that large put the bf16 operand rounding alone above the output
+  tolerance.  Its unit-noise twin (far sinks at excess 6) is a parity case.
 """
 
 from dataclasses import dataclass, field, replace
@@ -36,6 +42,8 @@ class LayerConfig:
     last_q: int = 64
     planting: str = "none"        # see synth.gen
     sink_every: int = 0           # sink spacing for planting "sinks_every"
+    qk_noise: float = 1.0         # std of the Q/K noise under the planted parts
+    far_sink_excess: float = 9.0  # logit excess of the far sinks ("far_sinks_stripes")
     recall_threshold: float = 0.9
     extra: dict = field(default_factory=dict)
 
@@ -81,10 +89,16 @@ FOURTEEN_B_512K_REFINE = LayerConfig(
     name="14b_512k_refine", cid=5, n_heads=40, n_kv_heads=8, head_dim=128,
     seq_len=524288, prefill_chunk=32768, in_dtype="bf16", rope_base=1e7,
     yarn_factor=2.0, dca_chunk=262144, dca_local=32768,
-    planting="far_sinks_stripes")
+    planting="far_sinks_stripes", qk_noise=0.5)
+
+# the refinement-stress planting over unit Q/K noise, far sinks at excess 6
+FOURTEEN_B_512K_UNIT_NOISE = replace(
+    FOURTEEN_B_512K_REFINE, name="14b_512k_unit_noise", cid=6, qk_noise=1.0,
+    far_sink_excess=6.0)
 
 CONFIGS = {c.name: c for c in (TINY, SEVEN_B_128K, FOURTEEN_B_256K,
-                               SEVEN_B_1M, FOURTEEN_B_512K_REFINE)}
+                               SEVEN_B_1M, FOURTEEN_B_512K_REFINE,
+                               FOURTEEN_B_512K_UNIT_NOISE)}
 
 
 def scaled(cfg, **kw):

@@ -7,10 +7,9 @@ oracle consume exactly the tensors made here.
 Recipe (all magnitudes are stated as the logit excess E over the background,
 whose standard deviation is 1 at the 1/sqrt(D) scale):
 
-* noise: V iid N(0, 1); Q and K iid N(0, 1) for the tiny config, and
-  N(0, NOISE_QK^2) under the planted components for the other layers, so
-  that their elements keep roughly unit scale while the far-field logits stay
-  flat (background logit std ~0.7), as trained heads have; bf16 configs are
+* noise: V iid N(0, 1); Q and K iid N(0, 1) under the planted components
+  (the config's qk_noise scales it: 0.5 for the refinement-stress layer,
+  whose recall calibration needs flatter far-field logits); bf16 configs are
   rounded to bf16 (torch's round-to-nearest-even), the tiny config stays fp32
   (the library rounds it on entry);
 * "sinks_band" / "sinks_every" (7B/14B-shaped layers): per KV head a unit
@@ -36,11 +35,11 @@ whose standard deviation is 1 at the 1/sqrt(D) scale):
   a = i mod P, so q.k peaks where i - j is a multiple of P.  The period P
   cycles over (64, 96, 128, 192, 256, 512, 1024, 2048) by KV head; the
   per-query-head stripe factor varies, so some heads are well covered by the
-  base budget and some are not.  Sink excess 9, stripe excess 4: about a
-  quarter of the heads reach a recall of 0.9 at the base budget and the
-  rest fall below it (measured on the last chunk, 128 rows); weaker sinks
-  leave every head far below 0.9, much stronger ones lift almost every head
-  above it;
+  base budget and some are not.  Sink excess 9 (the config's
+  far_sink_excess), stripe excess 4, Q/K noise 0.5: about a quarter of the
+  heads reach a recall of 0.9 at the base budget and the rest fall below it
+  (measured on the last chunk, 128 rows); weaker sinks leave every head far
+  below 0.9, much stronger ones lift almost every head above it;
 * "none" (tiny): noise only.
 """
 
@@ -49,11 +48,9 @@ import math
 import numpy as np
 import torch
 
-NOISE_QK = 0.5
 E_SINK = 3.0
 E_BAND = 4.0
 BAND_DRIFT = 32768.0
-E_FAR_SINK = 9.0
 E_STRIPE = 4.0
 BAND_PLANES = (10, 48)
 SINK_PLANES = 4
@@ -174,7 +171,7 @@ def generate(cfg, device="cpu", n_tokens=None):
     out_v = torch.empty((G, n, D), dtype=torch.bfloat16, device=device)
     group = H // G
     for g in range(G):
-        k = _noise((n, D), _torch_seed(cfg, 2, g), device) * NOISE_QK
+        k = _noise((n, D), _torch_seed(cfg, 2, g), device) * cfg.qk_noise
         per_head_q = []
         band = None
         if cfg.planting in ("sinks_band", "sinks_every"):
@@ -195,7 +192,7 @@ def generate(cfg, device="cpu", n_tokens=None):
             sinks = torch.as_tensor(sp[sp < n], device=device)
             # the sink keys carry exactly the planted amplitude along u
             ks = k[sinks]
-            k[sinks] = ks - (ks @ u)[:, None] * u + _amp(E_FAR_SINK, D) * u
+            k[sinks] = ks - (ks @ u)[:, None] * u + _amp(cfg.far_sink_excess, D) * u
             period = STRIPE_PERIODS[g % len(STRIPE_PERIODS)]
             codes = torch.tensor(_stripe_codes(cfg, g, np.arange(period)),
                                  dtype=torch.float32, device=device)
@@ -203,14 +200,14 @@ def generate(cfg, device="cpu", n_tokens=None):
             k += _amp(E_STRIPE, D) * codes[idx]
             for hh in range(group):
                 h = g * group + hh
-                per_head_q.append(_amp(E_FAR_SINK, D) * float(fac["sink"][h]) * u)
+                per_head_q.append(_amp(cfg.far_sink_excess, D) * float(fac["sink"][h]) * u)
         out_k[g] = k.to(torch.bfloat16)
         del k
         out_v[g] = _noise((n, D), _torch_seed(cfg, 3, g), device).to(
             torch.bfloat16)
         for hh in range(group):
             h = g * group + hh
-            q = _noise((n, D), _torch_seed(cfg, 1, h), device) * NOISE_QK
+            q = _noise((n, D), _torch_seed(cfg, 1, h), device) * cfg.qk_noise
             if per_head_q:
                 q += per_head_q[hh]
             if band is not None:

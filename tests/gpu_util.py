@@ -11,7 +11,8 @@ import long_context_sparse_rope_amd as L
 
 DEV = "cuda"
 
-# Output bar for bf16 inputs with fp32 accumulation.
+# Output bar for bf16 inputs with fp32 accumulation, against the fp64 oracle
+# with exact rotated operands.
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 
@@ -23,6 +24,15 @@ def rope_of(cfg, blend=False):
 
 def dca_of(cfg):
     return L.DcaConfig(cfg.dca_chunk, cfg.dca_local)
+
+
+def product_sm(cfg):
+    """The logit scale as the library forms it (lcsr_softmax_scale), checked
+    against the oracle's fp64 YaRN temperature to float rounding."""
+    sm = L.softmax_scale(cfg.head_dim, rope_of(cfg))
+    ref = oracle.softmax_scale(cfg.head_dim, cfg.yarn_factor)
+    assert abs(sm - ref) <= 2 ** -23 * ref, (sm, ref)
+    return sm
 
 
 def oracle_freqs(cfg, blend=False):
@@ -75,3 +85,76 @@ def lse_compare(gpu, ref, tol=2e-2):
     assert np.all(d <= tol), f"lse max diff {d.max():.3e} (worst excess {np.max(d - tol):.3e})"
     return d.max()
 
+
+
+# Estimate scores against fp64: every score within this fraction of the
+# largest score of its kind.
+SCORE_REL = 1e-3
+# Independent selections (GPU scores vs fp64 scores) may differ only where
+# the fp64 score sits this close (a fraction of the largest score) to the
+# fp64 boundary score.
+NEAR_TIE_REL = 1e-5
+
+
+def score_compare(got, ref, what, quiet=False):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = float(np.max(np.abs(ref)))
+    d = np.abs(got - ref)
+    if not quiet:
+        big = ref > 1e-3 * scale
+        rel_big = float(np.max(d[big] / ref[big])) if big.any() else 0.0
+        print(f"  {what}: max |d| {d.max():.2e} = {d.max() / scale:.2e} of the largest score; "
+              f"max relative error of scores above 1e-3 of it: {rel_big:.2e}", flush=True)
+    assert d.max() <= SCORE_REL * scale, f"{what}: max |d| {d.max():.3e} > {SCORE_REL} x {scale:.3e}"
+    return d.max() / scale
+
+
+def near_tie_check(gpu_sel, ref_scores, k, what):
+    """The GPU's selection (from its own scores) against the oracle's
+    selection of the fp64 scores: every index in one set but not the other
+    must be a near-tie of the fp64 boundary score."""
+    ref = np.asarray(ref_scores, np.float64)
+    sel = oracle.select_top(ref, k)
+    diff = np.array(sorted(set(np.asarray(gpu_sel).tolist()) ^ set(sel.tolist())), np.int64)
+    if diff.size == 0:
+        print(f"  {what}: selections identical ({sel.size})", flush=True)
+        return 0.0
+    kth = float(np.min(ref[sel]))
+    gap = float(np.max(np.abs(ref[diff] - kth)))
+    scale = float(np.max(ref))
+    print(f"  {what}: {diff.size // 2} swaps of {sel.size}; widest gap to the boundary "
+          f"{gap:.2e} = {gap / scale:.2e} of the largest score", flush=True)
+    assert gap <= NEAR_TIE_REL * scale, f"{what}: disagreement {gap:.3e} is not a near-tie"
+    return gap / scale
+
+
+def _one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def _run_job(job):
+    fn, args = job
+    return fn(*args)
+
+
+def parallel_map(fn, arg_list, workers=12):
+    """fn(*args) for every args tuple, in forked worker processes (CPU only:
+    the workers run the numpy oracle and never touch the GPU), results in
+    order.  Large read-only state (key contexts) must be built before the
+    call; the workers inherit it instead of receiving it.  At most 12
+    workers: with the parent that keeps the process count on the GPU machine
+    within its limit.  They end with os._exit (multiprocessing's own), so no
+    GPU runtime teardown runs in them."""
+    import multiprocessing as mp
+    import os
+    arg_list = list(arg_list)
+    n = min(len(arg_list), workers, os.cpu_count() or 1)
+    if n <= 1:
+        return [fn(*a) for a in arg_list]
+    with mp.get_context("fork").Pool(n, initializer=_one_thread) as pool:
+        return pool.map(_run_job, [(fn, a) for a in arg_list], chunksize=1)

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(C.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -62,6 +62,29 @@ def pattern(max_vert=1000, max_slash=6096):
 
 def err(lib):
     return lib.lcsr_last_error().decode()
+
+
+def test_softmax_scale_yarn_temperature(lib):
+    """lcsr_softmax_scale against the closed form worked by hand in
+    tests/golden/yarn_temperature.txt (1/t for s = 1, 2, 4) at D 64 and 128,
+    and its error returns."""
+    path = os.path.join(ROOT, "tests", "golden", "yarn_temperature.txt")
+    rows = [[float(x) for x in ln.split()] for ln in open(path)
+            if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 3
+    for s, _, inv_t in rows:
+        for d in (64, 128):
+            r = C.lcsr_rope_t(1e7, s, 262144, 32.0, 1.0, 0)
+            got = lib.lcsr_softmax_scale(ctypes.byref(r), d)
+            want = inv_t / d ** 0.5
+            assert abs(got - want) <= 2 ** -24 * want, (s, d, got, want)
+    # s below 1 means no temperature
+    r = C.lcsr_rope_t(1e7, 0.5, 262144, 32.0, 1.0, 0)
+    assert lib.lcsr_softmax_scale(ctypes.byref(r), 128) == pytest.approx(128 ** -0.5, rel=1e-7)
+    assert lib.lcsr_softmax_scale(None, 128) == 0.0 and "rope" in err(lib)
+    assert lib.lcsr_softmax_scale(ctypes.byref(r), 0) == 0.0 and "head_dim" in err(lib)
+    r.yarn_factor = float("nan")
+    assert lib.lcsr_softmax_scale(ctypes.byref(r), 128) == 0.0 and "finite" in err(lib)
 
 
 def test_workspace_bytes(lib):

@@ -12,7 +12,7 @@ import oracle
 import synth
 from synth.configs import FOURTEEN_B_256K, SEVEN_B_128K, TINY, scaled
 from tests.gpu_util import (DEV, build_cache, compare, dca_of, host64, lse_compare,
-                            oracle_freqs, oracle_inputs, rope_of)
+                            oracle_freqs, oracle_inputs, product_sm, rope_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,15 +32,14 @@ CFG14 = scaled(FOURTEEN_B_256K, n_heads=10, n_kv_heads=2, seq_len=4096, prefill_
 def _layer(cfg):
     return L.ChunkedSparsePrefill(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len,
                                   rope_of(cfg), dca_of(cfg),
-                                  oracle.softmax_scale(cfg.head_dim, cfg.yarn_factor),
+                                  product_sm(cfg),
                                   cfg.n_vert, cfg.n_slash, cfg.last_q, DEV)
 
 
 def _contexts(cfg, k, v, upto):
     _, ko, vo = oracle_inputs(k[:1], k, v)
     th = oracle_freqs(cfg)
-    return [oracle.KeyContext(ko[g, :upto], vo[g, :upto], th, cfg.dca_chunk, cfg.dca_local,
-                              operands="bf16") for g in range(cfg.n_kv_heads)]
+    return [oracle.KeyContext(ko[g, :upto], vo[g, :upto], th, cfg.dca_chunk, cfg.dca_local) for g in range(cfg.n_kv_heads)]
 
 
 def _estimate(layer, q, c0, c1, budgets, max_blocks):
@@ -236,7 +235,7 @@ def test_tiny_ragged_chunk_bf16_out():
     _check_selection(pat, sc, c0, budgets)
     qo, ko, vo = oracle_inputs(q, k, v)
     ctx = oracle.KeyContext(ko[0, :c1], vo[0, :c1], oracle_freqs(cfg), cfg.dca_chunk,
-                            cfg.dca_local, operands="bf16")
+                            cfg.dca_local)
     ref_sc = oracle.block_scores(qo[0, c0:c1], c0, ctx, layer.sm_scale)
     fin = np.isfinite(ref_sc)
     assert np.all(np.abs(host64(sc[0])[fin] - ref_sc[fin]) <= 1e-4 + 1e-4 * np.abs(ref_sc[fin]))

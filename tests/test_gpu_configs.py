@@ -2,9 +2,10 @@
 
 Each layer (7B-shaped 128K, 14B-shaped 256K, 7B-shaped 1M with DCA and
 YaRN s = 4, 14B-shaped 512K refinement stress) runs its whole chunk loop on
-the GPU through the C ABI, in the launch configuration the benchmark times.
-For a few chunks per layer (the first, the ones that straddle a DCA key
-period or the local window, the last) the run keeps:
+the GPU through the C ABI, in the launch configuration the benchmark times,
+with the logit scale the library forms (lcsr_softmax_scale).  For a few
+chunks per layer (the first, the ones that straddle a DCA key period or the
+local window, the last) the run keeps:
 
 * the estimate scores of every head, so that the selection can be checked
   bit for bit against the oracle's selection of the same fp32 scores;
@@ -12,10 +13,12 @@ period or the local window, the last) the run keeps:
   its first rows, rows beside each DCA period edge (S k +- 2) and beside the
   local-window edge (S k + W - 1, S k + W), and 128 seeded rows.
 
-Three query heads per layer (the first, the last of the first KV group and
-the last head) are recomputed by the fp64 oracle: estimate scores of the
-last checked chunk, and attention of the sampled rows with the GPU's own
-pattern.  Every chunk's full output is checked to be finite.
+The fp64 oracle (exact rotated operands) recomputes every query head on the
+sampled rows of the last checked chunk and one head of every KV group on the
+other checked chunks (a different head of the group per chunk), with the
+GPU's own pattern; and the estimate scores of one head per KV group on the
+last checked chunk, where the fp64 selection may differ from the GPU's only
+on near-ties.  Every chunk's full output is checked to be finite.
 """
 
 import functools
@@ -27,8 +30,9 @@ import torch
 import long_context_sparse_rope_amd as L
 import oracle
 import synth
-from synth.configs import CONFIGS
-from tests.gpu_util import DEV, compare, dca_of, lse_compare, oracle_freqs, rope_of
+from synth.configs import CONFIGS, scaled
+from tests.gpu_util import (DEV, compare, dca_of, lse_compare, near_tie_check, oracle_freqs,
+                            parallel_map, product_sm, rope_of, score_compare)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,13 +41,20 @@ CHECK_CHUNKS = {
     "14b_256k": (0, 7),
     "7b_1m_dca": (7, 8, 31),
     "14b_512k_refine": (7, 8, 15),
+    "14b_512k_unit_noise": (8, 15),
 }
 N_SEEDED_ROWS = 128
-RECALL_ROWS = 16  # rows per oracle head in the recall check
+RECALL_ROWS = 16   # rows per oracle head in the recall check
+DENSE_ROWS = 128   # dense-mode rows at the 1M context, spread over the KV groups
 
 
-def oracle_heads(cfg):
-    return sorted({0, cfg.group - 1, cfg.n_heads - 1})
+def group_heads(cfg, c):
+    """One query head per KV group, a different one of the group per chunk."""
+    return [g * cfg.group + (g + c) % cfg.group for g in range(cfg.n_kv_heads)]
+
+
+def heads_of_chunk(cfg, c, last):
+    return list(range(cfg.n_heads)) if c == last else group_heads(cfg, c)
 
 
 def sample_rows(cfg, c0, lc):
@@ -63,17 +74,54 @@ def sample_rows(cfg, c0, lc):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@functools.lru_cache(maxsize=2)
+def _dca_twin(cfg, layer, q, k, v, res):
+    """The 256K layer again with DCA on (C = 262,144 = the sequence, W =
+    32,768): every causal relative position is then the plain one, so the
+    estimate scores and, on the DCA-off pattern, the attention rows must
+    agree with the DCA-off run to rounding."""
+    C, W = 262144, 32768
+    tw = scaled(cfg, dca_chunk=C, dca_local=W)
+    sm = product_sm(tw)
+    twin = L.ChunkedSparsePrefill(tw.n_heads, tw.n_kv_heads, tw.head_dim, tw.seq_len,
+                                  rope_of(tw), dca_of(tw), sm, tw.n_vert, tw.n_slash,
+                                  tw.last_q, DEV)
+    out = torch.empty(tw.n_heads, tw.prefill_chunk, tw.head_dim, dtype=torch.float32, device=DEV)
+    lse = torch.empty(tw.n_heads, tw.prefill_chunk, dtype=torch.float32, device=DEV)
+    res["twin"] = {}
+    for c in range(tw.n_chunks):
+        c0, lc = tw.chunk_bounds(c)
+        c1 = c0 + lc
+        twin.append_kv(k[:, c0:c1], v[:, c0:c1], c0)
+        if c not in CHECK_CHUNKS[cfg.name]:
+            continue
+        ch = res["chunks"][c]
+        vs = torch.empty(tw.n_heads, c1, device=DEV)
+        ss = torch.empty(tw.n_heads, c1, device=DEV)
+        L.vs_pattern_estimate(q[:, c0:c1], twin.k_cache[:, :c1], c0, twin.rope, twin.dca, sm,
+                              twin.n_vert, twin.n_slash, twin.pattern, last_q=tw.last_q,
+                              vert_score=vs, slash_score=ss)
+        pat = L.Pattern.from_lists(ch["verts"], ch["slashes"], DEV, max_vert=tw.n_vert,
+                                   max_slash=tw.n_slash)
+        L.vs_sparse_attn_prefill(q[:, c0:c1], twin.k_cache[:, :c1], twin.v_cache[:, :c1], c0,
+                                 twin.rope, twin.dca, sm, pat, out=out[:, :lc], lse=lse[:, :lc])
+        ri = torch.as_tensor(ch["rows"] - c0, device=DEV)
+        res["twin"][c] = {"vs": vs.cpu().numpy(), "ss": ss.cpu().numpy(),
+                          "out": out[:, ri].cpu().numpy(), "lse": lse[:, ri].cpu().numpy()}
+    del twin
+
+
+@functools.lru_cache(maxsize=1)
 def run_layer(name):
     """Run the layer's chunk loop on the GPU; keep what the checks need."""
     cfg = CONFIGS[name]
+    key_context.cache_clear()
     torch.cuda.empty_cache()
     q, k, v = synth.generate(cfg, DEV)
-    sm = oracle.softmax_scale(cfg.head_dim, cfg.yarn_factor)
+    sm = product_sm(cfg)
     H, D = cfg.n_heads, cfg.head_dim
     layer = L.ChunkedSparsePrefill(H, cfg.n_kv_heads, D, cfg.seq_len, rope_of(cfg),
                                    dca_of(cfg), sm, cfg.n_vert, cfg.n_slash, cfg.last_q, DEV)
-    res = {"chunks": {}, "sm": sm}
+    res = {"chunks": {}, "sm": oracle.softmax_scale(cfg.head_dim, cfg.yarn_factor)}
     out = torch.empty(H, cfg.prefill_chunk, D, dtype=torch.float32, device=DEV)
     lse = torch.empty(H, cfg.prefill_chunk, dtype=torch.float32, device=DEV)
     for c in range(cfg.n_chunks):
@@ -105,6 +153,17 @@ def run_layer(name):
                 "verts": [x.numpy() for x in verts], "slashes": [x.numpy() for x in slashes],
                 "stats": stats.cpu().tolist(),
             }
+    if name == "7b_1m_dca":
+        # the same call again on the last chunk: bitwise the same output
+        c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
+        again = torch.empty_like(out[:, :lc])
+        lse2 = torch.empty_like(lse[:, :lc])
+        layer.attend(q[:, c0:c0 + lc], c0, out=again, lse=lse2)
+        res["repeat_equal"] = (bool(torch.equal(again, out[:, :lc])),
+                               bool(torch.equal(lse2, lse[:, :lc])))
+        del again, lse2
+    if name == "14b_256k":
+        _dca_twin(cfg, layer, q, k, v, res)
     if name == "14b_512k_refine":
         c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
         qc = q[:, c0:c0 + lc]
@@ -121,13 +180,15 @@ def run_layer(name):
                          "q": q[:, torch.as_tensor(rows + c0, device=DEV)].float().cpu().numpy()}
         base_v, base_s = list(layer.n_vert), list(layer.n_slash)
         hist = layer.refine_chunk(qc, c0, rows_t, out[:, :lc], lse=lse[:, :lc])
-        res["refine"] = {"history": [h.numpy() for h in hist], "base": (base_v, base_s),
+        res["refine"] = {"history": hist, "base": (base_v, base_s),
                          "after": (list(layer.n_vert), list(layer.n_slash)), "c1": c0 + lc}
     if name == "7b_1m_dca":
         # dense mode (every causal key, same DCA logits) on the last chunk
         c0, lc = cfg.chunk_bounds(cfg.n_chunks - 1)
         layer.attend(q[:, c0:c0 + lc], c0, out=out[:, :lc], lse=lse[:, :lc], dense=True)
-        rows = np.array([c0, c0 + 1, c0 + lc // 2, c0 + lc - 1], dtype=np.int64)
+        rng = np.random.default_rng([cfg.seed, 11])
+        rows = np.sort(rng.choice(np.arange(c0, c0 + lc), DENSE_ROWS - 4, replace=False))
+        rows = np.unique(np.concatenate([rows, [c0, c0 + 1, c0 + lc // 2, c0 + lc - 1]]))
         ri = torch.as_tensor(rows - c0, device=DEV)
         res["dense"] = {"rows": rows, "out": out[:, ri].cpu().numpy(),
                         "lse": lse[:, ri].cpu().numpy(),
@@ -136,7 +197,7 @@ def run_layer(name):
         # block-sparse with 100 kept blocks and A-shape with sink 16 + window
         # 2048 (the measured configurations)
         c1 = c0 + lc
-        oh = oracle_heads(cfg)
+        oh = group_heads(cfg, cfg.n_chunks - 1)
         rows = sample_rows(cfg, c0, lc)
         ri = torch.as_tensor(rows - c0, device=DEV)
         qr = q[:, torch.as_tensor(rows, device=DEV)].float().cpu().numpy()
@@ -150,7 +211,7 @@ def run_layer(name):
                                     c0, layer.rope, layer.dca, sm, bp, out=out[:, :lc],
                                     lse=lse[:, :lc], stats=st_b)
         res["block"] = {"c0": c0, "rows": rows, "q": qr, "out": out[:, ri].cpu().numpy(),
-                        "lse": lse[:, ri].cpu().numpy(),
+                        "lse": lse[:, ri].cpu().numpy(), "heads": oh,
                         "idx": {h: bp.idx[h].cpu().numpy() for h in oh},
                         "cnt": {h: bp.cnt[h].cpu().numpy() for h in oh},
                         "scores": {h: sc[h].cpu().numpy() for h in oh},
@@ -163,7 +224,7 @@ def run_layer(name):
                                  layer.rope, layer.dca, sm, ap, out=out[:, :lc], lse=lse[:, :lc])
         av, asl = ap.lists()
         res["a_shape"] = {"rows": rows, "q": qr, "out": out[:, ri].cpu().numpy(),
-                          "lse": lse[:, ri].cpu().numpy(),
+                          "lse": lse[:, ri].cpu().numpy(), "heads": oh,
                           "verts": [x.numpy() for x in av], "slashes": [x.numpy() for x in asl]}
     if name in ("7b_1m_dca", "14b_256k"):
         # decode steps on the full cache: the newest rows (as many as fill the
@@ -182,22 +243,62 @@ def run_layer(name):
             res["decode"].append({"rows": np.arange(p0, c1), "out": od.cpu().numpy(),
                                   "lse": lse_d.cpu().numpy(),
                                   "q": q[:, p0:c1].float().cpu().numpy()})
-    kv_heads = sorted({h // cfg.group for h in oracle_heads(cfg)})
-    res["k"] = {g: k[g].float().cpu().numpy() for g in kv_heads}
-    res["v"] = {g: v[g].float().cpu().numpy() for g in kv_heads}
+    res["k"] = {g: k[g].float().cpu().numpy() for g in range(cfg.n_kv_heads)}
+    res["v"] = {g: v[g].float().cpu().numpy() for g in range(cfg.n_kv_heads)}
     del q, k, v, layer, out, lse
     torch.cuda.empty_cache()
     return res
 
 
-@functools.lru_cache(maxsize=2)
-def key_context(name, g):
+@functools.lru_cache(maxsize=8)
+def key_context(name, g, operands="fp64"):
     """fp64 keys and values of KV head g over the whole layer (the oracle only
     reads keys j <= i of each row)."""
     cfg = CONFIGS[name]
     res = run_layer(name)
     return oracle.KeyContext(res["k"][g].astype(np.float64), res["v"][g].astype(np.float64),
-                             oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local, operands="bf16")
+                             oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local, operands=operands)
+
+
+def warm_contexts(name, groups, cont=False):
+    """Build the oracle's rotated keys of these KV heads before forking the
+    workers, which then share them."""
+    for g in sorted(set(groups)):
+        ctx = key_context(name, g)
+        ctx.k_dca()
+        if cont:
+            ctx.k_cont()
+
+
+def _sparse_job(name, g, q, rows, verts, slashes, sm):
+    return oracle.sparse_rows(q, rows, key_context(name, g), verts, slashes, sm)
+
+
+def _dense_job(name, g, q, rows, sm):
+    return oracle.dense_causal_rows(q, rows, key_context(name, g), sm)
+
+
+def _estimate_job(name, g, q, rows, c1, sm):
+    return oracle.estimate_scores(q, rows, key_context(name, g), c1, sm)
+
+
+def _recall_job(name, g, q, rows, verts, slashes, sm):
+    return oracle.attention_recall(q, rows, key_context(name, g), verts, slashes, sm)
+
+
+def _block_job(name, g, qc, c0, sm):
+    return oracle.block_scores(qc, c0, key_context(name, g), sm)
+
+
+def _block_rows_job(name, g, q, rows, idx, cnt, c0, sm):
+    kept = lambda i: idx[(i - c0) // 64, :cnt[(i - c0) // 64]]  # noqa: E731
+    return oracle.block_sparse_rows(q, rows, key_context(name, g), kept, sm)
+
+
+def split_rows(rows, parts):
+    """Row index ranges cutting `rows` into about `parts` pieces."""
+    edges = np.linspace(0, len(rows), min(parts, len(rows)) + 1).astype(int)
+    return [slice(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
 
 
 NAMES = list(CHECK_CHUNKS)
@@ -212,12 +313,11 @@ def layer_run(request):
 
 def test_selection_bit_exact_full_size(layer_run):
     """The selection is the oracle's selection of the same scores: every head
-    in the last chunk, the oracle heads in the others."""
+    of every checked chunk."""
     name, res = layer_run
     cfg = CONFIGS[name]
-    last = max(res["chunks"])
     for c, ch in res["chunks"].items():
-        for h in (range(cfg.n_heads) if c == last else oracle_heads(cfg)):
+        for h in range(cfg.n_heads):
             assert ch["verts"][h].tolist() == \
                 oracle.select_top(ch["vs"][h], cfg.n_vert).tolist(), (c, h)
             assert ch["slashes"][h].tolist() == \
@@ -225,76 +325,114 @@ def test_selection_bit_exact_full_size(layer_run):
 
 
 def test_estimate_scores_full_size(layer_run):
-    """Vertical and slash scores of the last checked chunk against fp64."""
+    """Vertical and slash scores of the last checked chunk against fp64 (one
+    head per KV group and the last head); the fp64 top sets differ from the
+    GPU's only by near-ties."""
     name, res = layer_run
     cfg = CONFIGS[name]
     c = max(res["chunks"])
     ch = res["chunks"][c]
     c1 = ch["c0"] + ch["lc"]
     rows = oracle.estimate.estimate_rows(ch["c0"], ch["lc"], cfg.last_q)
-    for h in oracle_heads(cfg):
-        ctx = key_context(name, h // cfg.group)
-        rv, rs = oracle.estimate_scores(ch["q_est"][h].astype(np.float64), rows, ctx, c1,
-                                        res["sm"])
+    heads = sorted(set(group_heads(cfg, c) + [cfg.n_heads - 1]))
+    warm_contexts(name, [h // cfg.group for h in heads], cont=True)
+    refs = parallel_map(_estimate_job, [(name, h // cfg.group,
+                                         ch["q_est"][h].astype(np.float64), rows, c1, res["sm"])
+                                        for h in heads], workers=8)
+    for h, (rv, rs) in zip(heads, refs):
         gv, gs = ch["vs"][h].astype(np.float64), ch["ss"][h].astype(np.float64)
         n = len(rows)
         assert abs(gv.sum() - n) < 1e-3 * n and abs(gs.sum() - n) < 1e-3 * n
-        dv, ds = np.max(np.abs(gv - rv)), np.max(np.abs(gs - rs))
-        print(f"[estimate] {name} chunk {c} head {h}: max |dv| {dv:.2e} (max v {rv.max():.2e})"
-              f" max |ds| {ds:.2e} (max s {rs.max():.2e})")
-        assert dv <= 2e-2 * rv.max() and ds <= 2e-2 * rs.max()
-        # the fp64 top sets differ from the GPU's only by near-ties
-        ov = set(oracle.select_top(rv, cfg.n_vert).tolist())
-        os_ = set(oracle.select_top(rs, cfg.n_slash).tolist())
-        assert len(ov & set(ch["verts"][h].tolist())) >= 0.9 * len(ov)
-        assert len(os_ & set(ch["slashes"][h].tolist())) >= 0.9 * len(os_)
+        print(f"[estimate] {name} chunk {c} head {h}:", flush=True)
+        score_compare(gv, rv, "vertical")
+        score_compare(gs, rs, "slash")
+        near_tie_check(ch["verts"][h], rv, cfg.n_vert, "vertical")
+        near_tie_check(ch["slashes"][h], rs, cfg.n_slash, "slash")
 
 
 def test_attention_sampled_rows_full_size(layer_run):
     """Sampled rows of every checked chunk against fp64 sparse attention with
-    the GPU's pattern."""
+    the GPU's pattern: every head on the last checked chunk, one head per KV
+    group on the others."""
     name, res = layer_run
     cfg = CONFIGS[name]
+    last = max(res["chunks"])
+    worst = [0.0, 0.0]
+    warm_contexts(name, range(cfg.n_kv_heads))
     for c, ch in res["chunks"].items():
-        c1 = ch["c0"] + ch["lc"]
         rows = ch["rows"]
-        for h in oracle_heads(cfg):
-            ctx = key_context(name, h // cfg.group)
-            ro, rl, sizes = oracle.sparse_rows(ch["q"][h].astype(np.float64), rows, ctx,
-                                               ch["verts"][h], ch["slashes"][h], res["sm"])
+        heads = heads_of_chunk(cfg, c, last)
+        refs = parallel_map(_sparse_job, [(name, h // cfg.group, ch["q"][h].astype(np.float64),
+                                           rows, ch["verts"][h], ch["slashes"][h], res["sm"])
+                                          for h in heads])
+        for h, (ro, rl, sizes) in zip(heads, refs):
             print(f"[attention] {name} chunk {c} head {h}: {rows.size} rows, "
-                  f"mean |C_i| {sizes.mean():.0f}")
-            compare(ch["out"][h].astype(np.float64), ro)
+                  f"mean |C_i| {sizes.mean():.0f}", flush=True)
+            mx, mn = compare(ch["out"][h].astype(np.float64), ro)
+            worst = [max(worst[0], mx), max(worst[1], mn)]
             lse_compare(ch["lse"][h].astype(np.float64), rl)
-            if h == 0:
-                # for information: against exact (fp64) rotated operands
-                ex = oracle.KeyContext(ctx.K, ctx.V, ctx.inv_freq, ctx.dca_chunk,
-                                       ctx.dca_local)
-                sel = slice(0, None, 4)
-                eo = oracle.sparse_rows(ch["q"][h][sel].astype(np.float64), rows[sel], ex,
-                                        ch["verts"][h], ch["slashes"][h], res["sm"])[0]
-                d = np.abs(ch["out"][h][sel] - eo)
-                print(f"[info] {name} chunk {c} head 0 vs exact operands: max-abs {d.max():.2e}"
-                      f" mean-abs {d.mean():.2e}")
         st = ch["stats"]
         assert st[0] >= st[1] > 0
+    # for information: the oracle with bf16-rounded rotated operands (the
+    # kernel's own operand rounding), head 0 of the last chunk
+    ch = res["chunks"][last]
+    bctx = oracle.KeyContext(key_context(name, 0).K, key_context(name, 0).V,
+                             oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local, operands="bf16")
+    sel = slice(0, None, 4)
+    bo = oracle.sparse_rows(ch["q"][0][sel].astype(np.float64), ch["rows"][sel], bctx,
+                            ch["verts"][0], ch["slashes"][0], res["sm"])[0]
+    d = np.abs(ch["out"][0][sel] - bo)
+    print(f"[info] {name}: worst vs fp64 max-abs {worst[0]:.2e} mean-abs {worst[1]:.2e}; "
+          f"head 0 vs bf16-operand oracle max-abs {d.max():.2e} mean-abs {d.mean():.2e}")
+
+
+def test_attention_repeat_bitwise():
+    """The 1M layer's last chunk attended twice: bitwise the same output and
+    lse (no atomics or order-dependent sums in the attention)."""
+    res = run_layer("7b_1m_dca")
+    assert res["repeat_equal"] == (True, True)
+
+
+def test_dca_is_identity_within_training_length():
+    """14B-shaped 256K layer with DCA on at C = 262,144 (the sequence
+    length), W = 32,768: every relative position stays the plain one
+    ([Qwen2.5-1M explainer] Length Extrapolation: intra-chunk pairs keep
+    their positions, successive pairs inside the window too), so the
+    estimate scores and the attention on the same pattern equal the DCA-off
+    run to rounding."""
+    name = "14b_256k"
+    cfg = CONFIGS[name]
+    res = run_layer(name)
+    for c, tw in res["twin"].items():
+        ch = res["chunks"][c]
+        for h in range(cfg.n_heads):
+            score_compare(tw["vs"][h].astype(np.float64), ch["vs"][h].astype(np.float64),
+                          "vertical (DCA on vs off)", quiet=True)
+            score_compare(tw["ss"][h].astype(np.float64), ch["ss"][h].astype(np.float64),
+                          "slash (DCA on vs off)", quiet=True)
+        d = np.abs(tw["out"] - ch["out"])
+        print(f"[dca-twin] chunk {c}: DCA on vs off max-abs {d.max():.2e} mean-abs "
+              f"{d.mean():.2e}", flush=True)
+        compare(tw["out"].astype(np.float64), ch["out"].astype(np.float64))
+        lse_compare(tw["lse"].astype(np.float64), ch["lse"].astype(np.float64))
 
 
 def test_recall_and_refinement_full_size():
     """Refinement stress layer: GPU recall against fp64 on sampled rows, the
     calibration rule (some heads under the threshold, some above), and the
-    budget decisions of one refinement round."""
+    budget decisions of every refinement round."""
     name = "14b_512k_refine"
     cfg = CONFIGS[name]
     res = run_layer(name)
     rc = res["recall"]
-    c1 = res["refine"]["c1"]
     sel = np.linspace(0, rc["rows"].size - 1, RECALL_ROWS).astype(np.int64)
-    for h in oracle_heads(cfg):
-        ctx = key_context(name, h // cfg.group)
-        rows = rc["rows"][sel]
-        of, os_, orc = oracle.attention_recall(rc["q"][h][sel].astype(np.float64), rows, ctx,
-                                               rc["verts"][h], rc["slashes"][h], res["sm"])
+    heads = group_heads(cfg, cfg.n_chunks - 1)
+    rows = rc["rows"][sel]
+    warm_contexts(name, [h // cfg.group for h in heads])
+    refs = parallel_map(_recall_job, [(name, h // cfg.group, rc["q"][h][sel].astype(np.float64),
+                                       rows, rc["verts"][h], rc["slashes"][h], res["sm"])
+                                      for h in heads])
+    for h, (of, os_, orc) in zip(heads, refs):
         lse_compare(rc["lse_full"][h][sel], of)
         lse_compare(rc["lse_sparse"][h][sel], os_)
         assert np.max(np.abs(rc["recall"][h][sel] - orc)) < 1e-2
@@ -305,57 +443,74 @@ def test_recall_and_refinement_full_size():
           f"{cfg.n_heads} under {cfg.recall_threshold}")
     assert (mean0 < cfg.recall_threshold).any() and (mean0 >= cfg.recall_threshold).any()
     base_v, base_s = res["refine"]["base"]
-    nv, ns, raised = oracle.refine_budgets(mean0, base_v, base_s, c1, cfg.recall_threshold)
+    nv, ns, raised = oracle.refine_budgets(mean0, base_v, base_s, res["refine"]["c1"],
+                                           cfg.recall_threshold)
     # budgets keep doubling for heads that stay low: replay every round
     for r in range(1, len(hist) - 1):
-        nv, ns, more = oracle.refine_budgets(hist[r], nv, ns, c1, cfg.recall_threshold)
+        nv, ns, more = oracle.refine_budgets(hist[r], nv, ns, res["refine"]["c1"],
+                                             cfg.recall_threshold)
     after_v, after_s = res["refine"]["after"]
     assert list(nv) == after_v and list(ns) == after_s
     # larger budgets select supersets of the same scores: recall cannot drop
     assert np.all(hist[1][raised] >= mean0[raised] - 1e-5)
 
 
+@pytest.mark.timeout(900)
 def test_dense_mode_1m_sampled_rows():
-    """Dense mode at the 1M context (last chunk): sampled rows against the
-    oracle's full causal attention with the same DCA logits."""
+    """Dense mode at the 1M context (last chunk): 128 sampled rows, spread
+    over the KV groups (a quarter of the rows on one head of each), against
+    the oracle's full causal attention with the same DCA logits."""
     name = "7b_1m_dca"
     cfg = CONFIGS[name]
     res = run_layer(name)
     dn = res["dense"]
-    for h in (0, cfg.n_heads - 1):
-        ctx = key_context(name, h // cfg.group)
-        ro, rl = oracle.dense_causal_rows(dn["q"][h].astype(np.float64), dn["rows"], ctx,
-                                          res["sm"])
-        compare(dn["out"][h].astype(np.float64), ro)
-        lse_compare(dn["lse"][h].astype(np.float64), rl)
+    n = dn["rows"].size
+    warm_contexts(name, range(cfg.n_kv_heads))
+    jobs, where = [], []
+    for g, h in enumerate(group_heads(cfg, 0)):
+        part = slice(g * n // cfg.n_kv_heads, (g + 1) * n // cfg.n_kv_heads)
+        sub = np.arange(n)[part]
+        for piece in split_rows(sub, 8):
+            idx = sub[piece]
+            jobs.append((name, g, dn["q"][h][idx].astype(np.float64), dn["rows"][idx], res["sm"]))
+            where.append((h, idx))
+    refs = parallel_map(_dense_job, jobs)
+    for (h, idx), (ro, rl) in zip(where, refs):
+        compare(dn["out"][h][idx].astype(np.float64), ro)
+        lse_compare(dn["lse"][h][idx].astype(np.float64), rl)
+    print(f"[dense] {n} rows over {cfg.n_kv_heads} KV groups", flush=True)
 
 
 def test_block_sparse_1m_sampled_rows():
     """Block-sparse heads at the 1M context (last chunk, 100 blocks): block
-    scores of the oracle heads against fp64, the selection bit-exact on the
-    GPU's scores, and sampled rows against the oracle on the GPU's lists."""
+    scores of one head per KV group against fp64, the selection bit-exact on
+    the GPU's scores, and sampled rows against the oracle on the GPU's
+    lists."""
     name = "7b_1m_dca"
-    cfg = CONFIGS[name]
     res = run_layer(name)
+    cfg = CONFIGS[name]
     b = res["block"]
     c0 = b["c0"]
-    for h in oracle_heads(cfg):
-        ctx = key_context(name, h // cfg.group)
-        ref = oracle.block_scores(b["q_chunk"][h].astype(np.float64), c0, ctx, res["sm"])
+    warm_contexts(name, [h // cfg.group for h in b["heads"]], cont=True)
+    scores = parallel_map(_block_job, [(name, h // cfg.group,
+                                        b["q_chunk"][h].astype(np.float64), c0, res["sm"])
+                                       for h in b["heads"]], workers=4)
+    rows_ref = parallel_map(_block_rows_job, [(name, h // cfg.group,
+                                               b["q"][h].astype(np.float64), b["rows"],
+                                               b["idx"][h], b["cnt"][h], c0, res["sm"])
+                                              for h in b["heads"]])
+    for h, ref, (ro, rl, sizes) in zip(b["heads"], scores, rows_ref):
         got = b["scores"][h].astype(np.float64)
         fin = np.isfinite(ref)
         d = np.abs(got[fin] - ref[fin])
         print(f"[block] {name} head {h}: score max |d| {d.max():.2e} (max |s| "
               f"{np.abs(ref[fin]).max():.2e})", flush=True)
-        assert np.all(d <= 1e-4 + 1e-4 * np.abs(ref[fin]))
+        assert np.all(d <= 1e-3 + 1e-3 * np.abs(ref[fin]))
         idx, cnt = b["idx"][h], b["cnt"][h]
         for qb in range(cnt.size):
             diag = c0 // 64 + qb
             sel = oracle.select_blocks(got[qb, :diag + 1], diag, 100)
             assert cnt[qb] == sel.size and idx[qb, :sel.size].tolist() == sel.tolist(), qb
-        kept = lambda i: idx[(i - c0) // 64, :cnt[(i - c0) // 64]]  # noqa: E731
-        ro, rl, sizes = oracle.block_sparse_rows(b["q"][h].astype(np.float64), b["rows"], ctx,
-                                                 kept, res["sm"])
         compare(b["out"][h].astype(np.float64), ro)
         lse_compare(b["lse"][h].astype(np.float64), rl)
     st = b["stats"]
@@ -364,7 +519,8 @@ def test_block_sparse_1m_sampled_rows():
 
 def test_a_shape_1m_sampled_rows():
     """A-shape heads (sink 16, window 2048) at the 1M context: the filled
-    lists are the oracle's, and sampled rows match its attention."""
+    lists are the oracle's, and sampled rows of one head per KV group match
+    its attention."""
     name = "7b_1m_dca"
     cfg = CONFIGS[name]
     res = run_layer(name)
@@ -372,10 +528,10 @@ def test_a_shape_1m_sampled_rows():
     ov, os_ = oracle.a_shape_lists(16, 2048, cfg.seq_len)
     for h in range(cfg.n_heads):
         assert a["verts"][h].tolist() == ov.tolist() and a["slashes"][h].tolist() == os_.tolist()
-    for h in oracle_heads(cfg):
-        ctx = key_context(name, h // cfg.group)
-        ro, rl, _ = oracle.sparse_rows(a["q"][h].astype(np.float64), a["rows"], ctx, ov, os_,
-                                       res["sm"])
+    warm_contexts(name, [h // cfg.group for h in a["heads"]])
+    refs = parallel_map(_sparse_job, [(name, h // cfg.group, a["q"][h].astype(np.float64),
+                                       a["rows"], ov, os_, res["sm"]) for h in a["heads"]])
+    for h, (ro, rl, _) in zip(a["heads"], refs):
         compare(a["out"][h].astype(np.float64), ro)
         lse_compare(a["lse"][h].astype(np.float64), rl)
 
@@ -383,13 +539,18 @@ def test_a_shape_1m_sampled_rows():
 @pytest.mark.parametrize("name", ["7b_1m_dca", "14b_256k"])
 def test_decode_full_size(name):
     """Decode steps over the whole cache (1M keys with DCA and YaRN; 256K with
-    5 query heads per KV head) against the oracle's dense causal rows."""
+    5 query heads per KV head) against the oracle's dense causal rows, one
+    head per KV group."""
     cfg = CONFIGS[name]
     res = run_layer(name)
+    warm_contexts(name, range(cfg.n_kv_heads))
+    jobs, where = [], []
     for case in res["decode"]:
-        for h in oracle_heads(cfg):
-            ctx = key_context(name, h // cfg.group)
-            ro, rl = oracle.dense_causal_rows(case["q"][h].astype(np.float64), case["rows"],
-                                              ctx, res["sm"])
-            compare(case["out"][h].astype(np.float64), ro)
-            lse_compare(case["lse"][h].astype(np.float64), rl)
+        for h in group_heads(cfg, case["rows"][0]):
+            jobs.append((name, h // cfg.group, case["q"][h].astype(np.float64), case["rows"],
+                         res["sm"]))
+            where.append((case, h))
+    refs = parallel_map(_dense_job, jobs)
+    for (case, h), (ro, rl) in zip(where, refs):
+        compare(case["out"][h].astype(np.float64), ro)
+        lse_compare(case["lse"][h].astype(np.float64), rl)

@@ -12,7 +12,7 @@ import oracle
 import synth
 from synth.configs import TINY, SEVEN_B_128K, scaled
 from tests.gpu_util import (DEV, MAX_ABS, MEAN_ABS, build_cache, compare, dca_of, host64,
-                            lse_compare, oracle_freqs, oracle_inputs, rope_of)
+                            lse_compare, oracle_freqs, oracle_inputs, product_sm, rope_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ L = pytest.importorskip("long_context_sparse_rope_amd")
 def _layer(cfg, k, v):
     layer = L.ChunkedSparsePrefill(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len,
                                    rope_of(cfg), dca_of(cfg),
-                                   oracle.softmax_scale(cfg.head_dim, cfg.yarn_factor),
+                                   product_sm(cfg),
                                    cfg.n_vert, cfg.n_slash, cfg.last_q, DEV)
     build_cache(layer, k, v, cfg.seq_len)
     return layer
@@ -43,7 +43,7 @@ def _decode_case(cfg, q, k, v, layer, p0, n, out_dtype=torch.float32):
     rows = np.arange(p0, c1)
     for h in range(H):
         ctx = oracle.KeyContext(ko[h // G, :c1], vo[h // G, :c1], th, cfg.dca_chunk,
-                                cfg.dca_local, operands="bf16")
+                                cfg.dca_local)
         ro, rl = oracle.dense_causal_rows(qo[h, p0:c1], rows, ctx, layer.sm_scale)
         if out_dtype == torch.bfloat16:
             d = np.abs(host64(out[h]) - ro)
@@ -58,13 +58,17 @@ def _decode_case(cfg, q, k, v, layer, p0, n, out_dtype=torch.float32):
 @pytest.fixture(scope="module")
 def tiny():
     cfg = TINY
+    assert cfg.dca_chunk - cfg.dca_local == 192
     q, k, v = synth.generate(cfg, DEV)
     return cfg, q, k, v, _layer(cfg, k, v)
 
 
-# TINY: one head, D 64, DCA C 256, W 32 (period S 224), 1024 tokens
-@pytest.mark.parametrize("p0,n", [(1023, 1), (0, 1), (1, 3), (1000, 24), (222, 4),
-                                  (255, 2), (447, 3), (480, 32), (63, 2), (700, 17)])
+# TINY: one head, D 64, DCA C 256, W 64 (period S 192), 1024 tokens.  The
+# rows (190, 4) and (382, 3) straddle the period edges 192 and 384: their
+# earlier rows meet key tiles of the next DCA chunk, all masked for them.
+@pytest.mark.parametrize("p0,n", [(1023, 1), (0, 1), (1, 3), (1000, 24), (190, 4),
+                                  (382, 3), (222, 4), (255, 2), (447, 3), (480, 32), (63, 2),
+                                  (700, 17)])
 def test_decode_tiny(tiny, p0, n):
     cfg, q, k, v, layer = tiny
     _decode_case(cfg, q, k, v, layer, p0, n)

@@ -14,7 +14,7 @@ import oracle
 import synth
 from synth.configs import FOURTEEN_B_512K_REFINE, SEVEN_B_128K, scaled
 from tests.gpu_util import (DEV, build_cache, compare, dca_of, host64, lse_compare,
-                            oracle_freqs, oracle_inputs, rope_of)
+                            oracle_freqs, oracle_inputs, product_sm, rope_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,15 +38,14 @@ BS = lambda k: {"kind": "block", "n_blocks": k}                           # noqa
 def _layer(cfg):
     return L.ChunkedSparsePrefill(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len,
                                   rope_of(cfg), dca_of(cfg),
-                                  oracle.softmax_scale(cfg.head_dim, cfg.yarn_factor),
+                                  product_sm(cfg),
                                   cfg.n_vert, cfg.n_slash, cfg.last_q, DEV)
 
 
 def _contexts(cfg, k, v, upto):
     _, ko, vo = oracle_inputs(k[:1], k, v)
     th = oracle_freqs(cfg)
-    return [oracle.KeyContext(ko[g, :upto], vo[g, :upto], th, cfg.dca_chunk, cfg.dca_local,
-                              operands="bf16") for g in range(cfg.n_kv_heads)]
+    return [oracle.KeyContext(ko[g, :upto], vo[g, :upto], th, cfg.dca_chunk, cfg.dca_local) for g in range(cfg.n_kv_heads)]
 
 
 @pytest.mark.parametrize("n_sink,n_local,n_ctx", [(16, 2048, 65536), (0, 300, 1000),
@@ -179,7 +178,7 @@ def test_search_head_patterns(cfg):
                     rec = oracle.attention_recall(qo[h, r], r, ctxs[h // G], ov, os_,
                                                   layer.sm_scale)[2]
                 ref[ci, h] += rec.mean() / len(chunks)
-    got = scores.numpy()
+    got = np.asarray(scores)
     d = np.abs(got - ref)
     print(f"[search] {cfg.name}: score max diff {d.max():.2e}; choices {choice}", flush=True)
     print("[search] scores (candidate x head):\n" + np.array2string(got, precision=3), flush=True)
@@ -237,11 +236,11 @@ def test_refinement_over_mixed_kinds():
     torch.cuda.synchronize()
     cur = start
     for r in range(len(hist) - 1):
-        nxt, raised = oracle.refine_sizes(hist[r].numpy(), kind_of, cur, c1)
+        nxt, raised = oracle.refine_sizes(hist[r], kind_of, cur, c1)
         assert raised.any()
-        assert np.all(hist[r + 1].numpy()[raised] >= hist[r].numpy()[raised] - 1e-5)
+        assert np.all(hist[r + 1][raised] >= hist[r][raised] - 1e-5)
         cur = nxt
-    final, _ = oracle.refine_sizes(hist[-1].numpy(), kind_of, cur, c1)
+    final, _ = oracle.refine_sizes(hist[-1], kind_of, cur, c1)
     assert sizes() == cur, (sizes(), cur)
     print(f"[refine] {len(hist) - 1} rounds; sizes {start} -> {cur}", flush=True)
     # final rows against the oracle on the final patterns

@@ -110,6 +110,19 @@ def test_yarn_blend_end_points_and_ramp():
         assert (fast.sum(), mid.sum(), slow.sum()) == (29, 14, 21)
 
 
+def test_yarn_ramp_hand_worked():
+    """Three pairs inside the ramp (base 1e7, D 128, s 4, L 262,144), worked
+    by hand step by step in tests/golden/yarn_ramp.txt."""
+    y = oracle.yarn_inv_freq(128, 1e7, 4.0, 262144, beta_fast=32.0, beta_slow=1.0)
+    th = oracle.rope_inv_freq(128, 1e7)
+    for p, theta, gamma, theta_new in _rows("yarn_ramp.txt"):
+        p = int(p)
+        assert th[p] == pytest.approx(theta, rel=1e-14)
+        assert y[p] == pytest.approx(theta_new, rel=1e-13)
+        # the kept fraction of the frequency is (1 - gamma) / s + gamma
+        assert y[p] / th[p] == pytest.approx((1 - gamma) / 4 + gamma, rel=1e-13)
+
+
 def test_bf16_round_ties_and_library():
     one = np.float32(1.0)
     cases = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0e38, 1e-40],
