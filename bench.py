@@ -258,7 +258,7 @@ def cpu_baseline(cfg, layer, q, k, v, budget_s=20.0, step_pairs=None):
     K = k[g, :c1].float().cpu().numpy().astype(np.float64)
     V = v[g, :c1].float().cpu().numpy().astype(np.float64)
     th = oracle.rope_inv_freq(cfg.head_dim, cfg.rope_base)
-    ctx = oracle.KeyContext(K, V, th, cfg.dca_chunk, cfg.dca_local, operands="bf16")
+    ctx = oracle.KeyContext(K, V, th, cfg.dca_chunk, cfg.dca_local)
     ctx.k_dca()
     setup_s = time.perf_counter() - t_setup
     rng = np.random.default_rng(0)

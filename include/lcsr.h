@@ -33,8 +33,13 @@
  *    LCSR_EHIP has written nothing.  lcsr_last_error() gives a message for
  *    the last failing call of the calling thread.  No exception crosses the
  *    ABI; calls are thread-safe.
- *  - Queries rotate in bf16 on the matrix cores with fp32 accumulation; RoPE
- *    angles are formed in fp64 from the integer position.
+ *  - Precision.  Inputs (queries, keys, values) are bf16 (fp32 queries are
+ *    rounded to bf16 on entry).  RoPE angles are formed in fp64 from the
+ *    integer position and the rotation in fp32.  QK^T runs on the matrix
+ *    cores with fp16 operands, the rotated keys of the K cache and the
+ *    rotated queries, each rounded to nearest; PV with bf16 operands (the V
+ *    cache and the probabilities); every product accumulates in fp32.
+ *    Rotated keys and queries must lie within the fp16 range (|x| < 65504).
  */
 #ifndef LCSR_H
 #define LCSR_H
@@ -60,10 +65,12 @@ extern "C" {
 /* ---- element types ----------------------------------------------------- */
 #define LCSR_BF16 0
 #define LCSR_FP32 1
+#define LCSR_FP16 2
 
 /* ---- flags ------------------------------------------------------------- */
 #define LCSR_ROPE_YARN_FREQ 0x1u  /* lcsr_rope_t.flags: YaRN frequency blend  */
 #define LCSR_ROPE_NO_ROTATE 0x2u  /* rope_yarn_apply: convert/scale only      */
+#define LCSR_ROPE_OUT_FP16 0x4u   /* rope_yarn_apply: store fp16, not bf16    */
 #define LCSR_EST_SELECT_ONLY 0x1u /* estimate: scores are inputs, select only */
 #define LCSR_ATTN_DENSE 0x1u      /* attention: every causal key (no pattern) */
 #define LCSR_BS_SELECT_ONLY 0x1u  /* block estimate: scores are inputs        */
@@ -115,8 +122,9 @@ typedef struct lcsr_problem {
   int32_t q_dtype;     /* LCSR_BF16 or LCSR_FP32 (fp32 is rounded to bf16)  */
   int64_t q_stride_h;
   int64_t q_stride_t;
-  const void* k_cache; /* bf16 [H_kv, >= chunk_start + chunk_len, D], keys
-                          rotated at P_k(j) (lcsr_rope_yarn_apply)         */
+  const void* k_cache; /* fp16 [H_kv, >= chunk_start + chunk_len, D], keys
+                          rotated at P_k(j) (lcsr_rope_yarn_apply with
+                          LCSR_ROPE_OUT_FP16)                              */
   const void* v_cache; /* bf16, same layout; unused by the estimate        */
   int64_t kv_stride_h;
   int64_t kv_stride_t;
@@ -164,17 +172,21 @@ const char* lcsr_last_error(void);
 float lcsr_softmax_scale(const lcsr_rope_t* rope, int32_t head_dim);
 
 /* lcsr_rope_yarn_apply — y[h, t, :] = scale * R(pos[t]) x[h, t, :], stored
- * bf16.  Rotation pairs (x_p, x_{p+D/2}) turn by pos[t] * theta_p
+ * bf16 (or fp16).  Rotation pairs (x_p, x_{p+D/2}) turn by pos[t] * theta_p
  * (rotate_half, [architecture overview] §2.4 code; relative-position
  * property, [long-context blog] RoPE原理の復習).  In the chunk loop, pos is
- * P_k of the chunk's tokens and y is the chunk's rows of the K cache.
+ * P_k of the chunk's tokens and y is the chunk's rows of the K cache
+ * (fp16).
  *   x      [n_heads, n_tok, head_dim], x_dtype LCSR_BF16 or LCSR_FP32
- *   y      bf16 [n_heads, n_tok, head_dim]; may equal x (in place) only
- *          when x is bf16 with the same strides
+ *   y      bf16 (fp16 with LCSR_ROPE_OUT_FP16) [n_heads, n_tok, head_dim],
+ *          rounded to nearest; may equal x (in place) only when x is bf16
+ *          with the same strides
  *   pos    int32 [n_tok] (device), positions >= 0
  *   rope   (host) frequency setup; scale multiplies the result (1 = none)
  *   flags  LCSR_ROPE_NO_ROTATE: y = scale * x (a dtype conversion/copy,
  *          used to fill the V cache); pos may then be NULL.
+ *          LCSR_ROPE_OUT_FP16: y is fp16 (the K cache of the attention
+ *          calls).
  * Errors: LCSR_EINVAL for null pointers, odd head_dim, head_dim > 256,
  * misalignment; LCSR_EHIP if the launch fails. */
 int lcsr_rope_yarn_apply(const void* x, int32_t x_dtype, int64_t x_stride_h,

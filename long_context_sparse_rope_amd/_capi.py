@@ -13,9 +13,11 @@ LCSR_EHIP = -4
 
 LCSR_BF16 = 0
 LCSR_FP32 = 1
+LCSR_FP16 = 2
 
 LCSR_ROPE_YARN_FREQ = 0x1
 LCSR_ROPE_NO_ROTATE = 0x2
+LCSR_ROPE_OUT_FP16 = 0x4
 LCSR_EST_SELECT_ONLY = 0x1
 LCSR_ATTN_DENSE = 0x1
 LCSR_BS_SELECT_ONLY = 0x1

@@ -264,6 +264,7 @@ int lcsr_rope_yarn_apply(const void* x, int32_t x_dtype, int64_t x_stride_h,
   a.src_sh = x_stride_h;
   a.src_st = x_stride_t;
   a.dst = static_cast<uint16_t*>(y);
+  a.dst_dtype = (flags & LCSR_ROPE_OUT_FP16) ? LCSR_FP16 : LCSR_BF16;
   a.dst_sh = y_stride_h;
   a.dst_st = y_stride_t;
   a.n_heads = n_heads;

@@ -22,7 +22,8 @@
 //  * per (wave, key tile) the pair mask is: key <= row and (offset bit of the
 //    wave's head or column bit in a marked granule); tiles a head does not
 //    touch are skipped by its wave, tiles it fully covers run unmasked;
-//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (V^T read
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (fp16 rotated keys and queries)
+//    and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (V^T read
 //    with the LDS transpose load ds_read_b64_tr_b16): each lane owns one
 //    query row, so the softmax max / sum and the O rescale are in-lane; a
 //    tile's own max is taken only when a row has none yet or its weights sum
@@ -400,7 +401,7 @@ __device__ __forceinline__ void issue_tile(const char* kg, const char* vg, uint3
 
 template <int D>
 struct WaveState {
-  bf16x8 q[D / 16];
+  f16x8 q[D / 16];   // rotated query rows, the fp16 operand of QK^T
   f32x16 o[D / 32];
   float m, l;
 };
@@ -415,7 +416,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int h, int32_t i0, int
   if (t > a.L - 1) t = a.L - 1;
   const uint16_t* base = a.q_rot + (((int64_t)var * a.H + h) * a.L + t) * D + 8 * (lane >> 5);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const bf16x8*>(base + s * 16);
+  for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const f16x8*>(base + s * 16);
 }
 
 // max / sum of this lane's value and the value of lane l ^ 32
@@ -453,17 +454,17 @@ __device__ __forceinline__ void wave_scores(float scale_log2, const char* smem,
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     if (!act[kb]) continue;
-    bf16x8 kf[KS];
+    f16x8 kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      kf[s] = *reinterpret_cast<const bf16x8*>(smem + c.k_rd[s] + kb * 32 * RB);
+      kf[s] = *reinterpret_cast<const f16x8*>(smem + c.k_rd[s] + kb * 32 * RB);
     // keep the reads ahead of the products (else the scheduler waits for each
     // read next to its MFMA)
     __builtin_amdgcn_sched_barrier(0);
     acc[kb] = (f32x16){};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], st.q[s], acc[kb], 0, 0, 0);
+      acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], st.q[s], acc[kb], 0, 0, 0);
   }
   mid();
   after_qk();
@@ -1314,7 +1315,7 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
     if (__ballot(var != cur_var) != 0ull) {
       const uint16_t* qb = a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const bf16x8*>(qb + s * 16);
+      for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const f16x8*>(qb + s * 16);
       wait_vm<0>();
       cur_var = var;
     }
@@ -1545,7 +1546,7 @@ __global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
       const uint16_t* qp =
           a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;
 #pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const bf16x8*>(qp + s2 * 16);
+      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const f16x8*>(qp + s2 * 16);
       wait_vm<0>();
       cur_var = var;
     }
@@ -1761,7 +1762,7 @@ __global__ void __launch_bounds__(64 * (NW + 1)) bs_attn_gqa_kernel(BsArgs a) {
       const uint16_t* qp =
           a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;
 #pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const bf16x8*>(qp + s2 * 16);
+      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const f16x8*>(qp + s2 * 16);
       wait_vm<0>();
       cur_var = var;
     }

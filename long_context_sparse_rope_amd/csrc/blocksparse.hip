@@ -33,7 +33,7 @@ __device__ __forceinline__ float load_q(const void* q, int32_t dtype, int64_t id
   return bf16_to_f32(static_cast<const uint16_t*>(q)[idx]);
 }
 
-// grid (n_kb, H_kv), 64 threads: mean of each 64-key block of the cache,
+// grid (n_kb, H_kv), 64 threads: mean of each 64-key block of the (fp16) cache,
 // stored as float4 [H_kv][D / 4][n_kb] so that lanes of the score kernel
 // (one key block each) read consecutive addresses.
 __global__ void __launch_bounds__(64) bs_pool_keys(const uint16_t* __restrict__ k, int64_t kv_sh,
@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(64) bs_pool_keys(const uint16_t* __restrict__ 
     const uint16_t* src = k + g * kv_sh + d;
     float s = 0.f;
 #pragma unroll 8
-    for (int64_t j = j0; j < j1; ++j) s += bf16_to_f32(src[j * kv_st]);
+    for (int64_t j = j0; j < j1; ++j) s += f16_to_f32(src[j * kv_st]);
     pk[(((int64_t)g * (D / 4) + d / 4) * n_kb + kb) * 4 + d % 4] = s * inv;
   }
 }

@@ -24,9 +24,9 @@ namespace lcsr {
 namespace {
 
 struct EstArgs {
-  const uint16_t* k;      // K cache, rotated at P_k
+  const uint16_t* k;      // K cache (fp16), rotated at P_k
   int64_t kv_sh, kv_st;
-  const uint16_t* q_est;  // [n_kc][H][64][D]
+  const uint16_t* q_est;  // [n_kc][H][64][D] fp16
   int32_t H, G;
   int64_t n_ctx;          // c1
   int64_t row0;           // first estimate row
@@ -136,24 +136,24 @@ __device__ void est_loader(const EstArgs& a, int g, int64_t t_begin, int64_t t_e
 
 template <int D>
 __device__ __forceinline__ void load_q_frags(const EstArgs& a, int h, int64_t c,
-                                             bf16x8 (&qf)[2][D / 16]) {
+                                             f16x8 (&qf)[2][D / 16]) {
   const int lane = threadIdx.x & 63;
   const uint16_t* base = a.q_est + (((int64_t)c * a.H + h) * kEstRows) * D;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      qf[b][s] = *reinterpret_cast<const bf16x8*>(
+      qf[b][s] = *reinterpret_cast<const f16x8*>(
           base + (int64_t)(b * 32 + (lane & 31)) * D + s * 16 + 8 * (lane >> 5));
 }
 
 // K fragment s of key block kb: lane -> key row 32 kb + lane % 32, chunk
 // 2 s + lane / 32.
 template <int D>
-__device__ __forceinline__ bf16x8 k_frag(const char* ks, int kb, int s) {
+__device__ __forceinline__ f16x8 k_frag(const char* ks, int kb, int s) {
   const int lane = threadIdx.x & 63;
   const int row = kb * 32 + (lane & 31);
-  return *reinterpret_cast<const bf16x8*>(ks + row * KTile<D>::kRowBytes +
+  return *reinterpret_cast<const f16x8*>(ks + row * KTile<D>::kRowBytes +
                                           kslot<D>(2 * s + (lane >> 5), row) * 16);
 }
 
@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
   }
   const int h = g * a.G + sub * a.nw + w;
   const bool active = w < n_here && ((a.head_mask >> h) & 1);
-  bf16x8 qf[2][D / 16];
+  f16x8 qf[2][D / 16];
   int64_t cur_c = -1;
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   const int half = lane >> 5;
@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
         acc[kb] = (f32x16){};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<D>(ks, kb, s), qf[b][s],
+          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k_frag<D>(ks, kb, s), qf[b][s],
                                                             acc[kb], 0, 0, 0);
       }
       const int64_t row = a.row0 + b * 32 + (lane & 31);
@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
   const int h = g * a.G + sub * a.nw + w;
   const bool active = w < n_here && ((a.head_mask >> h) & 1);
   const int half = lane >> 5;
-  bf16x8 qf[2][D / 16];
+  f16x8 qf[2][D / 16];
   int64_t cur_c = -1;
   // log2-sum-exp of the wave's 64 rows (INFINITY for padding rows -> p = 0),
   // kept in LDS: rows 8 j + 4 half .. + 3 of block b are one 16-byte read
@@ -360,7 +360,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
       f32x16 acc = {};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[b][s], k_frag<D>(ks, kb, s), acc, 0,
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[b][s], k_frag<D>(ks, kb, s), acc, 0,
                                                       0, 0);
       const int64_t key = k0 + kb * 32 + (lane & 31);
       float lr[16];

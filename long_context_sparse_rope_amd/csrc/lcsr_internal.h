@@ -18,6 +18,7 @@ int check_launch(const char* what);
 
 // ---------------------------------------------------------------- vectors
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -80,6 +81,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// fp16 <-> fp32 (round to nearest even on the way down).  The QK^T
+// operands (rotated keys in the K cache, rotated queries) are fp16: for the
+// unit-scale activations of attention its 11-bit significand rounds 8x finer
+// than bf16's 8 bits at the same matrix-core rate.
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_f16(lo)) | (static_cast<uint32_t>(f32_to_f16(hi)) << 16);
+}
+// Round to the destination type (LCSR_BF16 or LCSR_FP16).
+__device__ __forceinline__ uint16_t f32_to_16(float f, int32_t dtype) {
+  return dtype == LCSR_FP16 ? f32_to_f16(f) : f32_to_bf16(f);
+}
+__device__ __forceinline__ uint32_t pack_16x2(float lo, float hi, int32_t dtype) {
+  return dtype == LCSR_FP16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
 // Angle pos * theta in fp64, reduced to [-pi, pi], then cos/sin.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, double inv_freq,
                                              float* c, float* s) {
@@ -93,7 +115,7 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, double inv_freq,
 }
 
 // ---------------------------------------------------------------- launches
-// Rotate rows of a [H, n_tok, D] tensor into a bf16 destination.
+// Rotate rows of a [H, n_tok, D] tensor into a bf16 or fp16 destination.
 // Position of token t (0-based within the call):
 //   kPosArray:   pos[t]
 //   kPosAffine:  t + pos_offset
@@ -106,6 +128,7 @@ struct RotateArgs {
   int32_t src_dtype;
   int64_t src_sh, src_st;
   uint16_t* dst;
+  int32_t dst_dtype;   // LCSR_BF16 or LCSR_FP16
   int64_t dst_vs, dst_sh, dst_st;
   int64_t n_heads, n_tok, head_dim;
   const int32_t* pos;
@@ -125,13 +148,13 @@ int launch_dca_positions(int64_t tok_start, int64_t n_tok, const DcaParams& d,
 
 // Queries of the chunk rotated for the attention: variant v (0 intra,
 // 1 succ, 2 inter; only 0 = plain position without DCA) written to
-// dst[v][h][t][D] bf16.
+// dst[v][h][t][D] fp16 (the QK^T operand type).
 int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
                              const DcaParams& d, uint16_t* dst, int n_var,
                              hipStream_t s, bool decode = false);
 
 // Estimate rows rotated at continuous positions for each key DCA chunk c:
-// dst[c][h][r][D] with position (row - c * S).
+// dst[c][h][r][D] fp16 with position (row - c * S).
 int launch_rotate_q_estimate(const lcsr_problem_t& p, const FreqTable& ft,
                              const DcaParams& d, int64_t row0, int n_rows,
                              int n_kc, uint16_t* dst, hipStream_t s);

@@ -21,7 +21,7 @@ struct RecallArgs {
   const void* q;
   int32_t q_dtype;
   int64_t q_sh, q_st;
-  const uint16_t* k;
+  const uint16_t* k;      // K cache (fp16)
   int64_t kv_sh, kv_st;
   int32_t H, G, D;
   int64_t c0, L, n_ctx;
@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
   const int64_t i = a.c0 + t;
   const int half = a.D / 2;
   const int n_var = a.dca.period ? 3 : 1;
-  // rotated query variants, rounded to bf16 as the matrix-core path feeds them
+  // rotated query variants, rounded to fp16 as the matrix-core path feeds them
   for (int x = threadIdx.x; x < n_var * half; x += kRecallThreads) {
     const int v = x / half, p = x % half;
     const int64_t pos = dca_query_pos(i, v, a.dca);
@@ -92,8 +92,8 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
     }
     x1 = bf16_to_f32(f32_to_bf16(x1));
     x2 = bf16_to_f32(f32_to_bf16(x2));
-    qv[v][p] = bf16_to_f32(f32_to_bf16(x1 * c - x2 * s));
-    qv[v][p + half] = bf16_to_f32(f32_to_bf16(x2 * c + x1 * s));
+    qv[v][p] = f16_to_f32(f32_to_f16(x1 * c - x2 * s));
+    qv[v][p + half] = f16_to_f32(f32_to_f16(x2 * c + x1 * s));
   }
   const bool blocks = a.blk_idx != nullptr;
   if (blocks) {
@@ -129,8 +129,8 @@ __global__ void __launch_bounds__(kRecallThreads) recall_kernel(RecallArgs a) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(kr + d);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dot += qv[v][d + 2 * e] * __uint_as_float(w[e] << 16);
-        dot += qv[v][d + 2 * e + 1] * __uint_as_float(w[e] & 0xFFFF0000u);
+        dot += qv[v][d + 2 * e] * f16_to_f32((uint16_t)(w[e] & 0xFFFFu));
+        dot += qv[v][d + 2 * e + 1] * f16_to_f32((uint16_t)(w[e] >> 16));
       }
     }
     const float x = dot * a.scale_log2;

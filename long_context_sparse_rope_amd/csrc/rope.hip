@@ -4,7 +4,9 @@
 // architecture page, §2.4 code): the pair (x_p, x_{p+D/2}) turns by
 // pos * theta_p.  The angle is formed in fp64 from the integer position and
 // reduced to [-pi, pi] before sin/cos, so positions up to 2^31 keep full
-// fp32 accuracy; the rotation itself is fp32 and the store bf16 (RNE).
+// fp32 accuracy; the rotation itself is fp32 and the store bf16 or fp16
+// (RNE): fp16 for the QK^T operands (K cache, query variants), bf16 for
+// the V cache copy.
 #include <cmath>
 
 #include "lcsr_internal.h"
@@ -89,8 +91,8 @@ __global__ void __launch_bounds__(256) rotate_kernel(RotateArgs a, FreqTable ft,
       const float y1 = (x1 * c[v] - x2 * s[v]) * a.scale;
       const float y2 = (x2 * c[v] + x1 * s[v]) * a.scale;
       uint16_t* d = a.dst + v * a.dst_vs + h * a.dst_sh + t * a.dst_st;
-      d[p] = f32_to_bf16(y1);
-      d[p + half] = f32_to_bf16(y2);
+      d[p] = f32_to_16(y1, a.dst_dtype);
+      d[p + half] = f32_to_16(y2, a.dst_dtype);
     }
   }
 }
@@ -143,9 +145,11 @@ __global__ void __launch_bounds__(256) rotate4_kernel(RotateArgs a, FreqTable ft
         y2[j] = (x2[j] * c[v][j] + x1[j] * s[v][j]) * a.scale;
       }
       uint16_t* d = a.dst + v * a.dst_vs + h * a.dst_sh + t * a.dst_st + p0;
-      *reinterpret_cast<uint2*>(d) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+      const int32_t dt = a.dst_dtype;
+      *reinterpret_cast<uint2*>(d) =
+          make_uint2(pack_16x2(y1[0], y1[1], dt), pack_16x2(y1[2], y1[3], dt));
       *reinterpret_cast<uint2*>(d + half) =
-          make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+          make_uint2(pack_16x2(y2[0], y2[1], dt), pack_16x2(y2[2], y2[3], dt));
     }
   }
 }
@@ -230,6 +234,7 @@ int launch_rotate_q_variants(const lcsr_problem_t& p, const FreqTable& ft,
   a.src_sh = p.q_stride_h;
   a.src_st = p.q_stride_t;
   a.dst = dst;
+  a.dst_dtype = LCSR_FP16;
   a.dst_vs = H * L * D;
   a.dst_sh = L * D;
   a.dst_st = D;
@@ -259,6 +264,7 @@ int launch_rotate_q_estimate(const lcsr_problem_t& p, const FreqTable& ft,
     a.src_sh = p.q_stride_h;
     a.src_st = p.q_stride_t;
     a.dst = dst + (int64_t)c * H * kEstRows * D;
+    a.dst_dtype = LCSR_FP16;
     a.dst_sh = (int64_t)kEstRows * D;
     a.dst_st = D;
     a.n_heads = H;

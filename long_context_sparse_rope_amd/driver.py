@@ -38,8 +38,9 @@ def _head_means(recall):
 class ChunkedSparsePrefill:
     """One layer's KV cache plus the calls of the chunk loop.
 
-    K and V caches are bf16 [H_kv, max_ctx, D]; keys are stored rotated at
-    their DCA key position.  Budgets are per query head and may be raised by
+    The K cache is fp16 and the V cache bf16, both [H_kv, max_ctx, D]; keys
+    are stored rotated at their DCA key position (fp16: the QK^T operand
+    type of the kernels).  Budgets are per query head and may be raised by
     `refine_chunk`.  A head is a vertical-slash head (budgets n_vert,
     n_slash, pattern from the estimate), an A-shape head (n_sink, n_local, no
     estimate) or a block-sparse head (n_blocks key blocks per query block);
@@ -58,9 +59,10 @@ class ChunkedSparsePrefill:
         self.a_shape = [None] * n_heads      # (n_sink, n_local) of A-shape heads
         self.blocks = [None] * n_heads       # n_blocks of block-sparse heads
         self.block_pattern = None
-        self.k_cache = torch.empty((n_kv_heads, self.max_ctx, head_dim), dtype=torch.bfloat16,
+        self.k_cache = torch.empty((n_kv_heads, self.max_ctx, head_dim), dtype=torch.float16,
                                    device=self.device)
-        self.v_cache = torch.empty_like(self.k_cache)
+        self.v_cache = torch.empty((n_kv_heads, self.max_ctx, head_dim), dtype=torch.bfloat16,
+                                   device=self.device)
         mv = max_vert or max(self.n_vert)
         ms = max_slash or max(self.n_slash)
         self.pattern = ops.Pattern(n_heads, mv, ms, self.device)

@@ -165,8 +165,8 @@ def _problem(q, k_cache, v_cache, chunk_start, rope, dca, sm_scale):
         raise ValueError("q is [H, L, D], caches are [H_kv, N, D]")
     if q.stride(2) != 1 or k_cache.stride(2) != 1 or (v_cache is not None and v_cache.stride(2) != 1):
         raise ValueError("the head dimension must be contiguous")
-    if k_cache.dtype != torch.bfloat16 or (v_cache is not None and v_cache.dtype != torch.bfloat16):
-        raise TypeError("caches must be bfloat16")
+    if k_cache.dtype != torch.float16 or (v_cache is not None and v_cache.dtype != torch.bfloat16):
+        raise TypeError("the K cache must be float16 and the V cache bfloat16")
     if v_cache is not None and v_cache.stride() != k_cache.stride():
         raise ValueError("K and V caches must share strides")
     H, L, D = q.shape
@@ -200,16 +200,21 @@ def workspace_bytes(kind, q, k_cache, chunk_start, rope, dca, sm_scale=1.0, max_
     return C.load().lcsr_workspace_bytes(kind, ctypes.byref(prob), max_vert, max_slash)
 
 
-def rope_yarn_apply(x, pos, rope, out=None, scale=1.0, rotate=True, stream=None):
-    """out[h, t] = scale * R(pos[t]) x[h, t] in bf16 (lcsr_rope_yarn_apply)."""
+def rope_yarn_apply(x, pos, rope, out=None, scale=1.0, rotate=True, out_dtype=torch.bfloat16,
+                    stream=None):
+    """out[h, t] = scale * R(pos[t]) x[h, t] stored bf16 or fp16 (the dtype of
+    `out`, else out_dtype) (lcsr_rope_yarn_apply)."""
     if x.dim() != 3 or x.stride(2) != 1:
         raise ValueError("x must be [H, n, D] with a contiguous last dimension")
     H, n, D = x.shape
     if out is None:
-        out = torch.empty((H, n, D), dtype=torch.bfloat16, device=x.device)
-    if out.dtype != torch.bfloat16 or out.shape != x.shape or out.stride(2) != 1:
-        raise ValueError("out must be bf16 with the shape of x")
+        out = torch.empty((H, n, D), dtype=out_dtype, device=x.device)
+    if (out.dtype not in (torch.bfloat16, torch.float16) or out.shape != x.shape
+            or out.stride(2) != 1):
+        raise ValueError("out must be bf16 or fp16 with the shape of x")
     flags = 0 if rotate else C.LCSR_ROPE_NO_ROTATE
+    if out.dtype == torch.float16:
+        flags |= C.LCSR_ROPE_OUT_FP16
     r = rope.c()
     _check(C.load().lcsr_rope_yarn_apply(
         x.data_ptr(), _dtype_code(x), x.stride(0), x.stride(1), out.data_ptr(), out.stride(0),

@@ -31,8 +31,8 @@ beta_slow and beta_fast (the pages' snippet is garbled) is pinned by its end
 points, its band sizes and three pairs worked by hand inside the ramp.
 """
 
-from .rope import (bf16_round, bf16_round64, rope_inv_freq, yarn_inv_freq, yarn_mscale,
-                   softmax_scale, rope_rotate, rope_apply)
+from .rope import (bf16_round, bf16_round64, fp16_round64, rope_inv_freq, yarn_inv_freq,
+                   yarn_mscale, softmax_scale, rope_rotate, rope_apply)
 from .dca import (dca_position_maps, dca_chunk_of, query_positions,
                   relative_positions)
 from .attention import (KeyContext, attention_logits, dense_causal_rows,
@@ -44,7 +44,7 @@ from .blocksparse import (BLOCK, block_scores, select_blocks, block_key_set,
                           block_sparse_rows)
 
 __all__ = [
-    "bf16_round", "bf16_round64", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",
+    "bf16_round", "bf16_round64", "fp16_round64", "rope_inv_freq", "yarn_inv_freq", "yarn_mscale",
     "softmax_scale", "rope_rotate", "rope_apply",
     "dca_position_maps", "dca_chunk_of", "query_positions",
     "relative_positions",

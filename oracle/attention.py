@@ -12,7 +12,7 @@ caller passes the KeyContext of that KV head.
 import numpy as np
 
 from .dca import dca_position_maps, query_positions
-from .rope import bf16_round64, rope_rotate
+from .rope import bf16_round64, fp16_round64, rope_rotate
 
 
 class KeyContext:
@@ -22,19 +22,21 @@ class KeyContext:
     cached: at DCA key positions (attention) and at the plain token index
     (the continuous positions used for pattern selection).
 
-    operands="fp64" keeps rotated keys and queries exact.  operands="bf16"
-    takes the attention's precision statement, bf16 operands with fp32
-    accumulation, at its word: the rotated keys (the K cache, stored once at
-    the DCA key position: [Qwen2.5-1M explainer] 推論フレームワーク) and the
-    rotated queries enter the QK^T products as bfloat16, each rounded to the
-    nearest (ties to even) from its exact fp64 rotation.  Every other step
-    stays fp64.  Reading: in a bf16 model the RoPE output has the model's
-    dtype, and the interface fixes the cache as bf16.
+    operands="fp64" (the parity reference) keeps rotated keys and queries
+    exact.  operands="bf16" or "fp16" models a matrix-core operand type: the
+    rotated keys (the K cache, stored once at the DCA key position:
+    [Qwen2.5-1M explainer] 推論フレームワーク) and the rotated queries enter
+    the QK^T products rounded to the nearest (ties to even) value of that
+    type from their exact fp64 rotation.  Every other step stays fp64.
+    These modes only separate the operand rounding from the rest of an
+    error; nothing is asserted against them.
     """
 
+    _ROUND = {"bf16": bf16_round64, "fp16": fp16_round64}
+
     def __init__(self, K, V, inv_freq, dca_chunk=0, dca_local=0, operands="fp64"):
-        if operands not in ("fp64", "bf16"):
-            raise ValueError("operands must be 'fp64' or 'bf16'")
+        if operands not in ("fp64", "bf16", "fp16"):
+            raise ValueError("operands must be 'fp64', 'bf16' or 'fp16'")
         self.operands = operands
         self.K = np.asarray(K, dtype=np.float64)
         self.V = None if V is None else np.asarray(V, dtype=np.float64)
@@ -46,7 +48,7 @@ class KeyContext:
 
     def operand(self, x):
         """A rotated vector as it enters a QK^T product."""
-        return bf16_round64(x) if self.operands == "bf16" else x
+        return x if self.operands == "fp64" else self._ROUND[self.operands](x)
 
     @property
     def n_keys(self):
@@ -66,11 +68,11 @@ class KeyContext:
     def k_cont(self):
         """Keys rotated at their own index j (continuous positions).
 
-        From a bf16 cache, the cached key turns on by j - P_k(j), a multiple
-        of the key period: R(j) k = R(j - P_k(j)) R(P_k(j)) k."""
+        From a rounded cache, the cached key turns on by j - P_k(j), a
+        multiple of the key period: R(j) k = R(j - P_k(j)) R(P_k(j)) k."""
         if self._k_cont is None:
             idx = np.arange(self.n_keys)
-            if self.operands == "bf16":
+            if self.operands != "fp64":
                 self._k_cont = rope_rotate(self.k_dca(), idx - self._pk(), self.inv_freq)
             else:
                 self._k_cont = rope_rotate(self.K, idx, self.inv_freq)

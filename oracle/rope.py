@@ -14,8 +14,8 @@ def bf16_round(x):
     The library converts fp32 inputs to bf16 on entry; the oracle applies
     the same rounding to those inputs (the tiny fp32 config).  Rounding of
     rotated operands is a separate, optional mode of the oracle
-    (bf16_round64 through KeyContext(operands="bf16")) that models the
-    matrix cores' operand precision; parity is asserted without it.
+    (KeyContext(operands="bf16" or "fp16")) that models an operand precision
+    of the matrix cores; parity is asserted without it.
     """
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     bits = a.view(np.uint32).astype(np.uint64)
@@ -29,11 +29,18 @@ def bf16_round64(x):
     returned as float64, with no float32 step in between.
 
     bfloat16 keeps 8 significant bits: with x = m 2^e and 1/2 <= |m| < 1,
-    the result is round_half_even(256 m) 2^(e - 8).  Used for the bf16 K
-    cache, which stores keys after their rotation.
+    the result is round_half_even(256 m) 2^(e - 8).
     """
     m, e = np.frexp(np.asarray(x, dtype=np.float64))
     return np.ldexp(np.round(m * 256.0), e - 8)
+
+
+def fp16_round64(x):
+    """Round float64 values straight to the nearest IEEE binary16 (ties to
+    even), returned as float64.  numpy converts float64 to float16 in one
+    correctly rounded step (11 significant bits; subnormals below 2^-14,
+    overflow to inf above 65504)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
 def rope_inv_freq(head_dim, base):

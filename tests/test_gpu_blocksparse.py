@@ -105,7 +105,7 @@ def test_selection_ties_and_signed_zeros():
     sc_h = vals[rng.integers(0, vals.size, size=(H, n_qb, n_kb))]
     sc = torch.from_numpy(sc_h).to(DEV)
     q = torch.zeros(H, c1 - c0, 64, dtype=torch.bfloat16, device=DEV)
-    kc = torch.zeros(1, c1, 64, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(1, c1, 64, dtype=torch.float16, device=DEV)
     budgets = [3, 17, 41]
     pat = L.BlockPattern(H, n_qb, 64, DEV)
     L.block_sparse_estimate(q, kc, c0, L.RopeConfig(base=1e4), L.DcaConfig(0, 0), 0.125,

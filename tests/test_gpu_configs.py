@@ -31,8 +31,9 @@ import long_context_sparse_rope_amd as L
 import oracle
 import synth
 from synth.configs import CONFIGS, scaled
-from tests.gpu_util import (DEV, compare, dca_of, lse_compare, near_tie_check, oracle_freqs,
-                            parallel_map, product_sm, rope_of, score_compare)
+from tests.gpu_util import (DEV, MAX_ABS, MEAN_ABS, SCORE_REL, SCORE_REL_LARGE_LOGITS, compare,
+                            dca_of, lse_compare, near_tie_check, oracle_freqs, parallel_map,
+                            product_sm, rope_of, score_compare)
 
 pytestmark = pytest.mark.gpu
 
@@ -344,8 +345,9 @@ def test_estimate_scores_full_size(layer_run):
         n = len(rows)
         assert abs(gv.sum() - n) < 1e-3 * n and abs(gs.sum() - n) < 1e-3 * n
         print(f"[estimate] {name} chunk {c} head {h}:", flush=True)
-        score_compare(gv, rv, "vertical")
-        score_compare(gs, rs, "slash")
+        rel = SCORE_REL_LARGE_LOGITS if cfg.planting == "far_sinks_stripes" else SCORE_REL
+        score_compare(gv, rv, "vertical", rel=rel)
+        score_compare(gs, rs, "slash", rel=rel)
         near_tie_check(ch["verts"][h], rv, cfg.n_vert, "vertical")
         near_tie_check(ch["slashes"][h], rs, cfg.n_slash, "slash")
 
@@ -373,17 +375,17 @@ def test_attention_sampled_rows_full_size(layer_run):
             lse_compare(ch["lse"][h].astype(np.float64), rl)
         st = ch["stats"]
         assert st[0] >= st[1] > 0
-    # for information: the oracle with bf16-rounded rotated operands (the
-    # kernel's own operand rounding), head 0 of the last chunk
+    # for information: the oracle with fp16-rounded rotated operands (the
+    # kernel's own QK^T operand rounding), head 0 of the last chunk
     ch = res["chunks"][last]
     bctx = oracle.KeyContext(key_context(name, 0).K, key_context(name, 0).V,
-                             oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local, operands="bf16")
+                             oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local, operands="fp16")
     sel = slice(0, None, 4)
     bo = oracle.sparse_rows(ch["q"][0][sel].astype(np.float64), ch["rows"][sel], bctx,
                             ch["verts"][0], ch["slashes"][0], res["sm"])[0]
     d = np.abs(ch["out"][0][sel] - bo)
     print(f"[info] {name}: worst vs fp64 max-abs {worst[0]:.2e} mean-abs {worst[1]:.2e}; "
-          f"head 0 vs bf16-operand oracle max-abs {d.max():.2e} mean-abs {d.mean():.2e}")
+          f"head 0 vs fp16-operand oracle max-abs {d.max():.2e} mean-abs {d.mean():.2e}")
 
 
 def test_attention_repeat_bitwise():
@@ -403,18 +405,21 @@ def test_dca_is_identity_within_training_length():
     name = "14b_256k"
     cfg = CONFIGS[name]
     res = run_layer(name)
+    # two GPU runs, each within the oracle bars of the exact result: their
+    # difference is held to twice those bars
     for c, tw in res["twin"].items():
         ch = res["chunks"][c]
         for h in range(cfg.n_heads):
             score_compare(tw["vs"][h].astype(np.float64), ch["vs"][h].astype(np.float64),
-                          "vertical (DCA on vs off)", quiet=True)
+                          "vertical (DCA on vs off)", quiet=True, rel=2 * SCORE_REL)
             score_compare(tw["ss"][h].astype(np.float64), ch["ss"][h].astype(np.float64),
-                          "slash (DCA on vs off)", quiet=True)
+                          "slash (DCA on vs off)", quiet=True, rel=2 * SCORE_REL)
         d = np.abs(tw["out"] - ch["out"])
         print(f"[dca-twin] chunk {c}: DCA on vs off max-abs {d.max():.2e} mean-abs "
               f"{d.mean():.2e}", flush=True)
-        compare(tw["out"].astype(np.float64), ch["out"].astype(np.float64))
-        lse_compare(tw["lse"].astype(np.float64), ch["lse"].astype(np.float64))
+        compare(tw["out"].astype(np.float64), ch["out"].astype(np.float64), 2 * MAX_ABS,
+                2 * MEAN_ABS)
+        lse_compare(tw["lse"].astype(np.float64), ch["lse"].astype(np.float64), 4e-2)
 
 
 def test_recall_and_refinement_full_size():

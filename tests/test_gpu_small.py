@@ -20,22 +20,26 @@ L = pytest.importorskip("long_context_sparse_rope_amd")
 
 
 # ---------------------------------------------------------------- RoPE / DCA
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("blend", [False, True])
-def test_rope_yarn_apply(dtype, blend):
+def test_rope_yarn_apply(dtype, blend, out_dtype):
     torch.manual_seed(0)
     H, n, D = 3, 300, 128
     x = torch.randn(H, n, D, device=DEV).to(dtype)
     pos = torch.randint(0, 1 << 20, (n,), dtype=torch.int32, device=DEV)
     pos[:4] = torch.tensor([0, 1, 262143, (1 << 30) - 1], dtype=torch.int32)
     rope = L.RopeConfig(base=1e7, yarn_factor=4.0, orig_max_pos=262144, freq_blend=blend)
-    y = L.rope_yarn_apply(x, pos, rope, scale=1.25)
+    y = L.rope_yarn_apply(x, pos, rope, scale=1.25, out_dtype=out_dtype)
+    assert y.dtype == out_dtype
     xs = oracle_inputs(x, x, x)[0]      # fp32 inputs are rounded to bf16 on entry
     th = (oracle.yarn_inv_freq(D, 1e7, 4.0, 262144) if blend else oracle.rope_inv_freq(D, 1e7))
     ref = oracle.rope_apply(xs, pos.cpu().numpy(), th, scale=1.25)
     got = host64(y)
-    # bf16 store: half an ulp (2^-9 relative) plus fp32 rotation error
-    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+    # the store: half an ulp (2^-9 relative for bf16, 2^-12 for fp16) plus
+    # the fp32 rotation error
+    half_ulp = 2.0 ** -9 if out_dtype == torch.bfloat16 else 2.0 ** -12
+    assert np.all(np.abs(got - ref) <= 2 * half_ulp * np.abs(ref) + 1e-5)
 
 
 def test_rope_no_rotate_and_inplace():
@@ -75,7 +79,7 @@ def test_topk_select_only_bit_exact(n, k):
     s[2, :] = 0.0                               # all-equal head
     vs, ss = torch.from_numpy(v).to(DEV), torch.from_numpy(s).to(DEV)
     q = torch.zeros(H, 1, 64, dtype=torch.bfloat16, device=DEV)
-    kc = torch.zeros(1, n, 64, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(1, n, 64, dtype=torch.float16, device=DEV)
     pat = L.Pattern(H, max(k, 1) + 5, max(k, 1) + 5, DEV)
     L.vs_pattern_estimate(q, kc, n - 1, L.RopeConfig(), L.DcaConfig(), 0.125, [k] * H, [k] * H,
                           pat, vert_score=vs, slash_score=ss, select_only=True)

@@ -173,14 +173,17 @@ def test_recall_properties():
     assert np.all(full >= sp)
 
 
+@pytest.mark.parametrize("mode,bits", [("bf16", 8), ("fp16", 11)])
 @pytest.mark.parametrize("chunk,local", [(0, 0), (12, 4)])
-def test_bf16_operands(chunk, local):
-    """operands="bf16": the cached keys are the bf16 roundings of the exact
-    rotated keys (representable, within half an ulp); continuous-position
-    keys rotate back to the pre-RoPE keys within that rounding; with the
-    rotation switched off and bf16 inputs the rounding is a no-op, so both
-    modes agree exactly (nothing else is rounded); with it on they differ by
-    no more than the operand rounding allows."""
+def test_rounded_operands(chunk, local, mode, bits):
+    """operands="bf16" / "fp16": the cached keys are the roundings of the
+    exact rotated keys (representable, within half an ulp of a `bits`-bit
+    significand); continuous-position keys rotate back to the pre-RoPE keys
+    within that rounding; with the rotation switched off and bf16 inputs the
+    rounding is a no-op, so both modes agree exactly (nothing else is
+    rounded); with it on they differ by no more than the operand rounding
+    allows."""
+    rnd = {"bf16": oracle.bf16_round64, "fp16": oracle.fp16_round64}[mode]
     rng = np.random.default_rng(21)
     n, d = 40, 8
     K = oracle.bf16_round(rng.normal(size=(n, d))).astype(np.float64)
@@ -188,25 +191,38 @@ def test_bf16_operands(chunk, local):
     Q = oracle.bf16_round(rng.normal(size=(n, d))).astype(np.float64)
     th = oracle.rope_inv_freq(d, 100.0)
     exact = oracle.KeyContext(K, V, th, chunk, local)
-    bf = oracle.KeyContext(K, V, th, chunk, local, operands="bf16")
-    kd, ke = bf.k_dca(), exact.k_dca()
-    assert np.array_equal(oracle.bf16_round64(kd), kd)
-    assert np.all(np.abs(kd - ke) <= np.ldexp(1.0, np.frexp(ke)[1] - 9))
-    back = oracle.rope_rotate(bf.k_cont(), -np.arange(n), th)
-    assert np.max(np.abs(back - K)) <= 2.0 ** -8 * np.max(np.abs(K)) * 2
+    rc = oracle.KeyContext(K, V, th, chunk, local, operands=mode)
+    kd, ke = rc.k_dca(), exact.k_dca()
+    assert np.array_equal(rnd(kd), kd)
+    assert np.all(np.abs(kd - ke) <= np.ldexp(1.0, np.frexp(ke)[1] - bits - 1))
+    back = oracle.rope_rotate(rc.k_cont(), -np.arange(n), th)
+    assert np.max(np.abs(back - K)) <= 2.0 ** -(bits - 1) * np.max(np.abs(K))
     if chunk == 0:
-        assert np.array_equal(bf.k_cont(), kd)
+        assert np.array_equal(rc.k_cont(), kd)
     rows = np.arange(n)
     oe, le = oracle.dense_causal_rows(Q, rows, exact, 0.4)
-    ob, lb = oracle.dense_causal_rows(Q, rows, bf, 0.4)
-    # logits move by at most 2 * 2^-8 * sm |q| |k| (both operands rounded)
-    bound = 2 * 2.0 ** -8 * 0.4 * np.linalg.norm(Q, axis=1) * np.max(np.linalg.norm(K, axis=1))
+    ob, lb = oracle.dense_causal_rows(Q, rows, rc, 0.4)
+    # logits move by at most 2 * 2^-bits * sm |q| |k| (both operands rounded)
+    bound = 2 * 2.0 ** -bits * 0.4 * np.linalg.norm(Q, axis=1) * np.max(np.linalg.norm(K, axis=1))
     assert np.max(np.abs(oe - ob)) > 0 and np.all(np.abs(le - lb) <= bound)
     zero = np.zeros(d // 2)
     a = oracle.KeyContext(K, V, zero, chunk, local)
-    b = oracle.KeyContext(K, V, zero, chunk, local, operands="bf16")
+    b = oracle.KeyContext(K, V, zero, chunk, local, operands=mode)
     oa, la = oracle.sparse_rows(Q, rows, a, [0, 3], [0, 1, 5], 0.4)[:2]
     ob2, lb2 = oracle.sparse_rows(Q, rows, b, [0, 3], [0, 1, 5], 0.4)[:2]
     assert np.array_equal(oa, ob2) and np.array_equal(la, lb2)
     with pytest.raises(ValueError):
-        oracle.KeyContext(K, V, th, operands="fp16")
+        oracle.KeyContext(K, V, th, operands="fp8")
+
+
+def test_fp16_round64_library():
+    """Direct fp64 -> fp16 rounding: torch's float32 -> float16 conversion on
+    float32-representable values, ties to even, and no double rounding just
+    off a tie."""
+    rng = np.random.default_rng(8)
+    x = (rng.normal(size=10000) * 10.0 ** rng.integers(-3, 4, 10000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.fp16_round64(x.astype(np.float64)), ref)
+    assert oracle.fp16_round64(np.array([1 + 2 ** -11]))[0] == 1.0            # tie -> even
+    assert oracle.fp16_round64(np.array([1 + 3 * 2 ** -11]))[0] == 1 + 2 ** -9  # tie -> even
+    assert oracle.fp16_round64(np.array([1 + 2 ** -11 + 2 ** -40]))[0] == 1 + 2 ** -10
