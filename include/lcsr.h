@@ -350,6 +350,19 @@ int lcsr_attn_decode(const lcsr_problem_t* p, void* out, int32_t out_dtype,
                      int64_t o_stride_h, int64_t o_stride_t, float* lse, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* lcsr_attn_decode_noalloc — lcsr_attn_decode without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid allocation).  Same arguments, results
+ * and errors as lcsr_attn_decode; the workspace is a static device array of
+ * the library (8 MiB per GPU, held until the process ends), which bounds
+ * every problem lcsr_attn_decode accepts (LCSR_ENOTSUP otherwise).  The call
+ * allocates nothing and launches the same kernels.  Calls on one GPU share
+ * that array: calls that may overlap on one GPU (different streams) race and
+ * must be serialised by the caller.  Asynchronous on `stream`. */
+int lcsr_attn_decode_noalloc(const lcsr_problem_t* p, void* out, int32_t out_dtype,
+                             int64_t o_stride_h, int64_t o_stride_t, float* lse,
+                             void* stream);
+
 /* lcsr_block_sparse_recall_check — attention recall of sampled rows for a
  * block-sparse pattern ([Qwen2.5-1M explainer] Chunked Prefill), C_i being
  * every key j <= i inside the kept blocks of i's query block (the set of

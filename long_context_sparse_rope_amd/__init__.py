@@ -9,7 +9,7 @@ fails loudly if it has not been built.
 from . import _capi
 from .ops import (LcsrError, RopeConfig, DcaConfig, Pattern, softmax_scale,
                   rope_yarn_apply, dca_positions, vs_pattern_estimate,
-                  vs_sparse_attn_prefill, attn_decode, attn_recall_check,
+                  vs_sparse_attn_prefill, attn_decode, attn_decode_noalloc, attn_recall_check,
                   workspace_bytes,
                   pattern_fill_a_shape, BlockPattern, block_sparse_estimate,
                   block_sparse_attn_prefill, block_sparse_recall_check)
@@ -19,7 +19,7 @@ _capi.load()
 
 __all__ = ["LcsrError", "RopeConfig", "DcaConfig", "Pattern", "softmax_scale",
            "rope_yarn_apply", "dca_positions", "vs_pattern_estimate",
-           "vs_sparse_attn_prefill", "attn_decode", "attn_recall_check",
+           "vs_sparse_attn_prefill", "attn_decode", "attn_decode_noalloc", "attn_recall_check",
            "workspace_bytes",
            "pattern_fill_a_shape", "BlockPattern", "block_sparse_estimate",
            "block_sparse_attn_prefill", "block_sparse_recall_check", "ChunkedSparsePrefill",

@@ -32,7 +32,8 @@ LCSR_WS_BLOCK_ATTN = 5
 EXPORTED = ("lcsr_workspace_bytes", "lcsr_last_error", "lcsr_softmax_scale",
             "lcsr_rope_yarn_apply",
             "lcsr_dca_positions", "lcsr_vs_pattern_estimate",
-            "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_recall_check",
+            "lcsr_vs_sparse_attn_prefill", "lcsr_attn_decode", "lcsr_attn_decode_noalloc",
+            "lcsr_attn_recall_check",
             "lcsr_pattern_fill_a_shape", "lcsr_block_sparse_estimate",
             "lcsr_block_sparse_attn_prefill", "lcsr_block_sparse_recall_check")
 
@@ -117,6 +118,8 @@ def load():
     lib.lcsr_attn_decode.restype = ctypes.c_int
     lib.lcsr_attn_decode.argtypes = [P(lcsr_problem_t), vp, i32, i64, i64, vp, vp,
                                      ctypes.c_size_t, vp]
+    lib.lcsr_attn_decode_noalloc.restype = ctypes.c_int
+    lib.lcsr_attn_decode_noalloc.argtypes = [P(lcsr_problem_t), vp, i32, i64, i64, vp, vp]
     lib.lcsr_attn_recall_check.restype = ctypes.c_int
     lib.lcsr_attn_recall_check.argtypes = [P(lcsr_problem_t), P(lcsr_pattern_t), vp, vp, i32,
                                            vp, vp, vp, vp, ctypes.c_size_t, vp]

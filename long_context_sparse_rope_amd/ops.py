@@ -388,6 +388,19 @@ def attn_decode(q, k_cache, v_cache, row_start, rope, dca, sm_scale, out=None,
     return out, lse
 
 
+def attn_decode_noalloc(q, k_cache, v_cache, row_start, rope, dca, sm_scale, out, lse=None,
+                        stream=None):
+    """attn_decode on the library's static scratch (lcsr_attn_decode_noalloc):
+    no workspace and no allocation, so `out` (and `lse`, if wanted) must be
+    given.  Calls that may overlap on one GPU must not use it concurrently."""
+    prob = _problem(q, k_cache, v_cache, row_start, rope, dca, sm_scale)
+    H, n, D = q.shape
+    _check(C.load().lcsr_attn_decode_noalloc(
+        ctypes.byref(prob), out.data_ptr(), _dtype_code(out), out.stride(0), out.stride(1),
+        _dense_rows(lse, H, n, "lse"), _stream(stream)))
+    return out, lse
+
+
 def attn_recall_check(q, k_cache, chunk_start, rope, dca, sm_scale, pattern, rows,
                       head_mask=None, workspace=None, stream=None):
     """(lse_full, lse_sparse, recall), each [H, n_rows] (lcsr_attn_recall_check)."""

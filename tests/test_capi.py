@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(C.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -193,6 +193,30 @@ def test_decode_workspace_and_rejects(lib):
     # the prefill keeps its 64-token chunk start with DCA
     q = problem(chunk_start=1048573, chunk_len=4, dca_chunk=262144, dca_local=32768)
     assert attn(lib, q, pattern()) == C.LCSR_ENOTSUP
+
+
+def test_decode_noalloc_rejects(lib):
+    """The no-alloc decode validates like lcsr_attn_decode before it looks up
+    its scratch or launches anything (no GPU is touched here)."""
+    def dec(pp, out=FAKE, out_dtype=C.LCSR_FP32, o_sh=4 * 128, o_st=128):
+        return lib.lcsr_attn_decode_noalloc(ctypes.byref(pp), out, out_dtype, o_sh, o_st, None,
+                                            None)
+
+    assert dec(problem(n_kv_heads=3, chunk_len=1)) == C.LCSR_EINVAL
+    assert "n_kv_heads" in err(lib)
+    # 7 heads per KV head x 5 rows > 32 matrix rows: the decode's own rule
+    assert dec(problem(chunk_start=1048573, chunk_len=5)) == C.LCSR_ENOTSUP
+    assert "<= 32" in err(lib)
+    p = problem(chunk_start=1048573, chunk_len=4, dca_chunk=262144, dca_local=32768)
+    assert dec(p, out=None) == C.LCSR_EINVAL
+    assert dec(p, out_dtype=9) == C.LCSR_EINVAL
+    assert dec(problem(head_dim=96, chunk_len=1)) == C.LCSR_ENOTSUP
+    # the largest problem the decode accepts fits the 8 MiB scratch: 64 KV
+    # heads of one query head, 32 rows each, head_dim 128, a 1M-token cache
+    big = problem(n_heads=64, n_kv_heads=64, chunk_start=1 << 20, chunk_len=32)
+    assert 0 < lib.lcsr_workspace_bytes(C.LCSR_WS_DECODE, ctypes.byref(big), 0, 0) <= 8 << 20
+    big = problem(n_heads=64, n_kv_heads=4, chunk_start=1 << 20, chunk_len=2)
+    assert 0 < lib.lcsr_workspace_bytes(C.LCSR_WS_DECODE, ctypes.byref(big), 0, 0) <= 8 << 20
 
 
 def test_fill_a_shape_rejects(lib):
