@@ -209,7 +209,7 @@ def decode_points(cfg, layer, q, row_counts, reps=20):
     n rows of the prompt against every key up to each, one lcsr_attn_decode
     call (the query rotations, the split-K kernel and the combine), median of
     `reps` calls timed with HIP events on the current stream.  The K and V
-    caches are read once per call: 2 x H_kv x N x D bf16 bytes."""
+    caches are read once per call: 2 x H_kv x N x D two-byte elements."""
     res = {}
     n_ctx = cfg.seq_len
     kv_bytes = 2 * cfg.n_kv_heads * n_ctx * cfg.head_dim * 2
@@ -359,13 +359,14 @@ def main():
     rec = {
         "metric": METRIC, "value": round(eff, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16/fp16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "seq_len": cfg.seq_len,
                    "prefill_chunk": cfg.prefill_chunk, "dca_chunk": cfg.dca_chunk,
                    "dca_local": cfg.dca_local, "yarn_factor": cfg.yarn_factor,
-                   "n_vert": cfg.n_vert, "n_slash": cfg.n_slash, "out_dtype": "bf16"},
+                   "n_vert": cfg.n_vert, "n_slash": cfg.n_slash, "out_dtype": "bf16",
+                   "qk_operands": "fp16", "pv_operands": "bf16", "qk_noise": cfg.qk_noise},
         "stage_ms": {k_: round(v_, 3) for k_, v_ in stages.items()},
         "attention_ms_per_chunk": att_chunks,
         "algorithmic_tflop_per_step": round(alg_flops / 1e12, 3),
@@ -376,8 +377,16 @@ def main():
     }
     if args.dense_ctx:
         print("[bench] dense one-chunk points", file=sys.stderr, flush=True)
-        rec["dense_chunk"] = dense_baseline(cfg, layer, q, k, v,
-                                            [int(x) for x in args.dense_ctx.split(",")])
+        dense = dense_baseline(cfg, layer, q, k, v, [int(x) for x in args.dense_ctx.split(",")])
+        # one-layer attention time, dense over sparse, of the chunk that ends
+        # at each context (context for the pages' Figure 11, which compares
+        # whole-model prefill, not one layer)
+        for c1_s, pt in dense.items():
+            ci = int(c1_s) // cfg.prefill_chunk - 1
+            if att_chunks and 0 <= ci < len(att_chunks) and att_chunks[ci] > 0:
+                pt["sparse_ms"] = att_chunks[ci]
+                pt["dense_over_sparse"] = round(pt["ms"] / att_chunks[ci], 2)
+        rec["dense_chunk"] = dense
     if not args.no_a_shape:
         print("[bench] a-shape chunk point", file=sys.stderr, flush=True)
         rec["a_shape_chunk"] = a_shape_point(cfg, layer, q)
