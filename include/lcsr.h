@@ -116,7 +116,10 @@ typedef struct lcsr_dca {
  * Grouped-query attention: query head h reads KV head h / (H / H_kv)
  * ([architecture overview] §4.6).  Supported: head_dim 64 or 128,
  * n_heads <= 64, n_heads % n_kv_heads == 0, n_heads / n_kv_heads <= 16.
- * With DCA on, S = C - W and chunk_start must be multiples of 64. */
+ * With DCA on, S = C - W >= 64 and chunk_start % 64 == 0 (any chunk_start
+ * for lcsr_attn_decode); lcsr_vs_sparse_attn_prefill takes S % 16 == 0 (its
+ * 16-key granules stay inside one DCA chunk) and the block-sparse calls
+ * S % 64 == 0 (their 64-key blocks do); the other calls take any S. */
 typedef struct lcsr_problem {
   const void* q;       /* [H, chunk_len, D] pre-RoPE queries of the chunk   */
   int32_t q_dtype;     /* LCSR_BF16 or LCSR_FP32 (fp32 is rounded to bf16)  */

@@ -129,8 +129,13 @@ namespace {
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // any_start: the rows may start anywhere (decode); otherwise, with DCA, the
-// chunk must start on a 64-token tile
-int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = false) {
+// chunk must start on a 64-token tile.  period_align: the DCA key period S =
+// chunk - local must be a multiple of it (16 for the vertical-slash
+// attention, whose 16-key granules must not straddle a DCA chunk edge; 64
+// for the block-sparse calls, whose 64-key blocks must not; 1 elsewhere).
+// Every call takes S >= 64, so a 64-key tile meets at most one edge.
+int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = false,
+                     int64_t period_align = 1) {
   if (!p) return fail(LCSR_EINVAL, "problem is NULL");
   // an empty chunk reads no query (its pointer may be NULL)
   if ((!p->q && p->chunk_len > 0) || !p->k_cache || (need_v && !p->v_cache))
@@ -162,9 +167,11 @@ int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = fals
     if (p->dca.local < 0 || p->dca.local >= p->dca.chunk)
       return fail(LCSR_EINVAL, "dca.local must be in [0, dca.chunk)");
     const int64_t period = p->dca.chunk - p->dca.local;
-    if (period % kTileK || (!any_start && p->chunk_start % kTileK))
-      return fail(LCSR_ENOTSUP, "with DCA, chunk - local (%lld) and chunk_start must be "
-                  "multiples of %d", (long long)period, kTileK);
+    if (period < kTileK || period % period_align)
+      return fail(LCSR_ENOTSUP, "with DCA, chunk - local (%lld) must be >= %d and a multiple "
+                  "of %lld for this call", (long long)period, kTileK, (long long)period_align);
+    if (!any_start && p->chunk_start % kTileK)
+      return fail(LCSR_ENOTSUP, "with DCA, chunk_start must be a multiple of %d", kTileK);
     if (p->dca.chunk > ((int64_t)1 << 30))
       return fail(LCSR_ENOTSUP, "dca.chunk beyond 2^30");
   }
@@ -223,7 +230,10 @@ float lcsr_softmax_scale(const lcsr_rope_t* rope, int32_t head_dim) {
 
 size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert,
                             int32_t max_slash) {
-  if (!p || validate_problem(p, false, which == LCSR_WS_DECODE) != LCSR_OK) return 0;
+  const int64_t align = which == LCSR_WS_ATTN ? kGranule
+                        : (which == LCSR_WS_BLOCK_EST || which == LCSR_WS_BLOCK_ATTN) ? kTileK
+                                                                                       : 1;
+  if (!p || validate_problem(p, false, which == LCSR_WS_DECODE, align) != LCSR_OK) return 0;
   switch (which) {
     case LCSR_WS_ESTIMATE: return estimate_layout(*p).total;
     case LCSR_WS_ATTN: return attn_layout(*p, max_vert, max_slash, true).total;
@@ -350,7 +360,7 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
                                 int64_t o_stride_h, int64_t o_stride_t, float* lse,
                                 int64_t* stats, uint32_t flags, void* ws,
                                 size_t ws_bytes, void* stream) {
-  int rc = validate_problem(p, true);
+  int rc = validate_problem(p, true, false, kGranule);
   if (rc) return rc;
   const bool dense = flags & LCSR_ATTN_DENSE;
   if (!dense) {
@@ -391,7 +401,7 @@ int lcsr_block_sparse_estimate(const lcsr_problem_t* p, const int32_t* n_blocks,
                                const int32_t* head_mask, int32_t max_blocks, int32_t* blk_idx,
                                int32_t* blk_cnt, float* scores, uint32_t flags, void* ws,
                                size_t ws_bytes, void* stream) {
-  int rc = validate_problem(p, false);
+  int rc = validate_problem(p, false, false, kTileK);
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
@@ -421,7 +431,7 @@ int lcsr_block_sparse_attn_prefill(const lcsr_problem_t* p, const int32_t* blk_i
                                    const int32_t* head_mask, void* out, int32_t out_dtype,
                                    int64_t o_stride_h, int64_t o_stride_t, float* lse,
                                    int64_t* stats, void* ws, size_t ws_bytes, void* stream) {
-  int rc = validate_problem(p, true);
+  int rc = validate_problem(p, true, false, kTileK);
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
@@ -495,7 +505,7 @@ int lcsr_block_sparse_recall_check(const lcsr_problem_t* p, const int32_t* blk_i
                                    const int32_t* head_mask, const int32_t* rows,
                                    int32_t n_rows, float* lse_full, float* lse_sparse,
                                    float* recall, void* stream) {
-  int rc = validate_problem(p, false);
+  int rc = validate_problem(p, false, false, kTileK);
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;

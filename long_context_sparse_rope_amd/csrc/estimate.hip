@@ -147,6 +147,25 @@ __device__ __forceinline__ void load_q_frags(const EstArgs& a, int h, int64_t c,
           base + (int64_t)(b * 32 + (lane & 31)) * D + s * 16 + 8 * (lane >> 5));
 }
 
+// Query fragment s of row block b for key chunk c, read from memory (the
+// layout of load_q_frags).
+template <int D>
+__device__ __forceinline__ f16x8 q_frag(const EstArgs& a, int h, int64_t c, int b, int s) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* base = a.q_est + (((int64_t)c * a.H + h) * kEstRows) * D;
+  return *reinterpret_cast<const f16x8*>(base + (int64_t)(b * 32 + (lane & 31)) * D + s * 16 +
+                                         8 * (lane >> 5));
+}
+
+// First key of the next DCA chunk if the 64-key tile at k0 meets a chunk
+// edge, else k0 + 64 (never, without DCA).
+__device__ __forceinline__ int64_t straddle_edge(const EstArgs& a, int64_t k0) {
+  if (!a.period) return k0 + kTileK;
+  const int64_t last = (k0 + kTileK - 1 < a.n_ctx - 1 ? k0 + kTileK - 1 : a.n_ctx - 1);
+  const int64_t c_last = last / a.period;
+  return c_last != k0 / a.period ? c_last * a.period : k0 + kTileK;
+}
+
 // K fragment s of key block kb: lane -> key row 32 kb + lane % 32, chunk
 // 2 s + lane / 32.
 template <int D>
@@ -197,6 +216,9 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
     }
     // the tile needs masking only at the causal edge or past n_ctx
     const bool edge = (k0 + kTileK - 1 > a.row0);
+    // first key of the next DCA chunk when the tile meets a chunk edge (at
+    // most one: the period is at least 64 keys), else past the tile
+    const int64_t kedge = straddle_edge(a, k0);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       f32x16 acc[2];
@@ -207,6 +229,24 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
         for (int s = 0; s < D / 16; ++s)
           acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k_frag<D>(ks, kb, s), qf[b][s],
                                                             acc[kb], 0, 0, 0);
+      }
+      if (kedge < k0 + kTileK) {
+        // keys past the edge score against the next chunk's query rows,
+        // read straight from memory (one tile per chunk edge)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x16 acc2 = {};
+#pragma unroll
+          for (int s = 0; s < D / 16; ++s)
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k_frag<D>(ks, kb, s),
+                                                          q_frag<D>(a, h, c + 1, b, s), acc2, 0,
+                                                          0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key >= kedge) acc[kb][r] = acc2[r];
+          }
+        }
       }
       const int64_t row = a.row0 + b * 32 + (lane & 31);
       // row max and sum over four interleaved partial chains (fixed order),
@@ -355,6 +395,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
       cur_c = c;
     }
     const bool edge = (k0 + kTileK - 1 > a.row0);
+    const int64_t kedge = straddle_edge(a, k0);
     // probabilities of the 32x32 block (row block b, key block kb)
     auto block_p = [&](int kb, int b, float (&pp)[16]) {
       f32x16 acc = {};
@@ -363,6 +404,16 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[b][s], k_frag<D>(ks, kb, s), acc, 0,
                                                       0, 0);
       const int64_t key = k0 + kb * 32 + (lane & 31);
+      if (kedge < k0 + kTileK) {
+        // keys past a DCA chunk edge: the next chunk's query rows (this
+        // lane's key column takes that product)
+        f32x16 acc2 = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(q_frag<D>(a, h, c + 1, b, s),
+                                                        k_frag<D>(ks, kb, s), acc2, 0, 0, 0);
+        if (key >= kedge) acc = acc2;
+      }
       float lr[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j)

@@ -4,8 +4,9 @@ Shapes, budgets and RoPE/DCA/YaRN settings of the synthetic layers the path
 is measured and checked on.  Values the workload description leaves open are
 fixed here:
 
-* tiny: DCA local window W = 64 (so the key period S = C - W = 192 is a
-  multiple of the 64-key tile), one prefill chunk of 1024;
+* tiny: DCA local window W = 32 (key period S = C - W = 224, not a multiple
+  of the 64-key tile: tiles meet chunk edges at 224 and 672), one prefill
+  chunk of 1024;
 * 7B-shaped 128K and 14B-shaped 256K: no YaRN (s = 1) and DCA off (both are
   within the 262,144-token training length, where DCA is the identity);
 * 1M and refinement-stress: DCA chunk C = 262,144, local window W = 32,768,
@@ -67,7 +68,7 @@ class LayerConfig:
 TINY = LayerConfig(
     name="tiny", cid=1, n_heads=1, n_kv_heads=1, head_dim=64, seq_len=1024,
     prefill_chunk=1024, in_dtype="fp32", rope_base=1e4, dca_chunk=256,
-    dca_local=64, n_vert=32, n_slash=64, planting="none")
+    dca_local=32, n_vert=32, n_slash=64, planting="none")
 
 SEVEN_B_128K = LayerConfig(
     name="7b_128k", cid=2, n_heads=28, n_kv_heads=4, head_dim=128,

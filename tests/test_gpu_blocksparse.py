@@ -224,8 +224,10 @@ def test_every_block_is_dense():
 
 def test_tiny_ragged_chunk_bf16_out():
     """fp32 inputs (taken at bf16), D 64, DCA C 256 W 64, a 1000-row chunk
-    after 0 (last query block of 40 rows) and bf16 output."""
-    cfg = TINY
+    after 0 (last query block of 40 rows) and bf16 output.  The block-sparse
+    calls take DCA periods in whole 64-key blocks: the tiny layer runs here
+    with W 64 (S 192)."""
+    cfg = scaled(TINY, dca_local=64)
     q, k, v = synth.generate(cfg, DEV)
     layer = _layer(cfg)
     build_cache(layer, k, v, cfg.seq_len)

@@ -58,20 +58,33 @@ def _decode_case(cfg, q, k, v, layer, p0, n, out_dtype=torch.float32):
 @pytest.fixture(scope="module")
 def tiny():
     cfg = TINY
-    assert cfg.dca_chunk - cfg.dca_local == 192
+    assert cfg.dca_chunk - cfg.dca_local == 224
     q, k, v = synth.generate(cfg, DEV)
     return cfg, q, k, v, _layer(cfg, k, v)
 
 
-# TINY: one head, D 64, DCA C 256, W 64 (period S 192), 1024 tokens.  The
-# rows (190, 4) and (382, 3) straddle the period edges 192 and 384: their
-# earlier rows meet key tiles of the next DCA chunk, all masked for them.
-@pytest.mark.parametrize("p0,n", [(1023, 1), (0, 1), (1, 3), (1000, 24), (190, 4),
-                                  (382, 3), (222, 4), (255, 2), (447, 3), (480, 32), (63, 2),
-                                  (700, 17)])
+# TINY: one head, D 64, DCA C 256, W 32 (period S 224), 1024 tokens.  The
+# rows (222, 4), (447, 3), (670, 4) and (894, 3) straddle the period edges 224,
+# 448, 672 and 896: their earlier rows meet keys of the next DCA chunk, all
+# masked for them.  The 64-key tiles 192..255 and 640..703 hold an edge:
+# their keys on either side take their own chunk's query variant.
+@pytest.mark.parametrize("p0,n", [(1023, 1), (0, 1), (1, 3), (1000, 24), (222, 4),
+                                  (447, 3), (670, 4), (894, 3), (255, 2), (190, 4),
+                                  (480, 32), (63, 2), (700, 17)])
 def test_decode_tiny(tiny, p0, n):
     cfg, q, k, v, layer = tiny
     _decode_case(cfg, q, k, v, layer, p0, n)
+
+
+def test_decode_period_208():
+    """DCA period S 208 (C 256, W 48), a multiple of 16 only: the 64-key tiles
+    192..255 and 384..447 hold the chunk edges 208 and 416; rows on both sides
+    of each edge."""
+    cfg = scaled(TINY, dca_local=48)
+    q, k, v = synth.generate(cfg, DEV)
+    layer = _layer(cfg, k, v)
+    for p0, n in ((206, 4), (414, 3), (255, 2), (1023, 1), (600, 16)):
+        _decode_case(cfg, q, k, v, layer, p0, n)
 
 
 def test_decode_tiny_bf16_out_and_reproducible(tiny):

@@ -216,6 +216,43 @@ def test_attention_tiny_dense(c0, lc):
     _attn_case(TINY, c0, lc, None, None, dense=True)
 
 
+# A DCA period that is a multiple of 16 but not of 32 (C 256, W 48: S 208):
+# the 32-row blocks [192, 224), [416, 448), ... hold a chunk edge, so the rows
+# of one block take different query variants, and key tiles are cut at the
+# edges.
+TINY_S208 = scaled(TINY, dca_local=48)
+
+
+@pytest.mark.parametrize("c0,lc", [(0, 1024), (128, 448)])
+def test_attention_period_208(c0, lc):
+    rng = np.random.default_rng(208 + c0)
+    c1 = c0 + lc
+    verts = [sorted(rng.choice(c1, size=40, replace=False).tolist())]
+    slashes = [sorted(set([0, 1, 2, 200, 207, 208, 209] +
+                          rng.choice(c1, size=60, replace=False).tolist()))]
+    _attn_case(TINY_S208, c0, lc, verts, slashes)
+    _attn_case(TINY_S208, c0, lc, None, None, dense=True)
+
+
+def test_estimate_period_208():
+    """Estimate scores at S 208: 64-key tiles meet the chunk edges 208, 416,
+    624 and 832, and each key takes its own chunk's rotation."""
+    cfg = TINY_S208
+    q, k, v = synth.generate(cfg, DEV)
+    layer = _tiny_layer(cfg, q, k, v, 1024)
+    vs = torch.empty(1, 1024, device=DEV)
+    ss = torch.empty(1, 1024, device=DEV)
+    L.vs_pattern_estimate(q[:, 0:1024], layer.k_cache[:, :1024], 0, layer.rope, layer.dca,
+                          layer.sm_scale, [32], [64], layer.pattern, vert_score=vs,
+                          slash_score=ss)
+    qo, ko, _ = oracle_inputs(q, k, v)
+    ctx = oracle.KeyContext(ko[0], None, oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local)
+    rows = oracle.estimate.estimate_rows(0, 1024, 64)
+    rv, rs = oracle.estimate_scores(qo[0, rows], rows, ctx, 1024, layer.sm_scale)
+    score_compare(host64(vs[0]), rv, "vertical")
+    score_compare(host64(ss[0]), rs, "slash")
+
+
 def test_attention_empty_rows_and_bf16_out():
     # no slash 0 and verticals only far ahead: the first rows have empty sets
     _attn_case(TINY, 0, 256, [[200, 201]], [[150, 151]], out_dtype=torch.bfloat16)
@@ -240,7 +277,7 @@ def test_recall_tiny():
     q, k, v = synth.generate(cfg, DEV)
     layer = _tiny_layer(cfg, q, k, v, 1024)
     layer.estimate(q, 0)
-    rows = torch.tensor([0, 5, 100, 191, 192, 500, 959, 1023], dtype=torch.int32, device=DEV)
+    rows = torch.tensor([0, 5, 100, 223, 224, 500, 959, 1023], dtype=torch.int32, device=DEV)
     lf, ls, rc = layer.recall(q, 0, rows)
     verts, slashes = layer.pattern.lists()
     qo, ko, vo = oracle_inputs(q, k, v)
