@@ -117,8 +117,8 @@ typedef struct lcsr_dca {
  * ([architecture overview] §4.6).  Supported: head_dim 64 or 128,
  * n_heads <= 64, n_heads % n_kv_heads == 0, n_heads / n_kv_heads <= 16.
  * With DCA on, S = C - W >= 64 and chunk_start % 64 == 0 (any chunk_start
- * for lcsr_attn_decode); lcsr_vs_sparse_attn_prefill takes S % 16 == 0 (its
- * 16-key granules stay inside one DCA chunk) and the block-sparse calls
+ * for lcsr_attn_decode); lcsr_vs_sparse_attn_prefill takes S % 32 == 0 (its
+ * 32-query-row blocks stay inside one DCA chunk) and the block-sparse calls
  * S % 64 == 0 (their 64-key blocks do); the other calls take any S. */
 typedef struct lcsr_problem {
   const void* q;       /* [H, chunk_len, D] pre-RoPE queries of the chunk   */

@@ -50,7 +50,9 @@ EstimateLayout estimate_layout(const lcsr_problem_t& p) {
   // block) diagonal group e, with two slots
   L.n_diag = 2 * L.n_tiles + 2;
   L.q_est = align256((size_t)L.n_kc * H * kEstRows * D * 2);
-  L.part = align256((size_t)H * L.n_split * kEstRows * 2 * sizeof(float));
+  // one partial per key split, plus one for the keys past DCA chunk edges
+  // inside 64-key tiles (scored apart, with the next chunk's query rows)
+  L.part = align256((size_t)H * (L.n_split + 1) * kEstRows * 2 * sizeof(float));
   L.lse = align256((size_t)H * kEstRows * sizeof(float));
   L.vscore = align256((size_t)H * L.n_ctx * sizeof(float));
   L.sscore = L.vscore;
@@ -130,10 +132,11 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // any_start: the rows may start anywhere (decode); otherwise, with DCA, the
 // chunk must start on a 64-token tile.  period_align: the DCA key period S =
-// chunk - local must be a multiple of it (16 for the vertical-slash
-// attention, whose 16-key granules must not straddle a DCA chunk edge; 64
-// for the block-sparse calls, whose 64-key blocks must not; 1 elsewhere).
-// Every call takes S >= 64, so a 64-key tile meets at most one edge.
+// chunk - local must be a multiple of it (32 for the vertical-slash
+// attention, whose 32-row blocks share one query variant and whose 16-key
+// granules must not straddle a DCA chunk edge; 64 for the block-sparse
+// calls, whose 64-key blocks must not; 1 elsewhere).  Every call takes
+// S >= 64, so a 64-key tile meets at most one edge.
 int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = false,
                      int64_t period_align = 1) {
   if (!p) return fail(LCSR_EINVAL, "problem is NULL");
@@ -230,7 +233,7 @@ float lcsr_softmax_scale(const lcsr_rope_t* rope, int32_t head_dim) {
 
 size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert,
                             int32_t max_slash) {
-  const int64_t align = which == LCSR_WS_ATTN ? kGranule
+  const int64_t align = which == LCSR_WS_ATTN ? kRowBlock
                         : (which == LCSR_WS_BLOCK_EST || which == LCSR_WS_BLOCK_ATTN) ? kTileK
                                                                                        : 1;
   if (!p || validate_problem(p, false, which == LCSR_WS_DECODE, align) != LCSR_OK) return 0;
@@ -360,7 +363,7 @@ int lcsr_vs_sparse_attn_prefill(const lcsr_problem_t* p, const lcsr_pattern_t* p
                                 int64_t o_stride_h, int64_t o_stride_t, float* lse,
                                 int64_t* stats, uint32_t flags, void* ws,
                                 size_t ws_bytes, void* stream) {
-  int rc = validate_problem(p, true, false, kGranule);
+  int rc = validate_problem(p, true, false, kRowBlock);
   if (rc) return rc;
   const bool dense = flags & LCSR_ATTN_DENSE;
   if (!dense) {

@@ -783,11 +783,7 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     const int h = h_first + w;
     const bool live = w < n_here && ((a.head_mask >> h) & 1);
     const int32_t my_row = i0 + (lane & 31);
-    // DCA chunk of this lane's row: a row block may straddle a chunk edge
-    // when the period is not a multiple of 32, so the query variant is taken
-    // per lane (rows past the block's last row take the last row's chunk)
-    const int32_t qchunk = period ? (my_row <= rlast ? my_row : rlast) / period : 0;
-    const int32_t qc_first = period ? i0 / period : 0, qc_last = period ? rlast / period : 0;
+    const int32_t qchunk = period ? i0 / period : 0;
     LaneConst<D> lc;
     lane_consts<D>(lc, lane);
     WaveState<D> st;
@@ -806,16 +802,12 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     };
     ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
     Tile t0 = read_desc(&ring[0]);
-    // DCA relation of a row chunk and a tile: intra (0), successive (1) or
-    // inter (2); a row before the tile's chunk has no causal key in it and
-    // takes 0, so its query load stays inside the variants
-    auto var_rel = [&](int32_t qc, const Tile& tt) {
-      const int32_t rel = qc - tt.kchunk;
-      return a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : rel));
+    // DCA relation of a tile (the same for every wave and row: the period is
+    // a multiple of 32, so a 32-row block lies inside one DCA chunk)
+    auto var_of = [&](const Tile& tt) {
+      const int32_t rel = qchunk - tt.kchunk;
+      return a.n_var == 1 ? 0 : (rel >= 2 ? 2 : rel);
     };
-    // a run of tiles needs one query load: the variants of the block's first
-    // and last rows (the only two row chunks it can hold) stay the same
-    auto run_key = [&](const Tile& tt) { return 3 * var_rel(qc_first, tt) + var_rel(qc_last, tt); };
     Win W0{}, C0{}, W1{}, C1{};
     load_windows(t0, W0, C0);
     int i = 0;
@@ -882,14 +874,14 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     // the inner loop
     auto run = [&](auto lag) {
       while (t0.n > 0) {
-        const int key = run_key(t0);
+        const int var = var_of(t0);
         if (live) {
-          load_q<D>(a, h, i0, var_rel(qchunk, t0), st);
+          load_q<D>(a, h, i0, var, st);
           wait_vm<0>();
         }
         do {
           step(lag);
-        } while (t0.n > 0 && run_key(t0) == key);
+        } while (t0.n > 0 && var_of(t0) == var);
       }
       // a late wave's last PV product (the last stage is not refilled)
       if constexpr (decltype(lag)::value) wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1);
@@ -1310,44 +1302,61 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
   st.m = -INFINITY;
   st.l = 0.f;
   int cur_var = -1;
-  for (int i = 0; i < n_local; ++i) {
-    step_barrier();  // tile i in its stage; the stage of tile i - 1 is released
-    const Tile tt = tile_of(t_begin + i);
-    // keys <= this row's token; the other rows see the whole tile
-    const int64_t lim = live ? pos - tt.ks + 1 : kTileK;
-    const uint64_t causal = low_bits(lim < tt.n ? lim : tt.n);
-    // one pass per DCA key chunk in the tile: a tile meets at most one chunk
-    // edge (the period is at least 64 keys), and the keys on either side
-    // take the query variant of their own chunk
-    const int32_t kc_last = a.period ? (int32_t)((tt.ks + tt.n - 1) / a.period) : 0;
-    for (int32_t kc = tt.kchunk; kc <= kc_last; ++kc) {
-      uint64_t seg = ~0ull;
-      if (kc_last != tt.kchunk) {
-        const int64_t edge = (int64_t)kc_last * a.period - tt.ks;  // first key of the later chunk
-        seg = kc == tt.kchunk ? low_bits(edge) : ~low_bits(edge);
+  // One iteration per (tile, key chunk) pass: a tile meets at most one DCA
+  // chunk edge (the period is at least 64 keys), and the keys on either side
+  // take the query variant of their own chunk.  The products run on every
+  // iteration (a product that a branch may skip would merge two copies of
+  // the accumulators); the barrier comes with each new tile.
+  // the key chunk of the current tile and the first key of the next chunk,
+  // kept up to date as the tiles ascend (the period is at least one tile)
+  int32_t kc0 = a.period ? (int32_t)(t_begin * kTileK / a.period) : 0;
+  int64_t next_edge = a.period ? (int64_t)(kc0 + 1) * a.period : INT64_MAX;
+  int64_t ks = 0;
+  int32_t tn = 0;
+  uint64_t causal = 0;
+  int64_t edge = kTileK;  // first key of the later chunk in the tile
+  int seg = 0;
+  for (int i = 0; i < n_local;) {
+    if (seg == 0) {
+      step_barrier();  // tile i in its stage; the stage of tile i - 1 is released
+      ks = (t_begin + i) * kTileK;
+      tn = (int32_t)(a.n_ctx - ks < kTileK ? a.n_ctx - ks : kTileK);
+      if (ks >= next_edge) {
+        ++kc0;
+        next_edge += a.period;
       }
-      // the query variant of this lane's row against the key chunk.  Rows of
-      // one call may straddle a chunk edge: an earlier row then meets keys of
-      // the next chunk (rel < 0), which all lie after it and are masked; it
-      // takes variant 0 there, so the query load stays inside the variants
-      const int64_t rel = qchunk - kc;
-      const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
-      if (__ballot(var != cur_var) != 0ull) {
-        const uint16_t* qb = a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
+      // keys <= this row's token; the other rows see the whole tile
+      const int64_t lim = live ? pos - ks + 1 : kTileK;
+      causal = low_bits(lim < tn ? lim : tn);
+      edge = next_edge - ks < tn ? next_edge - ks : kTileK;
+    }
+    const int32_t kc = kc0 + seg;
+    // the query variant of this lane's row against the key chunk.  Rows of
+    // one call may straddle a chunk edge: an earlier row then meets keys of
+    // the next chunk (rel < 0), which all lie after it and are masked; it
+    // takes variant 0 there, so the query load stays inside the variants
+    const int64_t rel = qchunk - kc;
+    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
+    if (__ballot(var != cur_var) != 0ull) {
+      const uint16_t* qb = a.q_rot + (((int64_t)var * a.H + h) * a.n_q + r) * D + 8 * half;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const f16x8*>(qb + s * 16);
-        wait_vm<0>();
-        cur_var = var;
-      }
-      const uint64_t mword = causal & seg;
-      const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
-      const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
-      const bool masked = __ballot(mword == ~0ull) != ~0ull;
-      const char* bc = stage[i % kDecStages];
-      bf16x8 pf[4];
-      wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
-                     [] {});
-      wave_pv<D>(bc, lc, st, pf, act0, act1);
+      for (int s = 0; s < D / 16; ++s) st.q[s] = *reinterpret_cast<const f16x8*>(qb + s * 16);
+      wait_vm<0>();
+      cur_var = var;
+    }
+    const uint64_t mword = causal & (seg ? ~low_bits(edge) : low_bits(edge));
+    const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+    const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+    const bool masked = __ballot(mword == ~0ull) != ~0ull;
+    const char* bc = stage[i % kDecStages];
+    bf16x8 pf[4];
+    wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
+    wave_pv<D>(bc, lc, st, pf, act0, act1);
+    if (seg == 0 && edge < kTileK) {
+      seg = 1;
+    } else {
+      seg = 0;
+      ++i;
     }
   }
   // the split's partial for every live pair: O unnormalised, m in log2 units

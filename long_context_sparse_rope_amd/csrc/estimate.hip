@@ -15,6 +15,11 @@
 // diagonal sums of every 32x32 block (through a wave-private LDS scratch),
 // all in a fixed order: the scores are bitwise reproducible.
 // Reduce: slash score per offset from the <= 2 diagonal records covering it.
+// DCA key periods need not be multiples of the 64-key tile: in a tile that
+// meets a chunk edge the passes count only the keys before it, and the edge
+// kernels score the keys after it with the next chunk's query rows (a
+// partial of its own in pass 1; vertical scores and diagonal sums added
+// after pass 2).
 #include <cmath>
 
 #include "lcsr_internal.h"
@@ -34,8 +39,9 @@ struct EstArgs {
   int64_t period;         // S, 0 = DCA off
   int64_t n_tiles, tiles_per_split;
   int32_t n_split;
+  int32_t n_part;         // partials per head: n_split, + 1 when a tile meets a DCA edge
   float scale_log2;       // sm_scale * log2(e)
-  float* part;            // [H][n_split][64][2]
+  float* part;            // [H][n_part][64][2]
   float* lse2;            // [H][64]
   float* vscore;          // [H][n_ctx]
   float* sscore;          // [H][n_ctx]
@@ -147,23 +153,12 @@ __device__ __forceinline__ void load_q_frags(const EstArgs& a, int h, int64_t c,
           base + (int64_t)(b * 32 + (lane & 31)) * D + s * 16 + 8 * (lane >> 5));
 }
 
-// Query fragment s of row block b for key chunk c, read from memory (the
-// layout of load_q_frags).
-template <int D>
-__device__ __forceinline__ f16x8 q_frag(const EstArgs& a, int h, int64_t c, int b, int s) {
-  const int lane = threadIdx.x & 63;
-  const uint16_t* base = a.q_est + (((int64_t)c * a.H + h) * kEstRows) * D;
-  return *reinterpret_cast<const f16x8*>(base + (int64_t)(b * 32 + (lane & 31)) * D + s * 16 +
-                                         8 * (lane >> 5));
-}
-
-// First key of the next DCA chunk if the 64-key tile at k0 meets a chunk
-// edge, else k0 + 64 (never, without DCA).
-__device__ __forceinline__ int64_t straddle_edge(const EstArgs& a, int64_t k0) {
-  if (!a.period) return k0 + kTileK;
-  const int64_t last = (k0 + kTileK - 1 < a.n_ctx - 1 ? k0 + kTileK - 1 : a.n_ctx - 1);
-  const int64_t c_last = last / a.period;
-  return c_last != k0 / a.period ? c_last * a.period : k0 + kTileK;
+// First key of the next DCA chunk if the 64-key tile at k0 (in chunk c)
+// meets a chunk edge, else k0 + 64 (never, without DCA).  A tile meets at
+// most one edge: the period is at least 64 keys.
+__device__ __forceinline__ int64_t straddle_edge(const EstArgs& a, int64_t k0, int64_t c) {
+  const int64_t next = (c + 1) * a.period;
+  return (a.period && next < k0 + kTileK && next < a.n_ctx) ? next : k0 + kTileK;
 }
 
 // K fragment s of key block kb: lane -> key row 32 kb + lane % 32, chunk
@@ -214,11 +209,10 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
       load_q_frags<D>(a, h, c, qf);
       cur_c = c;
     }
-    // the tile needs masking only at the causal edge or past n_ctx
-    const bool edge = (k0 + kTileK - 1 > a.row0);
-    // first key of the next DCA chunk when the tile meets a chunk edge (at
-    // most one: the period is at least 64 keys), else past the tile
-    const int64_t kedge = straddle_edge(a, k0);
+    // the tile needs masking only at the causal edge, past n_ctx or past a
+    // DCA chunk edge inside it (those keys are the edge kernel's)
+    const int64_t kedge = straddle_edge(a, k0, c);
+    const bool edge = (k0 + kTileK - 1 > a.row0) || kedge < k0 + kTileK;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       f32x16 acc[2];
@@ -229,24 +223,6 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
         for (int s = 0; s < D / 16; ++s)
           acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k_frag<D>(ks, kb, s), qf[b][s],
                                                             acc[kb], 0, 0, 0);
-      }
-      if (kedge < k0 + kTileK) {
-        // keys past the edge score against the next chunk's query rows,
-        // read straight from memory (one tile per chunk edge)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          f32x16 acc2 = {};
-#pragma unroll
-          for (int s = 0; s < D / 16; ++s)
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k_frag<D>(ks, kb, s),
-                                                          q_frag<D>(a, h, c + 1, b, s), acc2, 0,
-                                                          0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= kedge) acc[kb][r] = acc2[r];
-          }
-        }
       }
       const int64_t row = a.row0 + b * 32 + (lane & 31);
       // row max and sum over four interleaved partial chains (fixed order),
@@ -260,7 +236,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
           float v = acc[kb][r] * a.scale_log2;
           if (edge) {
             const int64_t key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > row || key >= a.n_ctx) v = -INFINITY;
+            if (key > row || key >= a.n_ctx || key >= kedge) v = -INFINITY;
           }
           x[kb][r] = v;
           mp[r & 3] = fmaxf(mp[r & 3], v);
@@ -295,7 +271,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
       ll = la * exp2f(ma - mm) + lb * exp2f(mb - mm);
     }
     if (half == 0) {
-      float* dst = a.part + (((int64_t)h * a.n_split + split) * kEstRows + b * 32 + lane) * 2;
+      float* dst = a.part + (((int64_t)h * a.n_part + split) * kEstRows + b * 32 + lane) * 2;
       dst[0] = mm;
       dst[1] = ll;
     }
@@ -308,12 +284,12 @@ __global__ void __launch_bounds__(256) est_combine(EstArgs a) {
   const int h = blockIdx.x, r = threadIdx.x & 63, part = threadIdx.x >> 6;
   if (!((a.head_mask >> h) & 1)) return;
   __shared__ float pm[4][kEstRows], pl[4][kEstRows];
-  const float* p = a.part + ((int64_t)h * a.n_split * kEstRows + r) * 2;
+  const float* p = a.part + ((int64_t)h * a.n_part * kEstRows + r) * 2;
   float mm = -INFINITY;
-  for (int z = part; z < a.n_split; z += 4) mm = fmaxf(mm, p[(int64_t)z * kEstRows * 2]);
+  for (int z = part; z < a.n_part; z += 4) mm = fmaxf(mm, p[(int64_t)z * kEstRows * 2]);
   float ll = 0.f;
   if (mm != -INFINITY)
-    for (int z = part; z < a.n_split; z += 4)
+    for (int z = part; z < a.n_part; z += 4)
       ll += p[(int64_t)z * kEstRows * 2 + 1] * exp2f(p[(int64_t)z * kEstRows * 2] - mm);
   pm[part][r] = mm;
   pl[part][r] = ll;
@@ -394,8 +370,8 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
       load_q_frags<D>(a, h, c, qf);
       cur_c = c;
     }
-    const bool edge = (k0 + kTileK - 1 > a.row0);
-    const int64_t kedge = straddle_edge(a, k0);
+    const int64_t kedge = straddle_edge(a, k0, c);
+    const bool edge = (k0 + kTileK - 1 > a.row0) || kedge < k0 + kTileK;
     // probabilities of the 32x32 block (row block b, key block kb)
     auto block_p = [&](int kb, int b, float (&pp)[16]) {
       f32x16 acc = {};
@@ -404,16 +380,6 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[b][s], k_frag<D>(ks, kb, s), acc, 0,
                                                       0, 0);
       const int64_t key = k0 + kb * 32 + (lane & 31);
-      if (kedge < k0 + kTileK) {
-        // keys past a DCA chunk edge: the next chunk's query rows (this
-        // lane's key column takes that product)
-        f32x16 acc2 = {};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(q_frag<D>(a, h, c + 1, b, s),
-                                                        k_frag<D>(ks, kb, s), acc2, 0, 0, 0);
-        if (key >= kedge) acc = acc2;
-      }
       float lr[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -426,7 +392,7 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
         float v = __builtin_amdgcn_exp2f(acc[r] * a.scale_log2 - lr[r]);
         if (edge) {
           const int64_t row = a.row0 + b * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > row || key >= a.n_ctx) v = 0.f;
+          if (key > row || key >= a.n_ctx || key >= kedge) v = 0.f;
         }
         pp[r] = v;
       }
@@ -472,6 +438,120 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
     diag_record(pb, drec + ((2 * t + 2) * 2 + 0) * 64);
     }
     est_barrier();  // tile i done, tile i + 1 in its stage
+  }
+}
+
+// ------------------------------------------------------------ DCA edges
+// Keys after a DCA chunk edge inside a 64-key tile (edge e = c S not a
+// multiple of 64; keys e .. the tile's end), which the passes leave out:
+// they meet the query rows rotated for chunk c.  Scores on the vector units,
+// fp32 sums of the fp16 products (the operands of the matrix-core passes).
+
+// Whether chunk c's first key e = c S lies inside a 64-key tile (and inside
+// the context); e_end: one past the tile's last key.
+__device__ __forceinline__ bool edge_tile(const EstArgs& a, int64_t c, int64_t& e,
+                                          int64_t& e_end) {
+  e = c * a.period;
+  if (e >= a.n_ctx || (e % kTileK) == 0) return false;
+  const int64_t k_end = (e / kTileK + 1) * kTileK;
+  e_end = k_end < a.n_ctx ? k_end : a.n_ctx;
+  return true;
+}
+
+// sm_scale <q_est[c][h][r], K[j]> in log2 units
+template <int D>
+__device__ __forceinline__ float edge_logit(const EstArgs& a, int h, int g, int64_t c, int r,
+                                            int64_t j) {
+  const uint16_t* q = a.q_est + (((int64_t)c * a.H + h) * kEstRows + r) * D;
+  const uint16_t* k = a.k + (int64_t)g * a.kv_sh + j * a.kv_st;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int d = 0; d < D; ++d) acc = fmaf(f16_to_f32(q[d]), f16_to_f32(k[d]), acc);
+  return acc * a.scale_log2;
+}
+
+// Pass 1 for the edge keys: one thread per estimate row, the edges in
+// ascending order, an online max / sum into the head's last partial.
+template <int D>
+__global__ void __launch_bounds__(kEstRows) est_edge1(EstArgs a) {
+  const int h = blockIdx.x, r = threadIdx.x;
+  if (!((a.head_mask >> h) & 1)) return;
+  const int g = h / a.G;
+  const int64_t row = a.row0 + r;
+  const int64_t n_kc = (a.n_ctx + a.period - 1) / a.period;
+  float m = -INFINITY, l = 0.f;
+  for (int64_t c = 1; c < n_kc; ++c) {
+    int64_t e, e_end;
+    if (!edge_tile(a, c, e, e_end)) continue;
+    for (int64_t j = e; j < e_end && j <= row; ++j) {
+      const float v = edge_logit<D>(a, h, g, c, r, j);
+      if (v > m) {
+        l = l * exp2f(m - v) + 1.f;
+        m = v;
+      } else {
+        l += exp2f(v - m);
+      }
+    }
+  }
+  float* dst = a.part + (((int64_t)h * a.n_part + a.n_split) * kEstRows + r) * 2;
+  dst[0] = m;
+  dst[1] = l;
+}
+
+// Pass 2 for the edge keys, after est_pass2: the probabilities of the tile's
+// 64 rows x 64 keys (zero outside the edge keys) in LDS, then the vertical
+// scores of the edge keys (rows in ascending order) and the diagonal sums of
+// the tile's four 32 x 32 blocks, added to the records pass 2 wrote (same
+// record layout: blocks (0,0) + (1,1) in record 2t + 1 slot 0, block (row 1,
+// key 0) in record 2t slot 1, block (row 0, key 1) in record 2t + 2 slot 0).
+template <int D>
+__global__ void __launch_bounds__(256) est_edge2(EstArgs a) {
+  __shared__ float P[kEstRows][kTileK + 1];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (!((a.head_mask >> h) & 1)) return;
+  const int g = h / a.G;
+  const int64_t n_kc = (a.n_ctx + a.period - 1) / a.period;
+  float* drec = a.diag + (int64_t)h * a.n_diag * 2 * 64;
+  for (int64_t c = 1; c < n_kc; ++c) {
+    int64_t e, e_end;
+    if (!edge_tile(a, c, e, e_end)) continue;
+    const int64_t k0 = e / kTileK * kTileK, t = k0 / kTileK;
+    for (int x = tid; x < kEstRows * kTileK; x += 256) {
+      const int r = x / kTileK, n = x % kTileK;
+      const int64_t j = k0 + n, row = a.row0 + r;
+      float p = 0.f;
+      if (j >= e && j < e_end && j <= row)
+        p = exp2f(edge_logit<D>(a, h, g, c, r, j) - a.lse2[h * kEstRows + r]);
+      P[r][n] = p;
+    }
+    __syncthreads();
+    if (tid < kTileK) {
+      const int64_t j = k0 + tid;
+      if (j >= e && j < e_end) {
+        float v = 0.f;
+        for (int r = 0; r < kEstRows; ++r) v += P[r][tid];
+        a.vscore[(int64_t)h * a.n_ctx + j] = v;
+      }
+    }
+    // diagonal d = m - n' of a 32 x 32 block, d in [-31, 31]
+    if (tid < 3 * 63) {
+      const int target = tid / 63, d = tid % 63 - 31;
+      float sum = 0.f;
+      for (int blk = 0; blk < 2; ++blk) {
+        int b, kb;
+        if (target == 0) { b = blk; kb = blk; }           // (0,0) + (1,1)
+        else if (target == 1) { if (blk) break; b = 1; kb = 0; }
+        else { if (blk) break; b = 0; kb = 1; }
+        for (int mm = 0; mm < 32; ++mm) {
+          const int n = mm - d;
+          if (n >= 0 && n < 32) sum += P[32 * b + mm][32 * kb + n];
+        }
+      }
+      const int64_t rec = target == 0 ? ((2 * t + 1) * 2 + 0)
+                        : target == 1 ? ((2 * t) * 2 + 1) : ((2 * t + 2) * 2 + 0);
+      drec[rec * 64 + d + 31] += sum;
+    }
+    __syncthreads();
   }
 }
 
@@ -544,6 +624,12 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     a.period = d.period;
     a.n_tiles = L.n_tiles;
     a.n_split = (int32_t)L.n_split;
+    // a DCA chunk edge inside a 64-key tile: its later keys take the edge
+    // kernels and a partial of their own
+    bool edges = false;
+    for (int64_t c = 1; d.period && c * d.period < c1 && !edges; ++c)
+      edges = (c * d.period) % kTileK != 0;
+    a.n_part = a.n_split + (edges ? 1 : 0);
     a.tiles_per_split = (L.n_tiles + L.n_split - 1) / L.n_split;
     a.scale_log2 = p.sm_scale * kLog2e;
     a.part = part;
@@ -568,6 +654,12 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     else hipLaunchKernelGGL(est_pass1<64>, grid, block, 0, s, a);
     rc = check_launch("estimate pass 1");
     if (rc) return rc;
+    if (edges) {
+      if (p.head_dim == 128) hipLaunchKernelGGL(est_edge1<128>, dim3(p.n_heads), dim3(kEstRows), 0, s, a);
+      else hipLaunchKernelGGL(est_edge1<64>, dim3(p.n_heads), dim3(kEstRows), 0, s, a);
+      rc = check_launch("estimate edge pass 1");
+      if (rc) return rc;
+    }
     hipLaunchKernelGGL(est_combine, dim3(p.n_heads), dim3(256), 0, s, a);
     rc = check_launch("estimate combine");
     if (rc) return rc;
@@ -575,6 +667,12 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     else hipLaunchKernelGGL(est_pass2<64>, grid, block, 0, s, a);
     rc = check_launch("estimate pass 2");
     if (rc) return rc;
+    if (edges) {
+      if (p.head_dim == 128) hipLaunchKernelGGL(est_edge2<128>, dim3(p.n_heads), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL(est_edge2<64>, dim3(p.n_heads), dim3(256), 0, s, a);
+      rc = check_launch("estimate edge pass 2");
+      if (rc) return rc;
+    }
     hipLaunchKernelGGL(est_slash_reduce, dim3((unsigned)((c1 + 255) / 256), p.n_heads),
                        dim3(256), 0, s, a);
     rc = check_launch("estimate slash reduce");

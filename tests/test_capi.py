@@ -138,7 +138,7 @@ def test_attention_rejects_other_arguments(lib):
     assert attn(lib, p, pattern(), ws_bytes=need - 1) == C.LCSR_EWORKSPACE
     assert str(need) in err(lib)
     assert attn(lib, p, pattern(), ws=None) == C.LCSR_EWORKSPACE
-    # the DCA period must be a multiple of the 16-key granule here
+    # the DCA period must be a multiple of the 32-row block here
     q = problem(dca_chunk=262144, dca_local=32760)
     assert attn(lib, q, pattern()) == C.LCSR_ENOTSUP
     # the context cap (the row block's key bitmap lives in LDS)
@@ -149,15 +149,17 @@ def test_attention_rejects_other_arguments(lib):
 
 def test_dca_period_alignment_per_call(lib):
     """DCA key periods S = C - W: every call takes S >= 64; the vertical-slash
-    attention needs S % 16 == 0 (granules), the block-sparse calls S % 64 == 0
-    (blocks); decode, estimate and recall take any S."""
+    attention needs S % 32 == 0 (32-row blocks), the block-sparse calls
+    S % 64 == 0 (blocks); decode, estimate and recall take any S."""
     def ws(which, local):
         p = problem(dca_chunk=262144, dca_local=local)
         return lib.lcsr_workspace_bytes(which, ctypes.byref(p), 1000, 6096)
+    s32 = 32736    # S = 229408 = 32 x 7169
     s16 = 32752    # S = 229392 = 16 x 14337
     s4 = 32756     # S = 229388, a multiple of 4 only
-    assert ws(C.LCSR_WS_ATTN, s16) > 0 and ws(C.LCSR_WS_ATTN, s4) == 0
-    assert ws(C.LCSR_WS_BLOCK_ATTN, s16) == 0 and ws(C.LCSR_WS_BLOCK_EST, s16) == 0
+    assert ws(C.LCSR_WS_ATTN, s32) > 0
+    assert ws(C.LCSR_WS_ATTN, s16) == 0 and ws(C.LCSR_WS_ATTN, s4) == 0
+    assert ws(C.LCSR_WS_BLOCK_ATTN, s32) == 0 and ws(C.LCSR_WS_BLOCK_EST, s32) == 0
     assert ws(C.LCSR_WS_BLOCK_ATTN, 32768) > 0
     for which in (C.LCSR_WS_ESTIMATE, C.LCSR_WS_RECALL, C.LCSR_WS_DECODE):
         assert ws(which, s4) > 0

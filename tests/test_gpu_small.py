@@ -216,22 +216,22 @@ def test_attention_tiny_dense(c0, lc):
     _attn_case(TINY, c0, lc, None, None, dense=True)
 
 
-# A DCA period that is a multiple of 16 but not of 32 (C 256, W 48: S 208):
-# the 32-row blocks [192, 224), [416, 448), ... hold a chunk edge, so the rows
-# of one block take different query variants, and key tiles are cut at the
-# edges.
+# A DCA period that is a multiple of 32 but not of 64 (C 256, W 96: S 160):
+# the walk cuts the key tiles [128, 192), [448, 512), ... at the chunk edges
+# 160, 480, ..., and the row blocks on either side take different variants.
+TINY_S160 = scaled(TINY, dca_local=96)
 TINY_S208 = scaled(TINY, dca_local=48)
 
 
 @pytest.mark.parametrize("c0,lc", [(0, 1024), (128, 448)])
-def test_attention_period_208(c0, lc):
-    rng = np.random.default_rng(208 + c0)
+def test_attention_period_160(c0, lc):
+    rng = np.random.default_rng(160 + c0)
     c1 = c0 + lc
     verts = [sorted(rng.choice(c1, size=40, replace=False).tolist())]
-    slashes = [sorted(set([0, 1, 2, 200, 207, 208, 209] +
+    slashes = [sorted(set([0, 1, 2, 150, 159, 160, 161] +
                           rng.choice(c1, size=60, replace=False).tolist()))]
-    _attn_case(TINY_S208, c0, lc, verts, slashes)
-    _attn_case(TINY_S208, c0, lc, None, None, dense=True)
+    _attn_case(TINY_S160, c0, lc, verts, slashes)
+    _attn_case(TINY_S160, c0, lc, None, None, dense=True)
 
 
 def test_estimate_period_208():
