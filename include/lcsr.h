@@ -118,8 +118,8 @@ typedef struct lcsr_dca {
  * n_heads <= 64, n_heads % n_kv_heads == 0, n_heads / n_kv_heads <= 16.
  * With DCA on, S = C - W >= 64 and chunk_start % 64 == 0 (any chunk_start
  * for lcsr_attn_decode); lcsr_vs_sparse_attn_prefill takes S % 32 == 0 (its
- * 32-query-row blocks stay inside one DCA chunk) and the block-sparse calls
- * S % 64 == 0 (their 64-key blocks do); the other calls take any S. */
+ * 32-query-row blocks stay inside one DCA chunk); the other calls take any
+ * S. */
 typedef struct lcsr_problem {
   const void* q;       /* [H, chunk_len, D] pre-RoPE queries of the chunk   */
   int32_t q_dtype;     /* LCSR_BF16 or LCSR_FP32 (fp32 is rounded to bf16)  */

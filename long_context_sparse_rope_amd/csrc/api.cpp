@@ -133,10 +133,8 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // any_start: the rows may start anywhere (decode); otherwise, with DCA, the
 // chunk must start on a 64-token tile.  period_align: the DCA key period S =
 // chunk - local must be a multiple of it (32 for the vertical-slash
-// attention, whose 32-row blocks share one query variant and whose 16-key
-// granules must not straddle a DCA chunk edge; 64 for the block-sparse
-// calls, whose 64-key blocks must not; 1 elsewhere).  Every call takes
-// S >= 64, so a 64-key tile meets at most one edge.
+// attention, whose 32-row blocks share one query variant; 1 elsewhere).
+// Every call takes S >= 64, so a 64-key tile meets at most one edge.
 int validate_problem(const lcsr_problem_t* p, bool need_v, bool any_start = false,
                      int64_t period_align = 1) {
   if (!p) return fail(LCSR_EINVAL, "problem is NULL");
@@ -233,9 +231,7 @@ float lcsr_softmax_scale(const lcsr_rope_t* rope, int32_t head_dim) {
 
 size_t lcsr_workspace_bytes(int which, const lcsr_problem_t* p, int32_t max_vert,
                             int32_t max_slash) {
-  const int64_t align = which == LCSR_WS_ATTN ? kRowBlock
-                        : (which == LCSR_WS_BLOCK_EST || which == LCSR_WS_BLOCK_ATTN) ? kTileK
-                                                                                       : 1;
+  const int64_t align = which == LCSR_WS_ATTN ? kRowBlock : 1;
   if (!p || validate_problem(p, false, which == LCSR_WS_DECODE, align) != LCSR_OK) return 0;
   switch (which) {
     case LCSR_WS_ESTIMATE: return estimate_layout(*p).total;
@@ -404,7 +400,7 @@ int lcsr_block_sparse_estimate(const lcsr_problem_t* p, const int32_t* n_blocks,
                                const int32_t* head_mask, int32_t max_blocks, int32_t* blk_idx,
                                int32_t* blk_cnt, float* scores, uint32_t flags, void* ws,
                                size_t ws_bytes, void* stream) {
-  int rc = validate_problem(p, false, false, kTileK);
+  int rc = validate_problem(p, false);
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
@@ -434,7 +430,7 @@ int lcsr_block_sparse_attn_prefill(const lcsr_problem_t* p, const int32_t* blk_i
                                    const int32_t* head_mask, void* out, int32_t out_dtype,
                                    int64_t o_stride_h, int64_t o_stride_t, float* lse,
                                    int64_t* stats, void* ws, size_t ws_bytes, void* stream) {
-  int rc = validate_problem(p, true, false, kTileK);
+  int rc = validate_problem(p, true);
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;
@@ -508,7 +504,7 @@ int lcsr_block_sparse_recall_check(const lcsr_problem_t* p, const int32_t* blk_i
                                    const int32_t* head_mask, const int32_t* rows,
                                    int32_t n_rows, float* lse_full, float* lse_sparse,
                                    float* recall, void* stream) {
-  int rc = validate_problem(p, false, false, kTileK);
+  int rc = validate_problem(p, false);
   if (rc) return rc;
   rc = validate_blocks(p, max_blocks);
   if (rc) return rc;

@@ -1458,9 +1458,9 @@ __global__ void __launch_bounds__(256) decode_combine(DecArgs a, void* out, int3
 // attend to the key blocks listed for it, causally inside the diagonal
 // block.  The decode step's scheme with two consumers: waves 0 and 1 multiply
 // (rows 0-31 and 32-63 of the block, sharing every tile), wave 2 streams the
-// K tiles and wave 3 the V tiles of the list into a ring of kStages stages.  A 32-row block lies inside one DCA
-// chunk (the period and the chunk start are multiples of 64), so the query
-// variant changes only with the tile's key chunk.
+// K tiles and wave 3 the V tiles of the list into a ring of kStages stages.
+// Each lane takes the query variant of its own row; a key block that meets a
+// DCA chunk edge runs as two passes, one per key chunk.
 struct BsArgs {
   const uint16_t* __restrict__ q_rot;  // [n_var][H][L][D]
   const uint16_t* __restrict__ k;
@@ -1564,12 +1564,24 @@ __global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
   st.l = 0.f;
   int cur_var = -1;
   unsigned long long sel = 0;
-  for (int i = 0; i < n_local; ++i) {
-    step_barrier();
-    const Tile tt = tile_of(i);
-    // rel >= 0 here (kept blocks lie at or before the diagonal); clamped all
-    // the same, so that the query load can never leave the variants
-    const int64_t rel = qchunk - tt.kchunk;
+  // One iteration per (block, key chunk) pass: a block meets at most one DCA
+  // chunk edge (the period is at least 64 keys), and its keys on either side
+  // take the query variant of their own chunk; the barrier comes with each
+  // new block.
+  Tile tt{};
+  int64_t edge = kTileK;  // first key of the later chunk in the block
+  int seg = 0;
+  for (int i = 0; i < n_local;) {
+    if (seg == 0) {
+      step_barrier();
+      tt = tile_of(i);
+      const int64_t next = (int64_t)(tt.kchunk + 1) * a.period - tt.ks;
+      edge = (a.period && next < tt.n) ? next : kTileK;
+    }
+    // rel >= 0 here (kept blocks lie at or before the diagonal) except for a
+    // row before an edge inside its own block; clamped all the same, so that
+    // the query load can never leave the variants
+    const int64_t rel = qchunk - (tt.kchunk + seg);
     const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
     if (__ballot(var != cur_var) != 0ull) {
       const uint16_t* qp =
@@ -1580,7 +1592,8 @@ __global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
       cur_var = var;
     }
     const int64_t lim = my_row - tt.ks + 1;
-    const uint64_t mword = low_bits(lim < tt.n ? lim : tt.n);
+    const uint64_t mword =
+        low_bits(lim < tt.n ? lim : tt.n) & (seg ? ~low_bits(edge) : low_bits(edge));
     if (live && half == 0) sel += __popcll(mword);
     const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
     const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
@@ -1589,6 +1602,12 @@ __global__ void __launch_bounds__(256) bs_attn_kernel(BsArgs a) {
     bf16x8 pf[4];
     wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
     wave_pv<D>(bc, lc, st, pf, act0, act1);
+    if (seg == 0 && edge < kTileK) {
+      seg = 1;
+    } else {
+      seg = 0;
+      ++i;
+    }
   }
   const float l_tot = sum_halves(st.l);
   if (live) {
@@ -1780,32 +1799,51 @@ __global__ void __launch_bounds__(64 * (NW + 1)) bs_attn_gqa_kernel(BsArgs a) {
   st.l = 0.f;
   int cur_var = -1;
   unsigned long long sel = 0, exe = 0;
-  for (int i = 0; i < n_local; ++i) {
-    step_barrier();
-    const uint32_t heads = __builtin_amdgcn_readfirstlane(tile_heads[i]);
-    if (!head_on || !((heads >> hh) & 1u)) continue;
-    const Tile tt = tile_of(i);
-    const int64_t rel = qchunk - tt.kchunk;
-    const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
-    if (__ballot(var != cur_var) != 0ull) {
-      const uint16_t* qp =
-          a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;
-#pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) st.q[s2] = *reinterpret_cast<const f16x8*>(qp + s2 * 16);
-      wait_vm<0>();
-      cur_var = var;
+  // One iteration per (tile, key chunk) pass, as in bs_attn_kernel.
+  Tile tt{};
+  int64_t edge = kTileK;  // first key of the later chunk in the tile
+  uint32_t heads = 0;
+  int seg = 0;
+  for (int i = 0; i < n_local;) {
+    if (seg == 0) {
+      step_barrier();
+      heads = __builtin_amdgcn_readfirstlane(tile_heads[i]);
+      tt = tile_of(i);
+      const int64_t next = (int64_t)(tt.kchunk + 1) * a.period - tt.ks;
+      edge = (a.period && next < tt.n) ? next : kTileK;
     }
-    const int64_t lim = my_row - tt.ks + 1;
-    const uint64_t mword = low_bits(lim < tt.n ? lim : tt.n);
-    if (live && half == 0) sel += __popcll(mword);
-    ++exe;
-    const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
-    const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
-    const bool masked = __ballot(mword == ~0ull) != ~0ull;
-    const char* bc = stage[i % kBsgStages];
-    bf16x8 pf[4];
-    wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {}, [] {});
-    wave_pv<D>(bc, lc, st, pf, act0, act1);
+    if (head_on && ((heads >> hh) & 1u)) {
+      const int64_t rel = qchunk - (tt.kchunk + seg);
+      const int var = a.n_var == 1 ? 0 : (rel >= 2 ? 2 : (rel <= 0 ? 0 : (int)rel));
+      if (__ballot(var != cur_var) != 0ull) {
+        const uint16_t* qp =
+            a.q_rot + (((int64_t)var * a.H + h) * a.L + (my_row - a.c0)) * D + 8 * half;
+#pragma unroll
+        for (int s2 = 0; s2 < D / 16; ++s2)
+          st.q[s2] = *reinterpret_cast<const f16x8*>(qp + s2 * 16);
+        wait_vm<0>();
+        cur_var = var;
+      }
+      const int64_t lim = my_row - tt.ks + 1;
+      const uint64_t mword =
+          low_bits(lim < tt.n ? lim : tt.n) & (seg ? ~low_bits(edge) : low_bits(edge));
+      if (live && half == 0) sel += __popcll(mword);
+      if (seg == 0) ++exe;
+      const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+      const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+      const bool masked = __ballot(mword == ~0ull) != ~0ull;
+      const char* bc = stage[i % kBsgStages];
+      bf16x8 pf[4];
+      wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
+                     [] {});
+      wave_pv<D>(bc, lc, st, pf, act0, act1);
+    }
+    if (seg == 0 && edge < kTileK) {
+      seg = 1;
+    } else {
+      seg = 0;
+      ++i;
+    }
   }
   if (!head_on) return;
   const float l_tot = sum_halves(st.l);

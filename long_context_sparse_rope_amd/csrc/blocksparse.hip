@@ -12,8 +12,9 @@
 // The K cache holds R(P_k(j)) k_j with P_k(j) = j - S c(j), so the mean of a
 // key block is taken from the cache as it is and the query mean is turned
 // back by R(-S c) for key chunk c: <R(-S c) Q, mean R(j - S c) k_j> =
-// <Q, mean R(j) k_j>.  A key block never crosses a DCA chunk edge (S is a
-// multiple of 64).
+// <Q, mean R(j) k_j>.  A block's chunk c is that of its first key; keys of a
+// block after a chunk edge (S need not be a multiple of 64) are turned by
+// R(S) into the frame of chunk c before they are averaged.
 #include "lcsr_internal.h"
 
 namespace lcsr {
@@ -33,24 +34,45 @@ __device__ __forceinline__ float load_q(const void* q, int32_t dtype, int64_t id
   return bf16_to_f32(static_cast<const uint16_t*>(q)[idx]);
 }
 
-// grid (n_kb, H_kv), 64 threads: mean of each 64-key block of the (fp16) cache,
-// stored as float4 [H_kv][D / 4][n_kb] so that lanes of the score kernel
-// (one key block each) read consecutive addresses.
+// grid (n_kb, H_kv), 64 threads (one rotation pair (p, p + D/2) each): mean
+// of each 64-key block of the (fp16) cache in the frame of its first key's
+// DCA chunk, stored as float4 [H_kv][D / 4][n_kb] so that lanes of the score
+// kernel (one key block each) read consecutive addresses.
 __global__ void __launch_bounds__(64) bs_pool_keys(const uint16_t* __restrict__ k, int64_t kv_sh,
                                                    int64_t kv_st, int64_t n_ctx, int D,
-                                                   int64_t n_kb, float* __restrict__ pk) {
+                                                   int64_t n_kb, int64_t period, FreqTable ft,
+                                                   float* __restrict__ pk) {
   const int64_t kb = blockIdx.x;
   const int g = blockIdx.y;
+  const int half = D / 2, p = threadIdx.x;
+  if (p >= half) return;
   const int64_t j0 = kb * kBlk;
   const int64_t j1 = j0 + kBlk < n_ctx ? j0 + kBlk : n_ctx;
-  const float inv = 1.0f / (float)(j1 - j0);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    const uint16_t* src = k + g * kv_sh + d;
-    float s = 0.f;
-#pragma unroll 8
-    for (int64_t j = j0; j < j1; ++j) s += f16_to_f32(src[j * kv_st]);
-    pk[(((int64_t)g * (D / 4) + d / 4) * n_kb + kb) * 4 + d % 4] = s * inv;
+  // first key of the next DCA chunk, if inside the block
+  int64_t edge = j1;
+  if (period) {
+    const int64_t next = (j0 / period + 1) * period;
+    edge = next < j1 ? next : j1;
   }
+  const float inv = 1.0f / (float)(j1 - j0);
+  const uint16_t* src = k + g * kv_sh;
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll 8
+  for (int64_t j = j0; j < edge; ++j) {
+    s1 += f16_to_f32(src[j * kv_st + p]);
+    s2 += f16_to_f32(src[j * kv_st + p + half]);
+  }
+  if (edge < j1) {
+    float c, sn;
+    rope_cos_sin(period, ft.inv_freq[p], &c, &sn);
+    for (int64_t j = edge; j < j1; ++j) {
+      const float x1 = f16_to_f32(src[j * kv_st + p]), x2 = f16_to_f32(src[j * kv_st + p + half]);
+      s1 += x1 * c - x2 * sn;
+      s2 += x2 * c + x1 * sn;
+    }
+  }
+  pk[(((int64_t)g * (D / 4) + p / 4) * n_kb + kb) * 4 + p % 4] = s1 * inv;
+  pk[(((int64_t)g * (D / 4) + (p + half) / 4) * n_kb + kb) * 4 + (p + half) % 4] = s2 * inv;
 }
 
 // grid (n_qb, H), 64 threads (one rotation pair each): the block mean of
@@ -120,13 +142,14 @@ __global__ void __launch_bounds__(256) bs_score(ScoreArgs a) {
   const int nv = a.G * nq;  // vectors: v = hh * nq + b
   const int64_t diag0 = a.c0 / kBlk + qb0;        // diagonal of the first block
   const int64_t kb_end = diag0 + nq;              // one past the last diagonal
-  const int64_t kpc = a.period ? a.period / kBlk : kb_end;  // key blocks per key chunk
   const int64_t z0 = (int64_t)blockIdx.z * kScoreSpan;
   const int64_t z1 = z0 + kScoreSpan < kb_end ? z0 + kScoreSpan : kb_end;
   if (z0 >= z1) return;
   for (int kc = 0; kc < a.n_kc; ++kc) {
-    int64_t kb_lo = kc * kpc;
-    int64_t kb_hi = kb_lo + kpc < kb_end ? kb_lo + kpc : kb_end;
+    // the key blocks whose first key lies in chunk kc
+    int64_t kb_lo = a.period ? (kc * a.period + kBlk - 1) / kBlk : 0;
+    int64_t kb_hi = a.period ? ((kc + 1) * a.period + kBlk - 1) / kBlk : kb_end;
+    kb_hi = kb_hi < kb_end ? kb_hi : kb_end;
     if (kb_lo >= kb_hi) break;
     kb_lo = kb_lo > z0 ? kb_lo : z0;
     kb_hi = kb_hi < z1 ? kb_hi : z1;
@@ -379,7 +402,7 @@ int run_block_estimate(const lcsr_problem_t& p, const int32_t* budgets_host, uin
     float* pq = reinterpret_cast<float*>(ws + L.o_pq);
     hipLaunchKernelGGL(bs_pool_keys, dim3((unsigned)L.n_kb, (unsigned)p.n_kv_heads), dim3(64), 0,
                        s, static_cast<const uint16_t*>(p.k_cache), p.kv_stride_h, p.kv_stride_t,
-                       L.n_ctx, (int)p.head_dim, L.n_kb, pk);
+                       L.n_ctx, (int)p.head_dim, L.n_kb, period, ft, pk);
     rc = check_launch("block pool keys");
     if (rc) return rc;
     PoolQArgs qa{};

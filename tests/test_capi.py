@@ -149,8 +149,7 @@ def test_attention_rejects_other_arguments(lib):
 
 def test_dca_period_alignment_per_call(lib):
     """DCA key periods S = C - W: every call takes S >= 64; the vertical-slash
-    attention needs S % 32 == 0 (32-row blocks), the block-sparse calls
-    S % 64 == 0 (blocks); decode, estimate and recall take any S."""
+    attention needs S % 32 == 0 (32-row blocks); the other calls take any S."""
     def ws(which, local):
         p = problem(dca_chunk=262144, dca_local=local)
         return lib.lcsr_workspace_bytes(which, ctypes.byref(p), 1000, 6096)
@@ -159,9 +158,8 @@ def test_dca_period_alignment_per_call(lib):
     s4 = 32756     # S = 229388, a multiple of 4 only
     assert ws(C.LCSR_WS_ATTN, s32) > 0
     assert ws(C.LCSR_WS_ATTN, s16) == 0 and ws(C.LCSR_WS_ATTN, s4) == 0
-    assert ws(C.LCSR_WS_BLOCK_ATTN, s32) == 0 and ws(C.LCSR_WS_BLOCK_EST, s32) == 0
-    assert ws(C.LCSR_WS_BLOCK_ATTN, 32768) > 0
-    for which in (C.LCSR_WS_ESTIMATE, C.LCSR_WS_RECALL, C.LCSR_WS_DECODE):
+    for which in (C.LCSR_WS_ESTIMATE, C.LCSR_WS_RECALL, C.LCSR_WS_DECODE,
+                  C.LCSR_WS_BLOCK_EST, C.LCSR_WS_BLOCK_ATTN):
         assert ws(which, s4) > 0
     # a period below one 64-key tile is refused by every call
     for which in (C.LCSR_WS_ESTIMATE, C.LCSR_WS_ATTN, C.LCSR_WS_DECODE):

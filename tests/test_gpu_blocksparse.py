@@ -222,12 +222,13 @@ def test_every_block_is_dense():
     assert d <= 1e-3, d
 
 
-def test_tiny_ragged_chunk_bf16_out():
-    """fp32 inputs (taken at bf16), D 64, DCA C 256 W 64, a 1000-row chunk
-    after 0 (last query block of 40 rows) and bf16 output.  The block-sparse
-    calls take DCA periods in whole 64-key blocks: the tiny layer runs here
-    with W 64 (S 192)."""
-    cfg = scaled(TINY, dca_local=64)
+@pytest.mark.parametrize("local", [32, 48])
+def test_tiny_ragged_chunk_bf16_out(local):
+    """fp32 inputs (taken at bf16), D 64, DCA C 256 with W 32 (S 224) and W 48
+    (S 208): key blocks 192..255 (and more) hold a chunk edge, query blocks
+    too; a 1000-row chunk after 0 (last query block of 40 rows) and bf16
+    output."""
+    cfg = scaled(TINY, dca_local=local)
     q, k, v = synth.generate(cfg, DEV)
     layer = _layer(cfg)
     build_cache(layer, k, v, cfg.seq_len)
