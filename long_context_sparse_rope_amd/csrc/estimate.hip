@@ -9,7 +9,8 @@
 // estimate rows are rotated at (r - S * c) for the DCA chunk c of the key
 // tile, which gives the continuous relative position r - j.
 //
-// Pass 1: row max / sum of exp2 per key split (online, in-lane).
+// Pass 1: row sum of exp2 per key split against a running reference
+// (online, in-lane).
 // Combine: row logsumexp (log2 units of the scaled logits).
 // Pass 2: probabilities, vertical sums (per key, in-lane over rows) and
 // diagonal sums of every 32x32 block (through a wave-private LDS scratch),
@@ -213,46 +214,58 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
     // DCA chunk edge inside it (those keys are the edge kernel's)
     const int64_t kedge = straddle_edge(a, k0, c);
     const bool edge = (k0 + kTileK - 1 > a.row0) || kedge < k0 + kTileK;
+    // key block kb: its K fragments are read once and serve both row blocks
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int kb = 0; kb < 2; ++kb) {
+      f16x8 kf[D / 16];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) kf[s] = k_frag<D>(ks, kb, s);
       f32x16 acc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc[kb] = (f32x16){};
+      for (int b = 0; b < 2; ++b) {
+        acc[b] = (f32x16){};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
-          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k_frag<D>(ks, kb, s), qf[b][s],
-                                                            acc[kb], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[s], qf[b][s], acc[b], 0, 0, 0);
       }
-      const int64_t row = a.row0 + b * 32 + (lane & 31);
-      // row max and sum over four interleaved partial chains (fixed order),
-      // which keeps the dependent vector chains short
-      float x[2][16];
-      float mp[4] = {m[b], -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int b = 0; b < 2; ++b) {
+        if (edge) {
+          const int64_t row = a.row0 + b * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = acc[kb][r] * a.scale_log2;
-          if (edge) {
+          for (int r = 0; r < 16; ++r) {
             const int64_t key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key > row || key >= a.n_ctx || key >= kedge) v = -INFINITY;
+            if (key > row || key >= a.n_ctx || key >= kedge) acc[b][r] = -INFINITY;
           }
-          x[kb][r] = v;
-          mp[r & 3] = fmaxf(mp[r & 3], v);
         }
-      const float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-      if (mx == -INFINITY) continue;
-      // exponentials below 2^-126 flush to zero (v_exp_f32); they are far
-      // below the precision of the row sum
-      float sp[4] = {0.f, 0.f, 0.f, 0.f};
+        // The row sum is kept against a reference m that need not be the
+        // row max: 2^(x - m) is exact for any m.  The block's own max is
+        // taken only for a row's first keys or when the block's sum leaves
+        // 2^64 (then l is rescaled to the new m).  Exponentials below 2^-126
+        // flush to zero (v_exp_f32), far below the precision of the row sum.
+        // Four interleaved partial sums (fixed order) keep the chains short.
+        auto block_sum = [&](float mref) {
+          float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int r = 0; r < 16; ++r)
+            sp[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[b][r], a.scale_log2, -mref));
+          return (sp[0] + sp[1]) + (sp[2] + sp[3]);
+        };
+        float sum = block_sum(m[b] == -INFINITY ? 0.f : m[b]);
+        const bool slow = m[b] == -INFINITY || !(sum <= 0x1p64f);
+        if (__builtin_expect(__ballot(slow) != 0ull, 0) && slow) {
+          float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sp[r & 3] += __builtin_amdgcn_exp2f(x[kb][r] - mx);
-      const float sum = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-      l[b] = l[b] * exp2f(m[b] - mx) + sum;
-      m[b] = mx;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[b][r]);
+          mx *= a.scale_log2;
+          if (mx > m[b]) {
+            l[b] = m[b] == -INFINITY ? 0.f : l[b] * exp2f(m[b] - mx);
+            m[b] = mx;
+            sum = block_sum(mx);
+          }
+        }
+        l[b] += sum;
+      }
     }
     }
     est_barrier();  // tile i done, tile i + 1 in its stage
