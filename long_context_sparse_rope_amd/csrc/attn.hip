@@ -1222,15 +1222,20 @@ struct DecArgs {
 
 constexpr int kDecStages = 5;
 
-// Workgroup: wave 0 multiplies; wave 1 loads the K tiles and wave 2 the V
-// tiles of its key range (direct-to-LDS, 16 loads per tile each, so each
-// keeps four tiles in flight under the 63-load vmcnt limit).  A stage holds
-// K then V of one tile (no key list: 32 KB at D 128, so five stages fill the
-// 160 KB of LDS).  Tile i of the range sits in stage i mod 5; at barrier i
-// tile i has landed and the products of tile i - 1 are done, so tile i + 4
-// then refills that stage.
+// Workgroup: waves 0 and 1 multiply, wave 0 the first and wave 1 the second
+// 32-key half of every tile, each with an online softmax state of its own;
+// wave 2 loads the K tiles and wave 3 the V tiles of the key range
+// (direct-to-LDS, 16 loads per tile each, so each keeps four tiles in flight
+// under the 63-load vmcnt limit).  A stage holds K then V of one tile (no key
+// list: 32 KB at D 128, so five stages fill the 160 KB of LDS).  Tile i of
+// the range sits in stage i mod 5; at barrier i tile i has landed and the
+// products of tile i - 1 are done, so tile i + 4 then refills that stage.
+// At the end the two states are merged in a fixed order (wave 0's, then
+// wave 1's), so the partial does not depend on timing.
+constexpr int kDecThreads = 256;
+
 template <int D>
-__global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
+__global__ void __launch_bounds__(kDecThreads, 1) decode_kernel(DecArgs a) {
   using B = Buf<D>;
   constexpr int M = B::kInstrPerMat;  // loads per matrix and tile
   constexpr int R = B::kRowsPerInstr;
@@ -1253,9 +1258,9 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
     x.gran = 15;
     return x;
   };
-  if (w > 0) {
-    // ---------------- loaders: wave 1 K, wave 2 V
-    const bool isv = w == 2;
+  if (w >= 2) {
+    // ---------------- loaders: wave 2 K, wave 3 V
+    const bool isv = w == 3;
     const char* src = reinterpret_cast<const char*>((isv ? a.v : a.k) + (int64_t)g * a.kv_sh);
     const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
     const uint32_t base = lds_addr(&stage[0][0]) + (isv ? B::kKBytes : 0);
@@ -1283,9 +1288,11 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
       step_barrier();
       if (i + kDecStages - 1 < n_local) issue(i + kDecStages - 1);
     }
+    __syncthreads();  // the products are done: stage 0 takes wave 1's state
+    __syncthreads();  // wave 0 has read it
     return;
   }
-  // ---------------- wave 0: the products
+  // ---------------- waves 0 and 1: the products of key half w
   // this lane's matrix row: (head, row) pair rho; rows past G x n_q repeat a
   // live pair's query and are never written
   const int rho = lane & 31;
@@ -1345,8 +1352,8 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
       cur_var = var;
     }
     const uint64_t mword = causal & (seg ? ~low_bits(edge) : low_bits(edge));
-    const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
-    const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+    const bool act0 = w == 0 && __ballot((uint32_t)mword != 0u) != 0;
+    const bool act1 = w == 1 && __ballot((uint32_t)(mword >> 32) != 0u) != 0;
     const bool masked = __ballot(mword == ~0ull) != ~0ull;
     const char* bc = stage[i % kDecStages];
     bf16x8 pf[4];
@@ -1358,6 +1365,34 @@ __global__ void __launch_bounds__(192, 1) decode_kernel(DecArgs a) {
       seg = 0;
       ++i;
     }
+  }
+  // wave 1's state through LDS (stage 0, lane-major: conflict-free), merged
+  // into wave 0's: M = max(m0, m1), l and O weighted by 2^(m - M)
+  constexpr int NO = D / 32 * 16;  // O values per lane
+  float* xs = reinterpret_cast<float*>(&stage[0][0]);
+  __syncthreads();
+  if (w == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 16; ++i4) xs[(db * 16 + i4) * 64 + lane] = st.o[db][i4];
+    xs[NO * 64 + lane] = st.m;
+    xs[(NO + 1) * 64 + lane] = st.l;
+  }
+  __syncthreads();
+  if (w == 1) return;
+  {
+    const float m1 = xs[NO * 64 + lane], l1 = xs[(NO + 1) * 64 + lane];
+    const float mm = fmaxf(st.m, m1);
+    const float a0 = st.m == -INFINITY ? 0.f : exp2f(st.m - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - mm);
+    st.l = st.l * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 16; ++i4)
+        st.o[db][i4] = st.o[db][i4] * a0 + xs[(db * 16 + i4) * 64 + lane] * a1;
+    st.m = mm;
   }
   // the split's partial for every live pair: O unnormalised, m in log2 units
   if (live) {
@@ -1914,8 +1949,8 @@ int launch_block_attn(const BsArgs& a, hipStream_t s) {
 template <int D>
 int launch_decode(const DecArgs& a, void* out, int32_t out_dtype, int64_t o_sh, int64_t o_st,
                   float* lse, int n_kv, hipStream_t s) {
-  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)a.n_split, (unsigned)n_kv), dim3(192), 0, s,
-                     a);
+  hipLaunchKernelGGL(decode_kernel<D>, dim3((unsigned)a.n_split, (unsigned)n_kv),
+                     dim3(kDecThreads), 0, s, a);
   int rc = check_launch("decode attention");
   if (rc) return rc;
   hipLaunchKernelGGL(decode_combine<D>, dim3((unsigned)(a.G * a.n_q), (unsigned)n_kv), dim3(256),
