@@ -46,9 +46,6 @@ EstimateLayout estimate_layout(const lcsr_problem_t& p) {
   int64_t want = (1024 + p.n_kv_heads - 1) / p.n_kv_heads;
   L.n_split = want < L.n_tiles ? want : L.n_tiles;
   if (L.n_split < 1) L.n_split = 1;
-  // diagonal partial sums: one 64-float record per (32-query block, 32-key
-  // block) diagonal group e, with two slots
-  L.n_diag = 2 * L.n_tiles + 2;
   L.q_est = align256((size_t)L.n_kc * H * kEstRows * D * 2);
   // one partial per key split, plus one for the keys past DCA chunk edges
   // inside 64-key tiles (scored apart, with the next chunk's query rows)
@@ -56,9 +53,10 @@ EstimateLayout estimate_layout(const lcsr_problem_t& p) {
   L.lse = align256((size_t)H * kEstRows * sizeof(float));
   L.vscore = align256((size_t)H * L.n_ctx * sizeof(float));
   L.sscore = L.vscore;
-  L.diag = align256((size_t)H * L.n_diag * 2 * 64 * sizeof(float));
+  // slash-score parts at the key-split boundaries: five per lane of 32
+  L.bnd = align256((size_t)H * L.n_split * 5 * 32 * sizeof(float));
   L.topk = align256(topk_workspace(L.n_ctx, (int)H));
-  L.total = L.q_est + L.part + L.lse + L.vscore + L.sscore + L.diag + L.topk;
+  L.total = L.q_est + L.part + L.lse + L.vscore + L.sscore + L.bnd + L.topk;
   return L;
 }
 

@@ -13,9 +13,12 @@
 // (online, in-lane).
 // Combine: row logsumexp (log2 units of the scaled logits).
 // Pass 2: probabilities, vertical sums (per key, in-lane over rows) and
-// diagonal sums of every 32x32 block (through a wave-private LDS scratch),
-// all in a fixed order: the scores are bitwise reproducible.
-// Reduce: slash score per offset from the <= 2 diagonal records covering it.
+// diagonal sums of every 32x32 block (lane permutes), all in a fixed order:
+// the scores are bitwise reproducible.  A slash score gathers the diagonal
+// sums of two consecutive tiles; a wave carries the previous tile's sums and
+// writes each slash score once both tiles are done.  At the first tile of a
+// key split the two tiles belong to two workgroups: both write their parts
+// to a small boundary buffer and est_slash_fix adds them in the same order.
 // DCA key periods need not be multiples of the 64-key tile: in a tile that
 // meets a chunk edge the passes count only the keys before it, and the edge
 // kernels score the keys after it with the next chunk's query rows (a
@@ -46,8 +49,7 @@ struct EstArgs {
   float* lse2;            // [H][64]
   float* vscore;          // [H][n_ctx]
   float* sscore;          // [H][n_ctx]
-  float* diag;            // [H][n_diag][2][64]
-  int64_t n_diag;
+  float* bnd;             // [H][n_split][5][32] slash sums at key-split boundaries
   uint64_t head_mask;
   int32_t n_sub, nw;      // workgroups per KV head, query heads (waves) per workgroup
 };
@@ -291,41 +293,55 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass1(EstArgs a) 
   }
 }
 
-// Row logsumexp from the split partials: thread (part, r) reduces splits
-// part, part + 4, ... of row r; the four parts are then merged in order.
+// Row logsumexp from the split partials: one wave per (head, row); lane j
+// merges partials j, j + 64, ... online in ascending order, then the lanes
+// are merged pairwise over a fixed butterfly (lane distance 1, 2, ..., 32),
+// so the result does not depend on timing.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float mv, float lv) {
+  if (mv == -INFINITY) return;
+  if (mv > m) {
+    l = (m == -INFINITY ? 0.f : l * exp2f(m - mv)) + lv;
+    m = mv;
+  } else {
+    l += lv * exp2f(mv - m);
+  }
+}
+
 __global__ void __launch_bounds__(256) est_combine(EstArgs a) {
-  const int h = blockIdx.x, r = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int h = blockIdx.y, r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (!((a.head_mask >> h) & 1)) return;
-  __shared__ float pm[4][kEstRows], pl[4][kEstRows];
   const float* p = a.part + ((int64_t)h * a.n_part * kEstRows + r) * 2;
-  float mm = -INFINITY;
-  for (int z = part; z < a.n_part; z += 4) mm = fmaxf(mm, p[(int64_t)z * kEstRows * 2]);
-  float ll = 0.f;
-  if (mm != -INFINITY)
-    for (int z = part; z < a.n_part; z += 4)
-      ll += p[(int64_t)z * kEstRows * 2 + 1] * exp2f(p[(int64_t)z * kEstRows * 2] - mm);
-  pm[part][r] = mm;
-  pl[part][r] = ll;
-  __syncthreads();
-  if (part != 0) return;
-  float M = pm[0][r];
-  for (int u = 1; u < 4; ++u) M = fmaxf(M, pm[u][r]);
-  float L = 0.f;
-  if (M != -INFINITY)
-    for (int u = 0; u < 4; ++u)
-      if (pm[u][r] != -INFINITY) L += pl[u][r] * exp2f(pm[u][r] - M);
-  a.lse2[h * kEstRows + r] = (r < a.n_rows && L > 0.f) ? M + log2f(L) : INFINITY;
+  float m = -INFINITY, l = 0.f;
+  for (int z = lane; z < a.n_part; z += 64)
+    merge_ml(m, l, p[(int64_t)z * kEstRows * 2], p[(int64_t)z * kEstRows * 2 + 1]);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float mo = __shfl_xor(m, d), lo = __shfl_xor(l, d);
+    // the lower lane's state first, in both lanes of the pair
+    float ma = m, la = l, mb = mo, lb = lo;
+    if (lane & d) {
+      ma = mo;
+      la = lo;
+      mb = m;
+      lb = l;
+    }
+    merge_ml(ma, la, mb, lb);
+    m = ma;
+    l = la;
+  }
+  if (lane == 0) a.lse2[h * kEstRows + r] = (r < a.n_rows && l > 0.f) ? m + log2f(l) : INFINITY;
 }
 
 // ------------------------------------------------------------------ pass 2
 // Diagonal sums of a 32x32 block held in the S = Q K^T layout (lane -> key
 // column n = lane % 32, register r -> query row m = 8(r/4) + 4(lane/32) +
-// r%4): dst[d + 31] = sum_m X[m][m - d], d in [-31, 31] (dst[63] = 0).
+// r%4): pos = sum_m X[m][m - t] (diagonal t) and neg = sum_m X[m][m - t +
+// 32] (diagonal t - 32, zero for t = 0), t = lane % 32, in every lane.
 // Lane t of each half pulls, for each of its half's rows m, the value of
-// diagonal t (key n = m - t) or of diagonal t - 32 (key n = m - t + 32) with a
-// lane permute; the two halves are then added, lower half first.  The order
-// of the sums is fixed, so the records are reproducible.
-__device__ __forceinline__ void diag_record(const float (&x)[16], float* dst) {
+// diagonal t or t - 32 with a lane permute; the two halves are then added,
+// lower half first.  The order of the sums is fixed, so they are
+// reproducible.
+__device__ __forceinline__ void diag_pair(const float (&x)[16], float& pos_out, float& neg_out) {
   const int lane = threadIdx.x & 63;
   const int t = lane & 31, half = lane >> 5;
   float pos = 0.f, neg = 0.f;  // diagonal t, diagonal t - 32
@@ -339,11 +355,8 @@ __device__ __forceinline__ void diag_record(const float (&x)[16], float* dst) {
     else neg += v;
   }
   const float pos_o = __shfl_xor(pos, 32), neg_o = __shfl_xor(neg, 32);
-  if (half == 0) {
-    dst[t + 31] = pos + pos_o;
-    if (t > 0) dst[t - 1] = neg + neg_o;
-    else dst[63] = 0.f;
-  }
+  pos_out = half ? pos_o + pos : pos + pos_o;
+  neg_out = half ? neg_o + neg : neg + neg_o;
 }
 
 template <int D>
@@ -371,7 +384,21 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
   float* lse = lse_all[w];
   lse[lane] = active ? a.lse2[h * kEstRows + lane] : INFINITY;
   float* vout = a.vscore + (int64_t)h * a.n_ctx;
-  float* drec = a.diag + (int64_t)h * a.n_diag * 2 * 64;
+  float* sout = a.sscore + (int64_t)h * a.n_ctx;
+  float* bnd = a.bnd + ((int64_t)h * a.n_split + split) * 5 * 32;
+  const int lt = lane & 31;
+  // Diagonal group E of the tiles holds the offsets o = row0 - 32 E + lt
+  // (lt = lane % 32).  Tile t adds (row block b, key block kb) to group
+  // 2t + kb - b: its diagonal t part (pos) to offset row0 - 32 E + lt and
+  // its diagonal t - 32 part (neg) to offset row0 - 32 (E + 1) + lt.  So
+  // the slash score of group E is neg(E - 1) + pos(E), and groups 2t - 1 and
+  // 2t are complete after tile t.  Carried from the previous tile: neg of
+  // its group 2t (c_na), pos and neg of its block (b 0, kb 1) (c_pb0, c_nb0).
+  float c_na = 0.f, c_pb0 = 0.f, c_nb0 = 0.f;
+  auto put = [&](int64_t E, float v) {
+    const int64_t o = a.row0 - 32 * E + lt;
+    if (half == 0 && o >= 0 && o < a.n_ctx) sout[o] = v;
+  };
   est_barrier();  // the first tile is in its stage
   for (int64_t i = 0; t_begin + i < t_end; ++i) {
     const int64_t t = t_begin + i;
@@ -420,14 +447,20 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
     };
     // The four 32x32 blocks (key block kb, row block b) in the order that
     // keeps at most two of them live: (0,0) and (1,1) first (their sum is one
-    // diagonal record), then (kb 0, b 1) and (kb 1, b 0).  Vertical sums in a
+    // diagonal group), then (kb 0, b 1) and (kb 1, b 0).  Vertical sums in a
     // fixed order: key block 0 adds its b = 0 rows then its b = 1 rows, key
-    // block 1 its b = 1 rows then its b = 0 rows.  Diagonal records (index
-    // e + 1): e = 2t holds blocks (0,0) + (1,1), e = 2t + 1 slot 0 the block
-    // (b 0, kb 1), e = 2t - 1 slot 1 the block (b 1, kb 0).
+    // block 1 its b = 1 rows then its b = 0 rows.  Diagonal groups: A = (0,0)
+    // + (1,1) is group 2t, B1 = (b 1, kb 0) group 2t - 1, B0 = (b 0, kb 1)
+    // group 2t + 1.  Group 2t - 1 = (group 2t - 2's neg + group 2t - 1's pos
+    // of the previous tile) + its pos of this tile (B1); group 2t = (group
+    // 2t - 1's neg of the previous tile + that of B1) + A's pos.  At the
+    // first tile of a split the carried parts are zero, so the boundary
+    // buffer takes B1's own parts and A's pos.
+    const bool first = i == 0 && t_begin > 0;
     float pa[16], pb[16];
-    block_p(0, 0, pa);
     float s0 = 0.f, s1 = 0.f;
+    float p_a, n_a;
+    block_p(0, 0, pa);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s0 += pa[r];
     __builtin_amdgcn_sched_barrier(0);
@@ -436,22 +469,64 @@ __global__ void __launch_bounds__(64 * (kMaxEstWaves + 1)) est_pass2(EstArgs a) 
     for (int r = 0; r < 16; ++r) s1 += pb[r];
 #pragma unroll
     for (int r = 0; r < 16; ++r) pa[r] += pb[r];
-    diag_record(pa, drec + ((2 * t + 1) * 2 + 0) * 64);
+    diag_pair(pa, p_a, n_a);  // A
     __builtin_amdgcn_sched_barrier(0);
     block_p(0, 1, pa);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s0 += pa[r];
     vertical(0, s0);
-    diag_record(pa, drec + ((2 * t) * 2 + 1) * 64);
+    {
+      float p, n;
+      diag_pair(pa, p, n);  // B1
+      const float v1 = (c_na + c_pb0) + p;
+      const float w = c_nb0 + n;
+      if (first) {
+        if (half == 0) {
+          bnd[2 * 32 + lt] = v1;
+          bnd[3 * 32 + lt] = w;
+          bnd[4 * 32 + lt] = p_a;
+        }
+      } else {
+        put(2 * t - 1, v1);
+        put(2 * t, w + p_a);
+      }
+      c_na = n_a;
+    }
     __builtin_amdgcn_sched_barrier(0);
     block_p(1, 0, pb);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s1 += pb[r];
     vertical(1, s1);
-    diag_record(pb, drec + ((2 * t + 2) * 2 + 0) * 64);
+    diag_pair(pb, c_pb0, c_nb0);  // B0
     }
     est_barrier();  // tile i done, tile i + 1 in its stage
   }
+  if (!active || t_begin >= t_end) return;
+  if (t_end == a.n_tiles) {
+    // the last tile of the context: groups 2t + 1 and 2t + 2 have no later tile
+    const int64_t t = t_end - 1;
+    put(2 * t + 1, c_na + c_pb0);
+    put(2 * t + 2, c_nb0);
+  } else if (half == 0) {
+    bnd[0 * 32 + lt] = c_na + c_pb0;
+    bnd[1 * 32 + lt] = c_nb0;
+  }
+}
+
+// Slash scores of the two diagonal groups at each key-split boundary: the
+// previous split's parts, then the next split's, in pass 2's order.
+__global__ void __launch_bounds__(256) est_slash_fix(EstArgs a) {
+  const int h = blockIdx.y;
+  const int z = blockIdx.x * 8 + (threadIdx.x >> 5), lt = threadIdx.x & 31;
+  if (!((a.head_mask >> h) & 1) || z < 1 || z >= a.n_split) return;
+  const int64_t tb = (int64_t)z * a.tiles_per_split;
+  if (tb >= a.n_tiles) return;
+  const float* x = a.bnd + ((int64_t)h * a.n_split + z - 1) * 5 * 32;
+  const float* y = x + 5 * 32;
+  float* sout = a.sscore + (int64_t)h * a.n_ctx;
+  const int64_t o1 = a.row0 - 32 * (2 * tb - 1) + lt, o2 = o1 - 32;
+  if (o1 >= 0 && o1 < a.n_ctx) sout[o1] = x[0 * 32 + lt] + y[2 * 32 + lt];
+  if (o2 >= 0 && o2 < a.n_ctx) sout[o2] = (x[1 * 32 + lt] + y[3 * 32 + lt]) + y[4 * 32 + lt];
 }
 
 // ------------------------------------------------------------ DCA edges
@@ -511,12 +586,12 @@ __global__ void __launch_bounds__(kEstRows) est_edge1(EstArgs a) {
   dst[1] = l;
 }
 
-// Pass 2 for the edge keys, after est_pass2: the probabilities of the tile's
-// 64 rows x 64 keys (zero outside the edge keys) in LDS, then the vertical
-// scores of the edge keys (rows in ascending order) and the diagonal sums of
-// the tile's four 32 x 32 blocks, added to the records pass 2 wrote (same
-// record layout: blocks (0,0) + (1,1) in record 2t + 1 slot 0, block (row 1,
-// key 0) in record 2t slot 1, block (row 0, key 1) in record 2t + 2 slot 0).
+// Pass 2 for the edge keys, after est_pass2 and est_slash_fix: the
+// probabilities of the tile's 64 rows x 64 keys (zero outside the edge keys)
+// in LDS, then the vertical scores of the edge keys (rows in ascending order)
+// and, per offset row0 + r - (k0 + n) met in the tile, the sum over its rows
+// (ascending), added to the slash score pass 2 wrote.  One thread per offset,
+// and the edge tiles in ascending order, so the sums are reproducible.
 template <int D>
 __global__ void __launch_bounds__(256) est_edge2(EstArgs a) {
   __shared__ float P[kEstRows][kTileK + 1];
@@ -524,11 +599,10 @@ __global__ void __launch_bounds__(256) est_edge2(EstArgs a) {
   if (!((a.head_mask >> h) & 1)) return;
   const int g = h / a.G;
   const int64_t n_kc = (a.n_ctx + a.period - 1) / a.period;
-  float* drec = a.diag + (int64_t)h * a.n_diag * 2 * 64;
   for (int64_t c = 1; c < n_kc; ++c) {
     int64_t e, e_end;
     if (!edge_tile(a, c, e, e_end)) continue;
-    const int64_t k0 = e / kTileK * kTileK, t = k0 / kTileK;
+    const int64_t k0 = e / kTileK * kTileK;
     for (int x = tid; x < kEstRows * kTileK; x += 256) {
       const int r = x / kTileK, n = x % kTileK;
       const int64_t j = k0 + n, row = a.row0 + r;
@@ -546,52 +620,21 @@ __global__ void __launch_bounds__(256) est_edge2(EstArgs a) {
         a.vscore[(int64_t)h * a.n_ctx + j] = v;
       }
     }
-    // diagonal d = m - n' of a 32 x 32 block, d in [-31, 31]
-    if (tid < 3 * 63) {
-      const int target = tid / 63, d = tid % 63 - 31;
-      float sum = 0.f;
-      for (int blk = 0; blk < 2; ++blk) {
-        int b, kb;
-        if (target == 0) { b = blk; kb = blk; }           // (0,0) + (1,1)
-        else if (target == 1) { if (blk) break; b = 1; kb = 0; }
-        else { if (blk) break; b = 0; kb = 1; }
-        for (int mm = 0; mm < 32; ++mm) {
-          const int n = mm - d;
-          if (n >= 0 && n < 32) sum += P[32 * b + mm][32 * kb + n];
+    // offset o = row0 - k0 + dr, dr = r - n in [-63, 63]
+    if (tid < 2 * kTileK - 1) {
+      const int dr = tid - (kTileK - 1);
+      const int64_t o = a.row0 - k0 + dr;
+      if (o >= 0 && o < a.n_ctx) {
+        float sum = 0.f;
+        for (int r = 0; r < kEstRows; ++r) {
+          const int n = r - dr;
+          if (n >= 0 && n < kTileK) sum += P[r][n];
         }
+        a.sscore[(int64_t)h * a.n_ctx + o] += sum;
       }
-      const int64_t rec = target == 0 ? ((2 * t + 1) * 2 + 0)
-                        : target == 1 ? ((2 * t) * 2 + 1) : ((2 * t + 2) * 2 + 0);
-      drec[rec * 64 + d + 31] += sum;
     }
     __syncthreads();
   }
-}
-
-// s_o = sum over the diagonal records covering offset o (fixed order).
-__global__ void est_slash_reduce(EstArgs a) {
-  const int h = blockIdx.y;
-  const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (!((a.head_mask >> h) & 1) || o >= a.n_ctx) return;
-  const float* drec = a.diag + (int64_t)h * a.n_diag * 2 * 64;
-  // o = row0 - 32 e + d, |d| <= 31  =>  e in [(row0 - o - 31) / 32, (row0 - o + 31) / 32]
-  const int64_t num = a.row0 - o;
-  const int64_t lo = num - 31;
-  const int64_t e_lo = lo >= 0 ? lo / 32 : -((-lo + 31) / 32);  // floor(lo / 32)
-  float s = 0.f;
-  for (int64_t e = e_lo; e <= e_lo + 2; ++e) {
-    if (e < -1 || e > 2 * a.n_tiles - 1) continue;
-    const int64_t d = o - a.row0 + 32 * e;
-    if (d < -31 || d > 31) continue;
-    const float* rec = drec + (e + 1) * 2 * 64;
-    if ((e & 1) == 0) {
-      s += rec[d + 31];
-    } else {
-      if ((e - 1) / 2 >= 0 && e >= 1) s += rec[d + 31];                 // slot 0 (tile (e-1)/2)
-      if ((e + 1) / 2 < a.n_tiles) s += rec[64 + d + 31];              // slot 1 (tile (e+1)/2)
-    }
-  }
-  a.sscore[(int64_t)h * a.n_ctx + o] = s;
 }
 
 }  // namespace
@@ -611,8 +654,8 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
   cur += L.vscore;
   float* ss_ws = reinterpret_cast<float*>(cur);
   cur += L.sscore;
-  float* diag = reinterpret_cast<float*>(cur);
-  cur += L.diag;
+  float* bnd = reinterpret_cast<float*>(cur);
+  cur += L.bnd;
   void* topk_ws = cur;
   float* vsc = vscore ? vscore : vs_ws;
   float* ssc = sscore ? sscore : ss_ws;
@@ -649,8 +692,7 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
     a.lse2 = lse2;
     a.vscore = vsc;
     a.sscore = ssc;
-    a.diag = diag;
-    a.n_diag = L.n_diag;
+    a.bnd = bnd;
     a.head_mask = hs.mask;
     // padding rows of the estimate Q (rows >= n_rows) never reach a result
     // but must be finite: clear the buffer (a kernel, not a memset node)
@@ -673,23 +715,25 @@ int run_estimate(const lcsr_problem_t& p, int32_t last_q, const HeadSet& hs,
       rc = check_launch("estimate edge pass 1");
       if (rc) return rc;
     }
-    hipLaunchKernelGGL(est_combine, dim3(p.n_heads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(est_combine, dim3(kEstRows / 4, p.n_heads), dim3(256), 0, s, a);
     rc = check_launch("estimate combine");
     if (rc) return rc;
     if (p.head_dim == 128) hipLaunchKernelGGL(est_pass2<128>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(est_pass2<64>, grid, block, 0, s, a);
     rc = check_launch("estimate pass 2");
     if (rc) return rc;
+    if (a.n_split > 1) {
+      hipLaunchKernelGGL(est_slash_fix, dim3((unsigned)((a.n_split + 7) / 8), p.n_heads),
+                         dim3(256), 0, s, a);
+      rc = check_launch("estimate slash boundaries");
+      if (rc) return rc;
+    }
     if (edges) {
       if (p.head_dim == 128) hipLaunchKernelGGL(est_edge2<128>, dim3(p.n_heads), dim3(256), 0, s, a);
       else hipLaunchKernelGGL(est_edge2<64>, dim3(p.n_heads), dim3(256), 0, s, a);
       rc = check_launch("estimate edge pass 2");
       if (rc) return rc;
     }
-    hipLaunchKernelGGL(est_slash_reduce, dim3((unsigned)((c1 + 255) / 256), p.n_heads),
-                       dim3(256), 0, s, a);
-    rc = check_launch("estimate slash reduce");
-    if (rc) return rc;
   }
   TopkRequest r{};
   r.scores[0] = vsc;

@@ -166,8 +166,8 @@ namespace lcsr {
 // ---------------------------------------------------------------- workspace
 // Byte layout of the caller's workspace for each call (host side).
 struct EstimateLayout {
-  int64_t n_ctx, n_tiles, n_kc, n_split, n_diag;
-  size_t q_est, part, lse, vscore, sscore, diag, topk, total;
+  int64_t n_ctx, n_tiles, n_kc, n_split;
+  size_t q_est, part, lse, vscore, sscore, bnd, topk, total;
 };
 struct AttnLayout {
   int64_t n_ctx, n_words, n_var;

@@ -252,14 +252,31 @@ __global__ void __launch_bounds__(kThreads) topk_compact(TopkArgs a) {
     return;
   }
   const uint32_t T = st[0], need_eq = st[2];
-  // selected keys and ties at T in the slices before this one
+  // selected keys and ties at T in the slices before this one: keys above T
+  // plus the first need_eq ties (integer sums over the slices, in parallel)
   const uint32_t* cnts = a.counts + row * a.n_slices * 2;
-  uint32_t base = 0, eq_before = 0;
-  for (int u = 0; u < slice; ++u) {
-    const uint32_t g = cnts[u * 2], e = cnts[u * 2 + 1];
-    base += g + take_eq(need_eq, eq_before, e);
-    eq_before += e;
+  uint32_t gs = 0, es = 0;
+  for (int u = tid; u < slice; u += kThreads) {
+    gs += cnts[u * 2];
+    es += cnts[u * 2 + 1];
   }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    gs += __shfl_xor(gs, d);
+    es += __shfl_xor(es, d);
+  }
+  __shared__ uint32_t before[kThreads / 64][2];
+  if (lane == 0) {
+    before[w][0] = gs;
+    before[w][1] = es;
+  }
+  __syncthreads();
+  uint32_t g_before = 0, eq_before = 0;
+  for (int u = 0; u < kThreads / 64; ++u) {
+    g_before += before[u][0];
+    eq_before += before[u][1];
+  }
+  uint32_t base = g_before + (eq_before < need_eq ? eq_before : need_eq);
   constexpr int kPerWave = kSlice / (kThreads / 64);
   constexpr int kSteps = kPerWave / 64;
   const int64_t w0 = s0 + (int64_t)w * kPerWave;
