@@ -344,15 +344,27 @@ __global__ void __launch_bounds__(256) est_combine(EstArgs a) {
 __device__ __forceinline__ void diag_pair(const float (&x)[16], float& pos_out, float& neg_out) {
   const int lane = threadIdx.x & 63;
   const int t = lane & 31, half = lane >> 5;
-  float pos = 0.f, neg = 0.f;  // diagonal t, diagonal t - 32
+  // The rows m of registers r = 0..15 ascend, so the values of diagonal
+  // t - 32 (m < t) come first: one running sum, saved as neg and restarted
+  // at the first register with m >= t, adds each diagonal's values in
+  // register order.
+  float acc = 0.f, neg = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+    const int mp = r ? 8 * ((r - 1) >> 2) + 4 * half + ((r - 1) & 3) : -1;
     const int src = (half << 5) | ((m - t) & 31);
     const float v =
         __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x[r])));
-    if (m >= t) pos += v;
-    else neg += v;
+    const bool start = m >= t && mp < t;  // first register of diagonal t
+    neg = start ? acc : neg;
+    acc = (start ? 0.f : acc) + v;
+  }
+  // every row below t: all values belong to diagonal t - 32
+  float pos = acc;
+  if (8 * 3 + 4 * half + 3 < t) {
+    neg = acc;
+    pos = 0.f;
   }
   const float pos_o = __shfl_xor(pos, 32), neg_o = __shfl_xor(neg, 32);
   pos_out = half ? pos_o + pos : pos + pos_o;
