@@ -253,6 +253,35 @@ def test_estimate_period_208():
     score_compare(host64(ss[0]), rs, "slash")
 
 
+def test_estimate_multi_tile_splits_with_dca_edges():
+    """Estimate scores where every key split holds several tiles (the slash
+    sums carried from tile to tile and added across split boundaries) and the
+    DCA period (S 2800, four query heads, one per KV head) puts chunk edges
+    inside tiles; every head, every score, and the selection."""
+    cfg = scaled(TINY, n_heads=4, n_kv_heads=4, seq_len=40000, dca_chunk=3000,
+                 dca_local=200, n_vert=96, n_slash=160)
+    n = cfg.seq_len
+    q, k, v = synth.generate(cfg, DEV)
+    layer = _tiny_layer(cfg, q, k, v, n)
+    c0 = 39040  # a multiple of 64, as DCA chunk starts must be
+    vs = torch.empty(4, n, device=DEV)
+    ss = torch.empty(4, n, device=DEV)
+    L.vs_pattern_estimate(q[:, c0:n], layer.k_cache[:, :n], c0, layer.rope, layer.dca,
+                          layer.sm_scale, [96] * 4, [160] * 4, layer.pattern, vert_score=vs,
+                          slash_score=ss)
+    qo, ko, _ = oracle_inputs(q, k, v)
+    rows = oracle.estimate.estimate_rows(c0, n - c0, 64)
+    verts, slashes = layer.pattern.lists()
+    for h in range(4):
+        ctx = oracle.KeyContext(ko[h], None, oracle_freqs(cfg), cfg.dca_chunk, cfg.dca_local)
+        rv, rs = oracle.estimate_scores(qo[h, rows], rows, ctx, n, layer.sm_scale)
+        score_compare(host64(vs[h]), rv, f"vertical h{h}")
+        score_compare(host64(ss[h]), rs, f"slash h{h}")
+        assert verts[h].tolist() == oracle.select_top(vs[h].cpu().numpy(), 96).tolist()
+        assert slashes[h].tolist() == oracle.select_top(ss[h].cpu().numpy(), 160).tolist()
+        near_tie_check(slashes[h].numpy(), rs, 160, f"slash h{h}")
+
+
 def test_attention_empty_rows_and_bf16_out():
     # no slash 0 and verticals only far ahead: the first rows have empty sets
     _attn_case(TINY, 0, 256, [[200, 201]], [[150, 151]], out_dtype=torch.bfloat16)
