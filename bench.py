@@ -34,7 +34,8 @@ METRIC = ("ms + effective TFLOP/s per 1M-token sparse prefill (one layer); "
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 CSRC = os.path.join(ROOT, "long_context_sparse_rope_amd", "csrc")
-# sources of the kernels one vs_sparse_attn_prefill call launches
+# sources of the kernels one vs_sparse_attn_prefill call launches, and the
+# build script that holds their compiler flags
 ATTN_SOURCES = ("attn.hip", "rope.hip", "lcsr_internal.h")
 
 
@@ -43,6 +44,8 @@ def attn_source_digest():
     for f in ATTN_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(os.path.dirname(CSRC), "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

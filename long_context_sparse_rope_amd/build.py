@@ -23,6 +23,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops"]
+# Per-source extras.  The attention kernels take LLVM's memory-clause
+# scheduling strategy (AMDGPU backend): it groups the LDS fragment reads of
+# the consumer waves and measured about 1% less attention time per 1M-token
+# step than the default strategy (same registers, same results).
+EXTRA_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def sources():
@@ -31,7 +36,8 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + COMMON + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([HIPCC] + COMMON + HIP_FLAGS + EXTRA_FLAGS.get(src, []) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
