@@ -679,7 +679,11 @@ __device__ __forceinline__ Tile read_desc(const int4* slot) {
 // between them; wave NW walks the tiles and publishes a descriptor per tile
 // four tiles ahead.  Tile i sits in stage i mod 4; its loads are issued three
 // tiles ahead.  One barrier per tile.
-template <int D, int NW>
+// kPair: one barrier per pair of tiles (sparse calls: the heads' uneven
+// work per tile evens out over two); else one per tile, with the second
+// wave of each SIMD a whole tile late (dense calls: every head has the same
+// work, and the de-phasing is worth more).
+template <int D, int NW, bool kPair>
 __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
   using B = Buf<D>;
   constexpr int kPerTile = Issue<D>::kPerTile;  // walker loads per tile
@@ -762,21 +766,44 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
       if (ahead.n > 0) wait_vm<kPerTile>();
       else wait_vm<0>();
     };
-    for (int j = 0; j < 4; ++j) publish(j);
-    {
-      const Tile ta = read_desc(&ring[0]), tb = read_desc(&ring[1]);
-      issue(ta, 0);
-      issue(tb, 1);
-      land(tb);
-    }
-    ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
-    for (int i = 0; n_tiles < 0 || i < n_tiles; ++i) {
-      // the consumers multiply tile i
-      const Tile tn = read_desc(&ring[(i + 2) & (kRing - 1)]);
-      issue(tn, i + 2);
-      publish(i + 4);
-      land(tn);
-      ring_barrier();  // tile i done, tile i + 1 in its stage
+    if constexpr (kPair) {
+      for (int j = 0; j < 6; ++j) publish(j);
+      {
+        const Tile ta = read_desc(&ring[0]), tb = read_desc(&ring[1]);
+        issue(ta, 0);
+        issue(tb, 1);
+        wait_vm<0>();
+      }
+      ring_barrier();  // descriptors 0 .. 5 published, tiles 0 and 1 in their stages
+      for (int j = 0; n_tiles < 0 || 2 * j < n_tiles; ++j) {
+        // the consumers multiply tiles 2j and 2j + 1; tiles 2j + 2 and 2j + 3
+        // go into the stages of step j - 1, whose products are done
+        const Tile ta = read_desc(&ring[(2 * j + 2) & (kRing - 1)]);
+        const Tile tb = read_desc(&ring[(2 * j + 3) & (kRing - 1)]);
+        issue(ta, 2 * j + 2);
+        issue(tb, 2 * j + 3);
+        publish(2 * j + 6);
+        publish(2 * j + 7);
+        wait_vm<0>();
+        ring_barrier();  // tiles 2j, 2j + 1 done; 2j + 2, 2j + 3 in their stages
+      }
+    } else {
+      for (int j = 0; j < 4; ++j) publish(j);
+      {
+        const Tile ta = read_desc(&ring[0]), tb = read_desc(&ring[1]);
+        issue(ta, 0);
+        issue(tb, 1);
+        land(tb);
+      }
+      ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
+      for (int i = 0; n_tiles < 0 || i < n_tiles; ++i) {
+        // the consumers multiply tile i
+        const Tile tn = read_desc(&ring[(i + 2) & (kRing - 1)]);
+        issue(tn, i + 2);
+        publish(i + 4);
+        land(tn);
+        ring_barrier();  // tile i done, tile i + 1 in its stage
+      }
     }
   } else {
     // ---------------- consumers: wave w multiplies for head h
@@ -800,94 +827,182 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         C = load_win(colb, tt.ks);
       }
     };
-    ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
-    Tile t0 = read_desc(&ring[0]);
-    // DCA relation of a tile (the same for every wave and row: the period is
-    // a multiple of 32, so a 32-row block lies inside one DCA chunk)
-    auto var_of = [&](const Tile& tt) {
-      const int32_t rel = qchunk - tt.kchunk;
-      return a.n_var == 1 ? 0 : (rel >= 2 ? 2 : rel);
-    };
-    Win W0{}, C0{}, W1{}, C1{};
-    load_windows(t0, W0, C0);
-    int i = 0;
-    // The second wave on a SIMD (waves 4 .. 6 share SIMDs with waves 0 .. 2)
-    // multiplies each tile's PV product one step late, during its next
-    // tile's softmax: the two waves of a SIMD then alternate between the
-    // matrix cores and the vector ALUs instead of contending for the same
-    // unit at the same time.  The previous tile's stage is intact during the
-    // step (it is refilled after the step's barrier).
-    bf16x8 pf_prev[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) pf_prev[s] = (bf16x8){};
-    bool pa0 = false, pa1 = false;
-    const char* bc_prev = stage[0];
-    // one step per tile (tile i in stage i mod 4), then the step's barrier
-    auto step = [&](auto lag) {
-      constexpr bool kLag = decltype(lag)::value;
-      const Tile t1 = read_desc(&ring[(i + 1) & (kRing - 1)]);
-      const char* bc = stage[i & (kStages - 1)];
-      // this wave's key mask for the tile; act: any pair, full: all 64 x 32
-      uint64_t mword = 0;
-      if (live && t0.wave < 0)
-        mword = span_mask(t0, W0, C0, i0, my_row, lane & 31);
-      else if (live && t0.wave == w)
-        mword = gather_mask(t0, reinterpret_cast<const int32_t*>(bc + B::kKeyOff), my_row);
-      const bool row_ok = my_row <= rlast;
-      if (!row_ok) mword = 0;
-      const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
-      const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
-      const bool act = act0 || act1;
-      const bool masked = __ballot(mword == ~0ull) != ~0ull;
-      // the next tile's windows are requested during this tile's softmax
-      bf16x8 pf[4];
-      if constexpr (kLag) {
-        wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf,
-                       [&] { wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1); },
-                       [&] { load_windows(t1, W1, C1); });
-#pragma unroll
-        for (int s = 0; s < 4; ++s) pf_prev[s] = pf[s];
-        pa0 = act0;
-        pa1 = act1;
-        bc_prev = bc;
-      } else {
-        wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
-                       [&] { load_windows(t1, W1, C1); });
-        wave_pv<D>(bc, lc, st, pf, act0, act1);
-      }
-      if (act) {
-        ++exec_tiles;
-        if (half == 0 && row_ok) sel += (uint32_t)__popcll(mword);
-      }
-      // tile i done, tile i + 1 in its stage; a late wave's reads of the
-      // previous stage retire before the barrier (that stage is refilled
-      // right after it)
-      if constexpr (kLag) ring_barrier();
-      else step_barrier();
-      t0 = t1;
-      W0 = W1;
-      C0 = C1;
-      ++i;
-    };
-    // tiles come in runs of one DCA relation (keys ascend, so it changes at
-    // most twice per walk); the query variant is loaded once per run, outside
-    // the inner loop
-    auto run = [&](auto lag) {
-      while (t0.n > 0) {
-        const int var = var_of(t0);
-        if (live) {
+    if constexpr (kPair) {
+      ring_barrier();  // descriptors 0 .. 5 published, tiles 0 and 1 in their stages
+      // DCA relation of a tile (the same for every wave and row: the period is
+      // a multiple of 32, so a 32-row block lies inside one DCA chunk)
+      auto var_of = [&](const Tile& tt) {
+        const int32_t rel = qchunk - tt.kchunk;
+        return a.n_var == 1 ? 0 : (rel >= 2 ? 2 : rel);
+      };
+      // Tiles come in runs of one DCA relation (keys ascend, so it changes at
+      // most twice per walk): the query variant is reloaded only when it
+      // changes.
+      int cur_var = -1;
+      auto use_var = [&](const Tile& tt) {
+        const int var = var_of(tt);
+        if (live && var != cur_var) {
           load_q<D>(a, h, i0, var, st);
           wait_vm<0>();
         }
-        do {
-          step(lag);
-        } while (t0.n > 0 && var_of(t0) == var);
-      }
-      // a late wave's last PV product (the last stage is not refilled)
-      if constexpr (decltype(lag)::value) wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1);
-    };
-    if (w >= 4) run(std::true_type{});
-    else run(std::false_type{});
+        cur_var = var;
+      };
+      // This wave's key mask for a tile: pairs (row, key) of its head.
+      auto mask_of = [&](const Tile& tt, const Win& W, const Win& C, const char* bc) {
+        uint64_t m = 0;
+        if (live && tt.wave < 0)
+          m = span_mask(tt, W, C, i0, my_row, lane & 31);
+        else if (live && tt.wave == w)
+          m = gather_mask(tt, reinterpret_cast<const int32_t*>(bc + B::kKeyOff), my_row);
+        return my_row <= rlast ? m : 0ull;
+      };
+      // Scores of one tile into pf; `mid` runs once its QK products are
+      // issued, `next` requests the windows of the tile after it.
+      auto scores = [&](const Tile& tt, const Win& W, const Win& C, const char* bc,
+                        bf16x8 (&pf)[4], bool& act0, bool& act1, auto&& mid, auto&& next) {
+        use_var(tt);
+        const uint64_t mword = mask_of(tt, W, C, bc);
+        act0 = __ballot((uint32_t)mword != 0u) != 0;
+        act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+        const bool masked = __ballot(mword == ~0ull) != ~0ull;
+        wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, mid, next);
+        if (act0 || act1) {
+          ++exec_tiles;
+          if (half == 0) sel += (uint32_t)__popcll(mword);
+        }
+      };
+      // One step per pair of tiles (tile i in stage i mod 4), then one barrier:
+      // the step lasts as long as its slowest wave's two tiles, which evens out
+      // the heads' work better than a barrier per tile.  The second wave on a
+      // SIMD (waves 4 .. 6 share SIMDs with waves 0 .. 2) multiplies the first
+      // tile's PV product during the second tile's softmax, so the two waves of
+      // a SIMD alternate between the matrix cores and the vector ALUs.
+      auto run = [&](auto lag) {
+        constexpr bool kLate = decltype(lag)::value;
+        Tile ta = read_desc(&ring[0]);
+        Win W0{}, C0{}, W1{}, C1{};
+        if (ta.n > 0 && ta.wave < 0 && live) {
+          W0 = load_win(offb, i0 - ta.ks - 63);
+          C0 = load_win(colb, ta.ks);
+        }
+        for (int i = 0; ta.n > 0; i += 2) {
+          const Tile tb = read_desc(&ring[(i + 1) & (kRing - 1)]);
+          const Tile tc = read_desc(&ring[(i + 2) & (kRing - 1)]);
+          const char* ba = stage[i & (kStages - 1)];
+          const char* bb = stage[(i + 1) & (kStages - 1)];
+          bf16x8 pa[4];
+          bool a0, a1;
+          scores(ta, W0, C0, ba, pa, a0, a1, [] {}, [&] { load_windows(tb, W1, C1); });
+          if (!kLate || tb.n == 0) wave_pv<D>(ba, lc, st, pa, a0, a1);
+          if (tb.n > 0) {
+            bf16x8 pb[4];
+            bool b0, b1;
+            if constexpr (kLate)
+              scores(tb, W1, C1, bb, pb, b0, b1, [&] { wave_pv<D>(ba, lc, st, pa, a0, a1); },
+                     [&] { load_windows(tc, W0, C0); });
+            else
+              scores(tb, W1, C1, bb, pb, b0, b1, [] {}, [&] { load_windows(tc, W0, C0); });
+            wave_pv<D>(bb, lc, st, pb, b0, b1);
+          }
+          // tiles i, i + 1 done; both stages are refilled right after the
+          // barrier, and every LDS read of this step has been consumed by a
+          // product or a mask by then
+          step_barrier();
+          ta = tc;
+        }
+      };
+      if (w >= 4) run(std::true_type{});
+      else run(std::false_type{});
+    } else {
+      ring_barrier();  // descriptors 0 .. 3 published, tile 0 in its stage
+      Tile t0 = read_desc(&ring[0]);
+      // DCA relation of a tile (the same for every wave and row: the period is
+      // a multiple of 32, so a 32-row block lies inside one DCA chunk)
+      auto var_of = [&](const Tile& tt) {
+        const int32_t rel = qchunk - tt.kchunk;
+        return a.n_var == 1 ? 0 : (rel >= 2 ? 2 : rel);
+      };
+      Win W0{}, C0{}, W1{}, C1{};
+      load_windows(t0, W0, C0);
+      int i = 0;
+      // The second wave on a SIMD (waves 4 .. 6 share SIMDs with waves 0 .. 2)
+      // multiplies each tile's PV product one step late, during its next
+      // tile's softmax: the two waves of a SIMD then alternate between the
+      // matrix cores and the vector ALUs instead of contending for the same
+      // unit at the same time.  The previous tile's stage is intact during the
+      // step (it is refilled after the step's barrier).
+      bf16x8 pf_prev[4];
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) pf_prev[s] = (bf16x8){};
+      bool pa0 = false, pa1 = false;
+      const char* bc_prev = stage[0];
+      // one step per tile (tile i in stage i mod 4), then the step's barrier
+      auto step = [&](auto lag) {
+        constexpr bool kLag = decltype(lag)::value;
+        const Tile t1 = read_desc(&ring[(i + 1) & (kRing - 1)]);
+        const char* bc = stage[i & (kStages - 1)];
+        // this wave's key mask for the tile; act: any pair, full: all 64 x 32
+        uint64_t mword = 0;
+        if (live && t0.wave < 0)
+          mword = span_mask(t0, W0, C0, i0, my_row, lane & 31);
+        else if (live && t0.wave == w)
+          mword = gather_mask(t0, reinterpret_cast<const int32_t*>(bc + B::kKeyOff), my_row);
+        const bool row_ok = my_row <= rlast;
+        if (!row_ok) mword = 0;
+        const bool act0 = __ballot((uint32_t)mword != 0u) != 0;
+        const bool act1 = __ballot((uint32_t)(mword >> 32) != 0u) != 0;
+        const bool act = act0 || act1;
+        const bool masked = __ballot(mword == ~0ull) != ~0ull;
+        // the next tile's windows are requested during this tile's softmax
+        bf16x8 pf[4];
+        if constexpr (kLag) {
+          wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf,
+                         [&] { wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1); },
+                         [&] { load_windows(t1, W1, C1); });
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) pf_prev[s] = pf[s];
+          pa0 = act0;
+          pa1 = act1;
+          bc_prev = bc;
+        } else {
+          wave_scores<D>(a.scale_log2, bc, lc, st, act0, act1, masked, mword, half, pf, [] {},
+                         [&] { load_windows(t1, W1, C1); });
+          wave_pv<D>(bc, lc, st, pf, act0, act1);
+        }
+        if (act) {
+          ++exec_tiles;
+          if (half == 0 && row_ok) sel += (uint32_t)__popcll(mword);
+        }
+        // tile i done, tile i + 1 in its stage; a late wave's reads of the
+        // previous stage retire before the barrier (that stage is refilled
+        // right after it)
+        if constexpr (kLag) ring_barrier();
+        else step_barrier();
+        t0 = t1;
+        W0 = W1;
+        C0 = C1;
+        ++i;
+      };
+      // tiles come in runs of one DCA relation (keys ascend, so it changes at
+      // most twice per walk); the query variant is loaded once per run, outside
+      // the inner loop
+      auto run = [&](auto lag) {
+        while (t0.n > 0) {
+          const int var = var_of(t0);
+          if (live) {
+            load_q<D>(a, h, i0, var, st);
+            wait_vm<0>();
+          }
+          do {
+            step(lag);
+          } while (t0.n > 0 && var_of(t0) == var);
+        }
+        // a late wave's last PV product (the last stage is not refilled)
+        if constexpr (decltype(lag)::value) wave_pv<D>(bc_prev, lc, st, pf_prev, pa0, pa1);
+      };
+      if (w >= 4) run(std::true_type{});
+      else run(std::false_type{});
+    }
 
     // ---------------- epilogue
     if (live) {
@@ -1178,8 +1293,12 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
 
 template <int D, int NW>
 int launch_attn(const AttnArgs& a, int64_t grid, size_t dyn_lds, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * (NW + 1)), dyn_lds, s,
-                     a);
+  if (a.dense)
+    hipLaunchKernelGGL((attn_kernel<D, NW, false>), dim3((unsigned)grid), dim3(64 * (NW + 1)),
+                       dyn_lds, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, NW, true>), dim3((unsigned)grid), dim3(64 * (NW + 1)),
+                       dyn_lds, s, a);
   return check_launch("sparse attention");
 }
 
