@@ -780,9 +780,11 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         // go into the stages of step j - 1, whose products are done
         const Tile ta = read_desc(&ring[(2 * j + 2) & (kRing - 1)]);
         const Tile tb = read_desc(&ring[(2 * j + 3) & (kRing - 1)]);
+        // the second tile's loads go out after the first walk step, so that
+        // fewer loads are in flight at once
         issue(ta, 2 * j + 2);
-        issue(tb, 2 * j + 3);
         publish(2 * j + 6);
+        issue(tb, 2 * j + 3);
         publish(2 * j + 7);
         wait_vm<0>();
         ring_barrier();  // tiles 2j, 2j + 1 done; 2j + 2, 2j + 3 in their stages
