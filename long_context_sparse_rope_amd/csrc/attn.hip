@@ -746,9 +746,11 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
       if (!e && n_tiles < 0) n_tiles = j;
       if (lane == 0) ring[j & (kRing - 1)] = e ? pack_desc(t) : make_int4(0, 0, 0, 0);
     };
-    // K / V of every tile: tile i + 2 is loaded while tile i is multiplied
-    // (its stage last held tile i - 2); at most two tiles are in flight, so
-    // the vmcnt counter covers them
+    // K / V of every tile, issued ahead of the step that multiplies it (one
+    // tile per step: tile i + 2 while tile i is multiplied, into the stage of
+    // tile i - 2; pairs: tiles 2j + 2, 2j + 3 during step j, into the stages
+    // of step j - 1).  Two tiles are 66 loads: past the 63 the vmcnt counter
+    // holds, the wave's next load issue waits for the oldest to return.
     const char* kg = reinterpret_cast<const char*>(a.k + (int64_t)g * a.kv_sh);
     const char* vg = reinterpret_cast<const char*>(a.v + (int64_t)g * a.kv_sh);
     const uint32_t kvst_b = (uint32_t)(a.kv_st * 2);
