@@ -1348,8 +1348,9 @@ constexpr int kDecStages = 5;
 // Workgroup: waves 0 and 1 multiply, wave 0 the first and wave 1 the second
 // 32-key half of every tile, each with an online softmax state of its own;
 // wave 2 loads the K tiles and wave 3 the V tiles of the key range
-// (direct-to-LDS, 16 loads per tile each, so each keeps four tiles in flight
-// under the 63-load vmcnt limit).  A stage holds K then V of one tile (no key
+// (direct-to-LDS, 16 loads per tile each; four tiles in flight are 64 loads,
+// one past what the vmcnt counter holds, so the last issue waits for the
+// oldest load to return).  A stage holds K then V of one tile (no key
 // list: 32 KB at D 128, so five stages fill the 160 KB of LDS).  Tile i of
 // the range sits in stage i mod 5; at barrier i tile i has landed and the
 // products of tile i - 1 are done, so tile i + 4 then refills that stage.
