@@ -157,8 +157,8 @@ def parallel_map(fn, arg_list, workers=12):
     the workers run the numpy oracle and never touch the GPU), results in
     order.  Large read-only state (key contexts) must be built before the
     call; the workers inherit it instead of receiving it.  At most 12
-    workers: with the parent that keeps the process count on the GPU machine
-    within its limit.  They end with os._exit (multiprocessing's own), so no
+    workers, which with the parent keeps the number of processes on the
+    machine modest.  They end with os._exit (multiprocessing's own), so no
     GPU runtime teardown runs in them."""
     import multiprocessing as mp
     import os
