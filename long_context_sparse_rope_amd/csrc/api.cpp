@@ -89,6 +89,8 @@ AttnLayout attn_layout(const lcsr_problem_t& p, int32_t max_vert, int32_t max_sl
   off += align256((size_t)H * 4);
   L.o_union = off;
   off += attention ? align256((size_t)L.n_wgg * L.n_rb * L.ubw * 4) : 0;
+  L.o_first = off;  // 4 bits per granule: first pair key of each marked granule
+  off += attention ? align256((size_t)L.n_wgg * L.n_rb * L.ubw * 16) : 0;
   L.o_vl = off;
   off += attention ? align256((size_t)H * L.n_rb * max_vert * 4) : 0;
   L.o_vl_cnt = off;

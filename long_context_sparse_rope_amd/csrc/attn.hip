@@ -65,6 +65,7 @@ struct AttnArgs {
   const uint32_t* __restrict__ col_bits;  // [H][n_words]
   int64_t n_words;
   const uint32_t* __restrict__ ubits;     // [n_wgg][n_rb][ubw] granule bitmaps
+  const uint32_t* __restrict__ first;     // [n_wgg][n_rb][4 ubw] first pair key per granule, or null
   int64_t ubw;
   const int32_t* __restrict__ vl;         // [H][n_rb][max_vert] leftover verticals
   const int32_t* __restrict__ vl_cnt;     // [H][n_rb]
@@ -137,16 +138,17 @@ __device__ __forceinline__ uint64_t bitrev64(uint64_t x) {
   return ((uint64_t)lo << 32) | hi;
 }
 
-// One 64-key tile.  Span tiles (wave < 0): keys [ks, ks + n), granule bits of
-// its four granules in `gran`.  Gathered tiles: wave `wave` only (its head's
-// leftover list), keys list[ks .. ks + n).
+// One 64-key tile.  Span tiles (wave < 0): keys [ks, ks + n), marked bits of
+// granules ks/16 .. ks/16 + 4 in `gran` (ks need not be a granule start).
+// Gathered tiles: wave `wave` only (its head's leftover list), keys
+// list[ks .. ks + n).
 struct Tile {
   int32_t ks;      // first key (span) / first slot (gather)
   int32_t n;
   int32_t wave;    // -1: span tile; else the wave whose head owns the list
   int32_t kchunk;  // DCA chunk of the tile's keys
   int32_t kmax;    // last key
-  int32_t gran;    // span tile: marked bits of granules ks/16 .. ks/16 + 3
+  int32_t gran;    // span tile: marked bits of granules ks/16 .. ks/16 + 4
 };
 
 // The walk over one workgroup's tiles, identical in every wave: marked
@@ -165,38 +167,60 @@ struct Walk {
 
 struct WalkConst {
   int32_t rlast, period, glast, nwords, n_here, rb, h_first;
-  const uint32_t* ub;   // LDS bitmap
+  const uint32_t* ub;     // LDS bitmap
+  const uint32_t* first;  // first pair key of each granule (4 bits), or null
 };
 
 __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c, Walk& w,
-                                          uint32_t& cw, Tile& t) {
+                                          uint32_t& cw, uint4& nf, Tile& t) {
   const int lane = threadIdx.x & 63;
   if (w.phase == 0) {
-    // first granule at or after pos (pos is a multiple of 16 except after
-    // the tile that ends the row block's keys at rlast + 1)
-    int32_t g = (w.pos + kGranule - 1) / kGranule;
-    bool found = false;
-    while (g <= c.glast) {
-      const int32_t ch = g / kGranPerChunk;
-      if (ch != w.chunk) {
-        const int32_t wi = ch * 64 + lane;
-        cw = wi < c.nwords ? c.ub[wi] : 0u;
-        w.nz = __ballot(cw != 0u);
-        w.chunk = ch;
+    // Next tile: 64 keys from the first marked granule that holds keys >=
+    // pos (the granule holding pos itself when a tile ended inside it),
+    // starting at pos or at the granule's first key that a pair of the row
+    // block reaches, whichever is later; cut at a DCA chunk edge and after
+    // rlast.  No key a pair reaches is skipped: the granules in between are
+    // unmarked, and the granule's keys before its first reached key have no
+    // pair.  Starting there rather than at the granule's first key leaves
+    // fewer key halves with pairs (an isolated diagonal of a 32-row block
+    // then often fits one half).
+    const int32_t p = w.pos;
+    int32_t g = p / kGranule;
+    {
+      bool found = false;
+      while (g <= c.glast) {
+        const int32_t ch = g / kGranPerChunk;
+        if (ch != w.chunk) {
+          const int32_t wi = ch * 64 + lane;
+          cw = wi < c.nwords ? c.ub[wi] : 0u;
+          w.nz = __ballot(cw != 0u);
+          w.chunk = ch;
+          // the chunk's first-key nibbles, 32 granules per lane (a vector
+          // load: its first use waits for the tile loads in flight too, once
+          // per 2,048 granules)
+          if (c.first)
+            nf = wi < c.nwords ? reinterpret_cast<const uint4*>(c.first)[wi]
+                               : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const int32_t wl = (g >> 5) & 63;
+        const uint32_t word =
+            (uint32_t)__builtin_amdgcn_readlane(cw, wl) & (0xFFFFFFFFu << (g & 31));
+        if (word) {
+          g = (g & ~31) + __builtin_ctz(word);
+          found = true;
+          break;
+        }
+        const uint64_t rest = wl == 63 ? 0ull : (w.nz & (~0ull << (wl + 1)));
+        g = rest ? ch * kGranPerChunk + 32 * __builtin_ctzll(rest) : (ch + 1) * kGranPerChunk;
       }
-      const int32_t wl = (g >> 5) & 63;
-      const uint32_t word =
-          (uint32_t)__builtin_amdgcn_readlane(cw, wl) & (0xFFFFFFFFu << (g & 31));
-      if (word) {
-        g = (g & ~31) + __builtin_ctz(word);
-        found = true;
-        break;
+      int32_t ks = g * kGranule;
+      if (found && c.first) {
+        const int32_t wl = (g >> 5) & 63, sel = (g >> 3) & 3;
+        const uint32_t fw = sel == 0 ? nf.x : (sel == 1 ? nf.y : (sel == 2 ? nf.z : nf.w));
+        ks += (int32_t)(((uint32_t)__builtin_amdgcn_readlane(fw, wl) >> (4 * (g & 7))) & 15u);
       }
-      const uint64_t rest = wl == 63 ? 0ull : (w.nz & (~0ull << (wl + 1)));
-      g = rest ? ch * kGranPerChunk + 32 * __builtin_ctzll(rest) : (ch + 1) * kGranPerChunk;
-    }
-    if (found && g <= c.glast) {
-      const int32_t ks = g * kGranule;
+      if (ks < p) ks = p;
+      if (!found || g > c.glast || ks > c.rlast) goto spans_done;
       int32_t ke = ks + kTileK < c.rlast + 1 ? ks + kTileK : c.rlast + 1;
       if (c.period) {
         while (ks >= w.edge) {
@@ -205,11 +229,11 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c,
         }
         if (ke > w.edge) ke = w.edge;
       }
-      // marked bits of the tile's four granules (they may straddle a word)
+      // marked bits of the five granules from g (they may straddle a word)
       const int32_t wl = (g >> 5) & 63, sh = g & 31;
       // (readlane returns int: shift the word as unsigned)
       uint32_t gb = (uint32_t)__builtin_amdgcn_readlane(cw, wl) >> sh;
-      if (sh > 28) {
+      if (sh > 27) {
         const int32_t nwi = (g >> 5) + 1;
         const uint32_t nx =
             wl < 63 ? (uint32_t)__builtin_amdgcn_readlane(cw, wl + 1)
@@ -221,10 +245,11 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c,
       t.wave = -1;
       t.kchunk = w.kc;
       t.kmax = ke - 1;
-      t.gran = (int32_t)(gb & 15u);
+      t.gran = (int32_t)(gb & 31u);
       w.pos = ke;
       return true;
     }
+  spans_done:
     w.phase = 1;
     w.gw = -1;
     w.s0 = 0;
@@ -597,7 +622,11 @@ __device__ __forceinline__ uint64_t granule_keys(int32_t g) {
 // the 64-bit window shift depends on the lane.
 __device__ __forceinline__ uint64_t span_mask(const Tile& t, const Win& W, const Win& C,
                                               int32_t i0, int32_t row, int r) {
-  const uint64_t gk = granule_keys(t.gran) & low_bits(t.n);
+  // keys of the tile in marked granules (the tile may start inside a granule)
+  const int32_t gs = t.ks & (kGranule - 1);
+  uint64_t gk = granule_keys(t.gran);
+  if (gs) gk = (gk >> gs) | (((t.gran >> 4) & 1) ? (~0ull << (64 - gs)) : 0ull);
+  gk &= low_bits(t.n);
   const int cs = t.ks - C.base;  // 0 .. 31
   const uint64_t c01 = ((uint64_t)C.w1 << 32) | C.w0;
   const uint64_t wcol = (cs ? (c01 >> cs) | ((uint64_t)C.w2 << (64 - cs)) : c01) & gk;
@@ -671,7 +700,7 @@ __device__ __forceinline__ Tile read_desc(const int4* slot) {
   t.kmax = __builtin_amdgcn_readfirstlane(d.w);
   t.n = info & 0xFF;
   t.wave = ((info >> 8) & 0xFF) - 1;
-  t.gran = (info >> 16) & 0xF;
+  t.gran = (info >> 16) & 0x1F;
   return t;
 }
 
@@ -727,7 +756,9 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
   uint32_t exec_tiles = 0, sel = 0;
   if (w == NW) {
     // ---------------- walker: publishes tile j during step j - 4
-    const WalkConst wc{rlast, period, glast, nwords, n_here, rb, h_first, ub_lds};
+    const uint32_t* first =
+        a.first ? a.first + ((int64_t)wgg * a.n_rb + rb) * a.ubw * 4 : nullptr;
+    const WalkConst wc{rlast, period, glast, nwords, n_here, rb, h_first, ub_lds, first};
     Walk walk;
     walk.phase = 0;
     walk.pos = 0;
@@ -739,10 +770,11 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     walk.s0 = 0;
     walk.vcnt = 0;
     uint32_t cw = 0;
+    uint4 nf = make_uint4(0u, 0u, 0u, 0u);
     Tile t;
     int n_tiles = -1;  // known once the walk ends
     auto publish = [&](int j) {
-      const bool e = n_tiles < 0 && next_tile(a, wc, walk, cw, t);
+      const bool e = n_tiles < 0 && next_tile(a, wc, walk, cw, nf, t);
       if (!e && n_tiles < 0) n_tiles = j;
       if (lane == 0) ring[j & (kRing - 1)] = e ? pack_desc(t) : make_int4(0, 0, 0, 0);
     };
@@ -1195,6 +1227,7 @@ struct PlanArgs {
   int32_t n_rb, n_sub, nw, G;
   int64_t ubw;
   uint32_t* ubits;
+  uint32_t* first;  // [n_wgg][n_rb][4 ubw] first pair key of each granule, or null
   int32_t* vl;
   int32_t* vl_cnt;
   int32_t dense;
@@ -1212,9 +1245,25 @@ __device__ __forceinline__ void set_bits(uint32_t* bm, int32_t g0, int32_t g1) {
   }
 }
 
+// Lower nibble g of an LDS nibble array to at most v.
+__device__ __forceinline__ void nib_min(uint32_t* nib, int32_t g, uint32_t v) {
+  uint32_t* w = &nib[g >> 3];
+  const int sh = 4 * (g & 7);
+  uint32_t old = *reinterpret_cast<volatile uint32_t*>(w);
+  while (((old >> sh) & 15u) > v) {
+    const uint32_t prev = atomicCAS(w, old, (old & ~(15u << sh)) | (v << sh));
+    if (prev == old) break;
+    old = prev;
+  }
+}
+
 // Per (row block, KV sub-group): the granules any of its heads' slash runs
 // reach in the row block, and per head the verticals (<= the block's last
-// row) in unmarked granules, ascending.
+// row) in unmarked granules, ascending.  With `first`, also the first key of
+// each marked granule that a pair of the row block reaches, as an offset
+// 0..15 in the granule (4 bits per granule): the start of a run's key span
+// [r0 - ob, rlast - oa] inside the granule, 0 when a span covers the
+// granule's first key, or a vertical of a head in the granule.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   extern __shared__ uint32_t bm[];
   const int rb = blockIdx.x, wgg = blockIdx.y;
@@ -1226,11 +1275,28 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   const int32_t glast = (int32_t)(rlast / kGranule);
   const int32_t nwords = glast / 32 + 1;
   const int tid = threadIdx.x;
+  // with first: [ubw] marked granules, [ubw] granules whose first key a span
+  // covers, [4 ubw] first-key nibbles
+  const bool with_first = a.first != nullptr && !a.dense;
+  uint32_t* cov = bm + a.ubw;
+  uint32_t* nib = bm + 2 * a.ubw;
   for (int i = tid; i < nwords; i += kPlanThreads) bm[i] = 0u;
+  if (with_first) {
+    for (int i = tid; i < nwords; i += kPlanThreads) cov[i] = 0u;
+    for (int i = tid; i < 4 * nwords; i += kPlanThreads) nib[i] = 0xFFFFFFFFu;
+  }
   __syncthreads();
   for (int hh = 0; hh < n_here; ++hh) {
     const int h = h_first + hh;
     if (!((a.head_mask >> h) & 1)) continue;
+    if (with_first) {
+      const int nv = min(a.vert_cnt[h], a.max_vert);
+      const int32_t* vo = a.vert_idx + (int64_t)h * a.max_vert;
+      for (int i = tid; i < nv; i += kPlanThreads) {
+        const int32_t v = vo[i];
+        if (v >= 0 && v <= rlast) nib_min(nib, v / kGranule, (uint32_t)(v % kGranule));
+      }
+    }
     if (a.dense) {
       const uint32_t last = glast % 32 == 31 ? 0xFFFFFFFFu : (1u << (glast % 32 + 1)) - 1u;
       for (int i = tid; i < nwords; i += kPlanThreads)
@@ -1244,11 +1310,29 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
       if (oa > rlast) continue;
       const int64_t lo = r0 - ob > 0 ? r0 - ob : 0, hi = rlast - oa;
       set_bits(bm, (int32_t)(lo / kGranule), (int32_t)(hi / kGranule));
+      if (with_first) {
+        const int32_t gc = (int32_t)((lo + kGranule - 1) / kGranule), gh = (int32_t)(hi / kGranule);
+        if (gc <= gh) set_bits(cov, gc, gh);
+        if (lo % kGranule) nib_min(nib, (int32_t)(lo / kGranule), (uint32_t)(lo % kGranule));
+      }
     }
   }
   __syncthreads();
   uint32_t* dst = a.ubits + ((int64_t)wgg * a.n_rb + rb) * a.ubw;
   for (int i = tid; i < nwords; i += kPlanThreads) dst[i] = bm[i];
+  if (with_first) {
+    uint32_t* fd = a.first + ((int64_t)wgg * a.n_rb + rb) * a.ubw * 4;
+    for (int i = tid; i < 4 * nwords; i += kPlanThreads) {
+      // nibble word i holds granules 8i .. 8i + 7: zero where a span covers
+      // the granule's first key
+      const uint32_t cb = (cov[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      uint32_t clear = 0u;
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if ((cb >> b) & 1u) clear |= 15u << (4 * b);
+      fd[i] = nib[i] & ~clear;
+    }
+  }
   if (a.dense) {
     for (int hh = tid; hh < n_here; hh += kPlanThreads)
       a.vl_cnt[(int64_t)(h_first + hh) * a.n_rb + rb] = 0;
@@ -2100,6 +2184,13 @@ static int64_t attn_period(const DcaParams& d, int64_t n_ctx) {
   return d.period ? std::min<int64_t>(d.period, (n_ctx + kTileK) / kTileK * kTileK) : 0;
 }
 
+// Whether the plan records each granule's first pair key (sparse calls whose
+// plan bitmaps fit 160 KB of LDS six times over; else tiles start at granule
+// starts).
+static bool attn_first_keys(const AttnLayout& L, bool dense) {
+  return !dense && L.ubw * 4 * 6 <= 160 * 1024;
+}
+
 int build_pattern_aux(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t head_mask,
                       bool dense, const AttnLayout& L, char* ws, hipStream_t s) {
   AuxArgs a{};
@@ -2135,12 +2226,13 @@ int build_pattern_aux(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64
   b.G = p.n_heads / p.n_kv_heads;
   b.ubw = L.ubw;
   b.ubits = reinterpret_cast<uint32_t*>(ws + L.o_union);
+  b.first = attn_first_keys(L, dense) ? reinterpret_cast<uint32_t*>(ws + L.o_first) : nullptr;
   b.vl = reinterpret_cast<int32_t*>(ws + L.o_vl);
   b.vl_cnt = reinterpret_cast<int32_t*>(ws + L.o_vl_cnt);
   b.dense = dense ? 1 : 0;
   b.head_mask = head_mask;
   hipLaunchKernelGGL(plan_kernel, dim3((unsigned)L.n_rb, (unsigned)L.n_wgg), dim3(kPlanThreads),
-                     (size_t)L.ubw * 4, s, b);
+                     (size_t)L.ubw * 4 * (b.first ? 6 : 1), s, b);
   return check_launch("attention plan");
 }
 
@@ -2178,6 +2270,8 @@ int run_attention(const lcsr_problem_t& p, const lcsr_pattern_t& pat, uint64_t h
   a.col_bits = reinterpret_cast<const uint32_t*>(ws + L.o_col_bits);
   a.n_words = L.n_words;
   a.ubits = reinterpret_cast<const uint32_t*>(ws + L.o_union);
+  a.first =
+      attn_first_keys(L, dense) ? reinterpret_cast<const uint32_t*>(ws + L.o_first) : nullptr;
   a.ubw = L.ubw;
   a.vl = reinterpret_cast<const int32_t*>(ws + L.o_vl);
   a.vl_cnt = reinterpret_cast<const int32_t*>(ws + L.o_vl_cnt);

@@ -177,7 +177,8 @@ struct AttnLayout {
   int64_t n_wgg;     // KV head x sub-group
   int64_t ubw;       // 32-bit words of one row block's granule bitmap
   bool with_plan;    // attention: union bitmaps and leftover vertical lists
-  size_t o_q_rot, o_off_bits, o_col_bits, o_runs, o_run_cnt, o_union, o_vl, o_vl_cnt, total;
+  size_t o_q_rot, o_off_bits, o_col_bits, o_runs, o_run_cnt, o_union, o_first, o_vl, o_vl_cnt,
+      total;
 };
 struct DecodeLayout {
   int64_t n_ctx, n_tiles, n_var, n_split;
