@@ -138,6 +138,14 @@ __device__ __forceinline__ uint64_t bitrev64(uint64_t x) {
   return ((uint64_t)lo << 32) | hi;
 }
 
+// s_waitcnt vmcnt(N), other counters untouched: at most N of this wave's
+// vector-memory operations are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // One 64-key tile.  Span tiles (wave < 0): keys [ks, ks + n), marked bits of
 // granules ks/16 .. ks/16 + 4 in `gran` (ks need not be a granule start).
 // Gathered tiles: wave `wave` only (its head's leftover list), keys
@@ -196,8 +204,7 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c,
           w.nz = __ballot(cw != 0u);
           w.chunk = ch;
           // the chunk's first-key nibbles, 32 granules per lane (a vector
-          // load: its first use waits for the tile loads in flight too, once
-          // per 2,048 granules)
+          // load, waited for below)
           if (c.first)
             nf = wi < c.nwords ? reinterpret_cast<const uint4*>(c.first)[wi]
                                : make_uint4(0u, 0u, 0u, 0u);
@@ -215,6 +222,13 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c,
       }
       int32_t ks = g * kGranule;
       if (found && c.first) {
+        // vmcnt(0): the nibbles have landed, and so has the tile the walker
+        // issued just before this step.  The walker thus keeps one tile's
+        // loads in flight at a time, the first tile's loads land before the
+        // second's are issued; that halved the HBM traffic of a 1M-token
+        // call (fewer lines evicted from L2 before the other row blocks of
+        // the XCD read them) and was faster than issuing them back to back.
+        wait_vm<0>();
         const int32_t wl = (g >> 5) & 63, sel = (g >> 3) & 3;
         const uint32_t fw = sel == 0 ? nf.x : (sel == 1 ? nf.y : (sel == 2 ? nf.z : nf.w));
         ks += (int32_t)(((uint32_t)__builtin_amdgcn_readlane(fw, wl) >> (4 * (g & 7))) & 15u);
@@ -650,13 +664,6 @@ __device__ __forceinline__ uint64_t gather_mask(const Tile& t, const int32_t* ke
   return low_bits(lo);
 }
 
-// s_waitcnt vmcnt(N), other counters untouched: at most N of this wave's
-// vector-memory operations are still in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  constexpr int n = N > 63 ? 63 : N;
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Workgroup barrier of the tile ring.  It carries no release fence: a fenced
 // barrier waits for every load in flight (vmcnt(0)), which would drain the
@@ -1289,14 +1296,6 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   for (int hh = 0; hh < n_here; ++hh) {
     const int h = h_first + hh;
     if (!((a.head_mask >> h) & 1)) continue;
-    if (with_first) {
-      const int nv = min(a.vert_cnt[h], a.max_vert);
-      const int32_t* vo = a.vert_idx + (int64_t)h * a.max_vert;
-      for (int i = tid; i < nv; i += kPlanThreads) {
-        const int32_t v = vo[i];
-        if (v >= 0 && v <= rlast) nib_min(nib, v / kGranule, (uint32_t)(v % kGranule));
-      }
-    }
     if (a.dense) {
       const uint32_t last = glast % 32 == 31 ? 0xFFFFFFFFu : (1u << (glast % 32 + 1)) - 1u;
       for (int i = tid; i < nwords; i += kPlanThreads)
@@ -1320,19 +1319,6 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   __syncthreads();
   uint32_t* dst = a.ubits + ((int64_t)wgg * a.n_rb + rb) * a.ubw;
   for (int i = tid; i < nwords; i += kPlanThreads) dst[i] = bm[i];
-  if (with_first) {
-    uint32_t* fd = a.first + ((int64_t)wgg * a.n_rb + rb) * a.ubw * 4;
-    for (int i = tid; i < 4 * nwords; i += kPlanThreads) {
-      // nibble word i holds granules 8i .. 8i + 7: zero where a span covers
-      // the granule's first key
-      const uint32_t cb = (cov[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      uint32_t clear = 0u;
-#pragma unroll
-      for (int b = 0; b < 8; ++b)
-        if ((cb >> b) & 1u) clear |= 15u << (4 * b);
-      fd[i] = nib[i] & ~clear;
-    }
-  }
   if (a.dense) {
     for (int hh = tid; hh < n_here; hh += kPlanThreads)
       a.vl_cnt[(int64_t)(h_first + hh) * a.n_rb + rb] = 0;
@@ -1357,6 +1343,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
         if (v >= 0 && v <= rlast) {
           const int32_t gi = v / kGranule;
           keep = !((bm[gi >> 5] >> (gi & 31)) & 1u);
+          // a vertical in a marked granule is a span-tile key
+          if (!keep && with_first) nib_min(nib, gi, (uint32_t)(v % kGranule));
         }
       }
       const uint64_t bal = __ballot(keep);
@@ -1376,6 +1364,20 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
       total += tot;
     }
     if (tid == 0) a.vl_cnt[(int64_t)h * a.n_rb + rb] = total;
+  }
+  if (with_first) {
+    __syncthreads();
+    uint32_t* fd = a.first + ((int64_t)wgg * a.n_rb + rb) * a.ubw * 4;
+    for (int i = tid; i < 4 * nwords; i += kPlanThreads) {
+      // nibble word i holds granules 8i .. 8i + 7: zero where a span covers
+      // the granule's first key
+      const uint32_t cb = (cov[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      uint32_t clear = 0u;
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if ((cb >> b) & 1u) clear |= 15u << (4 * b);
+      fd[i] = nib[i] & ~clear;
+    }
   }
 }
 
