@@ -203,11 +203,14 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c,
           cw = wi < c.nwords ? c.ub[wi] : 0u;
           w.nz = __ballot(cw != 0u);
           w.chunk = ch;
-          // the chunk's first-key nibbles, 32 granules per lane (a vector
-          // load, waited for below)
-          if (c.first)
+          // the chunk's first-key nibbles, 32 granules per lane: a vector
+          // load, waited for at once (with any tile loads in flight, once per
+          // 2,048 granules), so that no wait for it is left at its uses
+          if (c.first) {
             nf = wi < c.nwords ? reinterpret_cast<const uint4*>(c.first)[wi]
                                : make_uint4(0u, 0u, 0u, 0u);
+            wait_vm<0>();
+          }
         }
         const int32_t wl = (g >> 5) & 63;
         const uint32_t word =
@@ -222,13 +225,6 @@ __device__ __forceinline__ bool next_tile(const AttnArgs& a, const WalkConst& c,
       }
       int32_t ks = g * kGranule;
       if (found && c.first) {
-        // vmcnt(0): the nibbles have landed, and so has the tile the walker
-        // issued just before this step.  The walker thus keeps one tile's
-        // loads in flight at a time, the first tile's loads land before the
-        // second's are issued; that halved the HBM traffic of a 1M-token
-        // call (fewer lines evicted from L2 before the other row blocks of
-        // the XCD read them) and was faster than issuing them back to back.
-        wait_vm<0>();
         const int32_t wl = (g >> 5) & 63, sel = (g >> 3) & 3;
         const uint32_t fw = sel == 0 ? nf.x : (sel == 1 ? nf.y : (sel == 2 ? nf.z : nf.w));
         ks += (int32_t)(((uint32_t)__builtin_amdgcn_readlane(fw, wl) >> (4 * (g & 7))) & 15u);
@@ -821,10 +817,15 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         // go into the stages of step j - 1, whose products are done
         const Tile ta = read_desc(&ring[(2 * j + 2) & (kRing - 1)]);
         const Tile tb = read_desc(&ring[(2 * j + 3) & (kRing - 1)]);
-        // the second tile's loads go out after the first walk step, so that
-        // fewer loads are in flight at once
+        // One tile's loads in flight at a time: the second tile's loads go
+        // out once the first tile's have landed, and a walk step runs while
+        // each tile is in flight.  Against issuing both tiles back to back
+        // this halved the HBM traffic of a 1M-token call (fewer lines evicted
+        // from L2 before the other row blocks of the XCD read them), and it
+        // is faster.
         issue(ta, 2 * j + 2);
         publish(2 * j + 6);
+        wait_vm<0>();
         issue(tb, 2 * j + 3);
         publish(2 * j + 7);
         wait_vm<0>();
