@@ -866,7 +866,7 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
     const uint32_t* colb = a.col_bits + (int64_t)(live ? h : 0) * a.n_words + kBitPad;
     // offset / column windows of a span tile for this head (scalar loads)
     auto load_windows = [&](const Tile& tt, Win& W, Win& C) {
-      if (tt.n > 0 && tt.wave < 0 && live) {
+      if (tt.n > 0 && tt.wave < 0 && live && !a.dense) {
         W = load_win(offb, i0 - tt.ks - 63);
         C = load_win(colb, tt.ks);
       }
@@ -987,8 +987,11 @@ __global__ void __launch_bounds__(64 * (NW + 1), 1) attn_kernel(AttnArgs a) {
         const char* bc = stage[i & (kStages - 1)];
         // this wave's key mask for the tile; act: any pair, full: all 64 x 32
         uint64_t mword = 0;
+        // dense calls select every offset, so the span mask is the causal
+        // one: no bitmap windows
         if (live && t0.wave < 0)
-          mword = span_mask(t0, W0, C0, i0, my_row, lane & 31);
+          mword = a.dense ? low_bits(my_row - t0.ks + 1) & low_bits(t0.n)
+                          : span_mask(t0, W0, C0, i0, my_row, lane & 31);
         else if (live && t0.wave == w)
           mword = gather_mask(t0, reinterpret_cast<const int32_t*>(bc + B::kKeyOff), my_row);
         const bool row_ok = my_row <= rlast;
