@@ -168,3 +168,21 @@ def parallel_map(fn, arg_list, workers=12):
         return [fn(*a) for a in arg_list]
     with mp.get_context("fork").Pool(n, initializer=_one_thread) as pool:
         return pool.map(_run_job, [(fn, a) for a in arg_list], chunksize=1)
+
+
+def critical_pair_total(verts, slashes, c0, c1):
+    """Sum over rows i in [c0, c1) of |C_i|, C_i = {v in verts : v <= i} U
+    {i - o : o in slashes, o <= i} (each key once), by inclusion and
+    exclusion on the index sets: the verticals' rows, plus the slashes'
+    rows, minus the (vertical, slash) pairs that name the same key of a row
+    (v + o = i).  verts and slashes hold distinct indices."""
+    v = np.unique(np.asarray(verts, dtype=np.int64))
+    o = np.unique(np.asarray(slashes, dtype=np.int64))
+    v = v[(v >= 0) & (v < c1)]
+    o = o[(o >= 0) & (o < c1)]
+    n_v = int(np.sum(c1 - np.maximum(v, c0)))
+    n_s = int(np.sum(c1 - np.maximum(o, c0)))
+    # pairs with c0 <= v + o < c1
+    both = int(np.sum(np.searchsorted(o, c1 - v, side="left") -
+                      np.searchsorted(o, c0 - v, side="left")))
+    return n_v + n_s - both

@@ -32,8 +32,8 @@ import oracle
 import synth
 from synth.configs import CONFIGS, scaled
 from tests.gpu_util import (DEV, MAX_ABS, MEAN_ABS, SCORE_REL, SCORE_REL_LARGE_LOGITS, compare,
-                            dca_of, lse_compare, near_tie_check, oracle_freqs, parallel_map,
-                            product_sm, rope_of, score_compare)
+                            critical_pair_total, dca_of, lse_compare, near_tie_check,
+                            oracle_freqs, parallel_map, product_sm, rope_of, score_compare)
 
 pytestmark = pytest.mark.gpu
 
@@ -323,6 +323,19 @@ def test_selection_bit_exact_full_size(layer_run):
                 oracle.select_top(ch["vs"][h], cfg.n_vert).tolist(), (c, h)
             assert ch["slashes"][h].tolist() == \
                 oracle.select_top(ch["ss"][h], cfg.n_slash).tolist(), (c, h)
+
+
+def test_pair_count_exact_full_size(layer_run):
+    """The attention's count of the pairs it weighted (a kernel statistic)
+    equals the exact sum of |C_i| over every row and head of each checked
+    chunk: the tile walk leaves out no key of any C_i and adds none."""
+    name, res = layer_run
+    cfg = CONFIGS[name]
+    for c, ch in res["chunks"].items():
+        c0, c1 = ch["c0"], ch["c0"] + ch["lc"]
+        want = sum(critical_pair_total(ch["verts"][h], ch["slashes"][h], c0, c1)
+                   for h in range(cfg.n_heads))
+        assert ch["stats"][1] == want, (name, c, ch["stats"], want)
 
 
 def test_estimate_scores_full_size(layer_run):

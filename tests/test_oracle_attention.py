@@ -83,6 +83,23 @@ def test_critical_set_semantics():
     assert oracle.critical_set(0, np.array([5]), np.array([1])).tolist() == []
 
 
+def test_critical_pair_total_counts_the_sets():
+    """The pair total the full-size GPU tests hold the kernel's pair count
+    to equals the sum of |C_i| over the oracle's critical sets, with
+    verticals on slash diagonals (overlaps), indices past the chunk and a
+    chunk that starts inside the context."""
+    from tests.gpu_util import critical_pair_total
+    rng = np.random.default_rng(11)
+    for c0, c1 in [(0, 300), (200, 520), (513, 514)]:
+        verts = np.sort(rng.choice(c1 + 40, size=45, replace=False))
+        slashes = np.sort(rng.choice(c1 + 40, size=70, replace=False))
+        # plant overlaps: vertical v on the diagonal o of row v + o
+        verts = np.unique(np.concatenate([verts, [c0 - slashes[3]] if c0 > slashes[3] else []])
+                          .astype(np.int64))
+        want = sum(oracle.critical_set(i, verts, slashes).size for i in range(c0, c1))
+        assert critical_pair_total(verts, slashes, c0, c1) == want
+
+
 @pytest.mark.parametrize("chunk,local", [(0, 0), (8, 2)])
 def test_sparse_rows_brute_force(chunk, local):
     rng = np.random.default_rng(13)
