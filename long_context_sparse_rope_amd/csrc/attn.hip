@@ -14,11 +14,13 @@
 //  * a planning kernel marks, per (KV group, row block), the 16-key granules
 //    that any head's slash runs reach (run [oa, ob] reaches keys
 //    [r0 - ob, rlast - oa]); the attention walks the marked granules in
-//    64-key tiles (cut at DCA chunk edges), and lists per head the verticals
-//    in unmarked granules, which are gathered 64 at a time;
+//    64-key tiles (each from the first key a pair reaches, cut at DCA chunk
+//    edges), and lists per head the verticals in unmarked granules, which
+//    are gathered 64 at a time;
 //  * K and V tiles go straight from HBM to LDS (global_load_lds_dwordx4,
-//    16-byte chunks XOR-swizzled by row) through a ring of four stages: three
-//    tiles are in flight while one is multiplied;
+//    16-byte chunks XOR-swizzled by row) through a ring of four stages: two
+//    tiles are multiplied per step while the next two are loaded, one after
+//    the other (dense calls: one tile per step, two loading);
 //  * per (wave, key tile) the pair mask is: key <= row and (offset bit of the
 //    wave's head or column bit in a marked granule); tiles a head does not
 //    touch are skipped by its wave, tiles it fully covers run unmasked;
