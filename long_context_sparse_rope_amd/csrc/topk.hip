@@ -60,6 +60,21 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Keys of indices first + u * step (u = 0..7), all eight loads issued
+// before the first is used; indices past last read index last (their keys
+// are ignored by the callers).
+__device__ __forceinline__ void load_keys8(const float* sc, int64_t first, int64_t step,
+                                           int64_t last, uint32_t (&key)[8]) {
+  float f[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = first + u * step;
+    f[u] = sc[i < last ? i : last];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) key[u] = order_key(f[u]);
+}
+
 __device__ __forceinline__ int level_shift(int l) { return l == 0 ? 20 : (l == 1 ? 8 : 0); }
 __device__ __forceinline__ uint32_t level_mask(int l) { return l == 2 ? 0xFFu : 0xFFFu; }
 
@@ -97,11 +112,14 @@ __global__ void __launch_bounds__(kThreads) topk_hist(TopkArgs a, int level) {
   const float* sc = a.set[set].scores + h * a.stride;
   const int64_t s0 = (int64_t)slice * kSlice;
   const int64_t s1 = s0 + kSlice < a.n ? s0 + kSlice : a.n;
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t i = s0 + (int64_t)j * kThreads + tid;
-    if (i < s1) {
-      const uint32_t key = order_key(sc[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & bmask], 1u);
+  // eight loads in flight per thread
+  for (int j0 = 0; j0 < kPerThread; j0 += 8) {
+    uint32_t key[8];
+    load_keys8(sc, s0 + (int64_t)j0 * kThreads + tid, kThreads, s1 - 1, key);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = s0 + (int64_t)(j0 + u) * kThreads + tid;
+      if (i < s1 && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & bmask], 1u);
     }
   }
   __syncthreads();
@@ -196,12 +214,15 @@ __global__ void __launch_bounds__(kThreads) topk_count(TopkArgs a) {
   const int64_t s0 = (int64_t)slice * kSlice;
   const int64_t s1 = s0 + kSlice < a.n ? s0 + kSlice : a.n;
   uint32_t gt = 0, eq = 0;
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t i = s0 + (int64_t)j * kThreads + tid;
-    const bool valid = i < s1;
-    const uint32_t key = valid ? order_key(sc[i]) : 0u;
-    gt += __popcll(__ballot(valid && key > T));
-    eq += __popcll(__ballot(valid && key == T));
+  for (int j0 = 0; j0 < kPerThread; j0 += 8) {
+    uint32_t key[8];
+    load_keys8(sc, s0 + (int64_t)j0 * kThreads + tid, kThreads, s1 - 1, key);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool valid = s0 + (int64_t)(j0 + u) * kThreads + tid < s1;
+      gt += __popcll(__ballot(valid && key[u] > T));
+      eq += __popcll(__ballot(valid && key[u] == T));
+    }
   }
   __shared__ uint32_t wc[kThreads / 64][2];
   if (lane == 0) {
@@ -228,8 +249,9 @@ __device__ __forceinline__ uint32_t take_eq(uint32_t need, uint32_t before, uint
 
 // ------------------------------------------------------------- compact
 // Wave w of the slice owns keys [s0 + 4096 w, s0 + 4096 (w + 1)), lane-
-// interleaved in steps of 64, held in registers between the count and the
-// write.
+// interleaved in steps of 64: read once to count them and again (from L2)
+// to write the selected indices.  (Holding the 64 keys of a lane in
+// registers between the two took 157 VGPRs and spilled SGPRs.)
 __global__ void __launch_bounds__(kThreads) topk_compact(TopkArgs a) {
   const int slice = blockIdx.x, h = blockIdx.y, set = blockIdx.z;
   if (!row_live(a, h)) return;
@@ -281,14 +303,16 @@ __global__ void __launch_bounds__(kThreads) topk_compact(TopkArgs a) {
   constexpr int kSteps = kPerWave / 64;
   const int64_t w0 = s0 + (int64_t)w * kPerWave;
   const float* sc = S.scores + h * a.stride;
-  uint32_t key[kSteps];
   uint32_t gt = 0, eq = 0;
+  for (int j0 = 0; j0 < kSteps; j0 += 8) {
+    uint32_t key[8];
+    load_keys8(sc, w0 + j0 * 64 + lane, 64, s1 - 1, key);
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j) {
-    const int64_t i = w0 + j * 64 + lane;
-    key[j] = i < s1 ? order_key(sc[i]) : 0u;  // key 0 ranks below every score
-    gt += __popcll(__ballot(i < s1 && key[j] > T));
-    eq += __popcll(__ballot(i < s1 && key[j] == T));
+    for (int u = 0; u < 8; ++u) {
+      const bool valid = w0 + (j0 + u) * 64 + lane < s1;
+      gt += __popcll(__ballot(valid && key[u] > T));
+      eq += __popcll(__ballot(valid && key[u] == T));
+    }
   }
   __shared__ uint32_t wc[kThreads / 64][2];
   if (lane == 0) {
@@ -301,18 +325,22 @@ __global__ void __launch_bounds__(kThreads) topk_compact(TopkArgs a) {
     eq_before += wc[u][1];
   }
   uint32_t eq_seen = 0, sel_seen = 0;
+  for (int j0 = 0; j0 < kSteps; j0 += 8) {
+    uint32_t key[8];
+    load_keys8(sc, w0 + j0 * 64 + lane, 64, s1 - 1, key);
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j) {
-    const int64_t i = w0 + j * 64 + lane;
-    const bool valid = i < s1;
-    const bool is_eq = valid && key[j] == T;
-    const uint64_t eq_mask = __ballot(is_eq);
-    const uint32_t rank = eq_before + eq_seen + lanes_below(eq_mask);
-    const bool sel = valid && (key[j] > T || (is_eq && rank < need_eq));
-    const uint64_t sel_mask = __ballot(sel);
-    if (sel) out[base + sel_seen + lanes_below(sel_mask)] = (int32_t)i;
-    eq_seen += __popcll(eq_mask);
-    sel_seen += __popcll(sel_mask);
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = w0 + (j0 + u) * 64 + lane;
+      const bool valid = i < s1;
+      const bool is_eq = valid && key[u] == T;
+      const uint64_t eq_mask = __ballot(is_eq);
+      const uint32_t rank = eq_before + eq_seen + lanes_below(eq_mask);
+      const bool sel = valid && (key[u] > T || (is_eq && rank < need_eq));
+      const uint64_t sel_mask = __ballot(sel);
+      if (sel) out[base + sel_seen + lanes_below(sel_mask)] = (int32_t)i;
+      eq_seen += __popcll(eq_mask);
+      sel_seen += __popcll(sel_mask);
+    }
   }
 }
 
