@@ -1309,16 +1309,28 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
       continue;
     }
     const int nr = min(a.run_cnt[h], a.max_runs);
-    const int32_t* rr = a.runs + (int64_t)h * a.max_runs * 2;
-    for (int i = tid; i < nr; i += kPlanThreads) {
-      const int64_t oa = rr[2 * i], ob = rr[2 * i + 1];
-      if (oa > rlast) continue;
-      const int64_t lo = r0 - ob > 0 ? r0 - ob : 0, hi = rlast - oa;
-      set_bits(bm, (int32_t)(lo / kGranule), (int32_t)(hi / kGranule));
-      if (with_first) {
-        const int32_t gc = (int32_t)((lo + kGranule - 1) / kGranule), gh = (int32_t)(hi / kGranule);
-        if (gc <= gh) set_bits(cov, gc, gh);
-        if (lo % kGranule) nib_min(nib, (int32_t)(lo / kGranule), (uint32_t)(lo % kGranule));
+    const int2* rr = reinterpret_cast<const int2*>(a.runs + (int64_t)h * a.max_runs * 2);
+    // four runs per thread loaded before the first is used (indices past the
+    // list read its last run and are skipped)
+    for (int i0 = tid; i0 < nr; i0 += 4 * kPlanThreads) {
+      int2 run[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kPlanThreads;
+        run[u] = rr[i < nr ? i : nr - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t oa = run[u].x, ob = run[u].y;
+        if (i0 + u * kPlanThreads >= nr || oa > rlast) continue;
+        const int64_t lo = r0 - ob > 0 ? r0 - ob : 0, hi = rlast - oa;
+        set_bits(bm, (int32_t)(lo / kGranule), (int32_t)(hi / kGranule));
+        if (with_first) {
+          const int32_t gc = (int32_t)((lo + kGranule - 1) / kGranule);
+          const int32_t gh = (int32_t)(hi / kGranule);
+          if (gc <= gh) set_bits(cov, gc, gh);
+          if (lo % kGranule) nib_min(nib, (int32_t)(lo / kGranule), (uint32_t)(lo % kGranule));
+        }
       }
     }
   }
@@ -1340,12 +1352,14 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
     int32_t* out = a.vl + ((int64_t)h * a.n_rb + rb) * a.max_vert;
     int total = 0;
     for (int b0 = 0; b0 < nv; b0 += kPlanThreads) {
-      if (vo[b0] > rlast) break;
       const int i = b0 + tid;
+      // this thread's vertical and the batch's first, loaded together
+      const int32_t vi = vo[i < nv ? i : nv - 1];
+      if (vo[b0] > rlast) break;
       bool keep = false;
       int32_t v = 0;
       if (i < nv) {
-        v = vo[i];
+        v = vi;
         if (v >= 0 && v <= rlast) {
           const int32_t gi = v / kGranule;
           keep = !((bm[gi >> 5] >> (gi & 31)) & 1u);
